@@ -1,0 +1,269 @@
+"""Python binding of libssm_adjoint.so (the MI355X selective-SSM adjoint-gradient library).
+
+Argument marshalling only: torch provides device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.  The
+entry points keep the C names (ssm_forward, ssm_adjoint_grad, ssm_stack_grad,
+ssm_workspace_bytes, ...).  Importing this module raises if the library has
+not been built -- there is no fallback path.
+
+Method: gradient of a diagonal selective state-space layer as the sum of
+per-token vector-Jacobian products driven by adjoint states, optionally
+truncated to a window (review of "Adjoint sharding for very long context
+training of state space models", Core claim: Propositions 2 and 3 and
+truncated adjoint sharding).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssm_adjoint.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+STATUS = {0: "SSM_OK", 1: "SSM_ERR_ARG", 2: "SSM_ERR_WORKSPACE", 3: "SSM_ERR_HIP", 4: "SSM_ERR_UNSUPPORTED"}
+
+EXPORTED = (
+    "ssm_version",
+    "ssm_status_str",
+    "ssm_saved_bytes",
+    "ssm_workspace_bytes",
+    "ssm_forward",
+    "ssm_adjoint_grad",
+    "ssm_stack_grad",
+)
+
+
+class SsmError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(code, code)}")
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("P", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("chunk", ctypes.c_int32), ("io", ctypes.c_int32)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("W_delta", ctypes.c_void_p), ("W_B", ctypes.c_void_p), ("W_C", ctypes.c_void_p),
+                ("alpha", ctypes.c_void_p), ("delta_bias", ctypes.c_void_p)]
+
+
+class Saved(ctypes.Structure):
+    _fields_ = [("s", ctypes.c_void_p), ("b", ctypes.c_void_p), ("c", ctypes.c_void_p),
+                ("h_ckpt", ctypes.c_void_p), ("s_sum", ctypes.c_void_p)]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [("dW_delta", ctypes.c_void_p), ("dW_B", ctypes.c_void_p), ("dW_C", ctypes.c_void_p),
+                ("dalpha", ctypes.c_void_p), ("dbias", ctypes.c_void_p), ("dx", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(python -m adjoint_gradients_amd._build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    lib.ssm_version.argtypes = []
+    lib.ssm_version.restype = ctypes.c_int32
+    lib.ssm_status_str.argtypes = [ctypes.c_int]
+    lib.ssm_status_str.restype = ctypes.c_char_p
+    lib.ssm_saved_bytes.argtypes = [P(Dims)]
+    lib.ssm_saved_bytes.restype = ctypes.c_size_t
+    lib.ssm_workspace_bytes.argtypes = [P(Dims), ctypes.c_int64, ctypes.c_int32]
+    lib.ssm_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssm_forward.argtypes = [P(Dims), P(Layer), ctypes.c_void_p, ctypes.c_void_p, P(Saved),
+                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.ssm_forward.restype = ctypes.c_int
+    lib.ssm_adjoint_grad.argtypes = [P(Dims), P(Layer), ctypes.c_void_p, P(Saved), ctypes.c_void_p,
+                                     ctypes.c_int64, P(Grads), ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_void_p]
+    lib.ssm_adjoint_grad.restype = ctypes.c_int
+    lib.ssm_stack_grad.argtypes = [ctypes.c_int32, P(Dims), P(Layer), ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_int64, P(Grads), ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.ssm_stack_grad.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+# ---------------------------------------------------------------- thin wrappers (C names)
+
+def ssm_version() -> int:
+    return int(lib.ssm_version())
+
+
+def ssm_status_str(code: int) -> str:
+    return lib.ssm_status_str(code).decode()
+
+
+def ssm_saved_bytes(dims: Dims) -> int:
+    return int(lib.ssm_saved_bytes(ctypes.byref(dims)))
+
+
+def ssm_workspace_bytes(dims: Dims, window: int = 0, K: int = 0) -> int:
+    return int(lib.ssm_workspace_bytes(ctypes.byref(dims), int(window), int(K)))
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return int(stream)
+    import torch
+
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise SsmError(code, where)
+
+
+def make_dims(T: int, P: int, N: int, chunk: int = 256, io: str = "f32") -> Dims:
+    return Dims(T, P, N, chunk, SSM_BF16 if io == "bf16" else SSM_F32)
+
+
+def layer_struct(W_delta, W_B, W_C, alpha, delta_bias=None) -> Layer:
+    return Layer(_ptr(W_delta), _ptr(W_B), _ptr(W_C), _ptr(alpha), _ptr(delta_bias))
+
+
+def saved_struct(saved: dict) -> Saved:
+    return Saved(_ptr(saved["s"]), _ptr(saved["b"]), _ptr(saved["c"]), _ptr(saved["h_ckpt"]),
+                 _ptr(saved["s_sum"]))
+
+
+def grads_struct(grads: dict) -> Grads:
+    return Grads(_ptr(grads.get("dW_delta")), _ptr(grads.get("dW_B")), _ptr(grads.get("dW_C")),
+                 _ptr(grads.get("dalpha")), _ptr(grads.get("dbias")), _ptr(grads.get("dx")))
+
+
+def ssm_forward(dims: Dims, layer: Layer, x, y, saved: Saved, ws, ws_bytes: int, stream=None):
+    _check(lib.ssm_forward(ctypes.byref(dims), ctypes.byref(layer), _ptr(x), _ptr(y), ctypes.byref(saved),
+                           _ptr(ws), int(ws_bytes), _stream(stream)), "ssm_forward")
+
+
+def ssm_adjoint_grad(dims: Dims, layer: Layer, x, saved: Saved, g, window: int, grads: Grads, ws,
+                     ws_bytes: int, stream=None):
+    _check(lib.ssm_adjoint_grad(ctypes.byref(dims), ctypes.byref(layer), _ptr(x), ctypes.byref(saved), _ptr(g),
+                                int(window), ctypes.byref(grads), _ptr(ws), int(ws_bytes), _stream(stream)),
+           "ssm_adjoint_grad")
+
+
+def ssm_stack_grad(K: int, dims: Dims, layers, x0, g, window: int, grads, dx0, xK, ws, ws_bytes: int,
+                   stream=None):
+    LArr = Layer * K
+    GArr = Grads * K
+    la = LArr(*layers)
+    ga = GArr(*grads)
+    _check(lib.ssm_stack_grad(int(K), ctypes.byref(dims), la, _ptr(x0), _ptr(g), int(window), ga, _ptr(dx0),
+                              _ptr(xK), _ptr(ws), int(ws_bytes), _stream(stream)), "ssm_stack_grad")
+
+
+# ---------------------------------------------------------------- torch-side conveniences
+
+@dataclass
+class LayerTensors:
+    """Device tensors of one layer (io dtype for the weights)."""
+    W_delta: object
+    W_B: object
+    W_C: object
+    alpha: object
+    delta_bias: object = None
+
+    def struct(self) -> Layer:
+        return layer_struct(self.W_delta, self.W_B, self.W_C, self.alpha, self.delta_bias)
+
+
+def io_dtype(io: str):
+    import torch
+
+    return torch.bfloat16 if io == "bf16" else torch.float32
+
+
+def alloc_saved(dims: Dims, device="cuda") -> dict:
+    import torch
+
+    K = (dims.T + dims.chunk - 1) // dims.chunk
+    f = dict(device=device, dtype=torch.float32)
+    return {
+        "s": torch.empty(dims.T, dims.P, **f),
+        "b": torch.empty(dims.T, dims.N, **f),
+        "c": torch.empty(dims.T, dims.N, **f),
+        "h_ckpt": torch.empty(K, dims.P, dims.N, **f),
+        "s_sum": torch.empty(K, dims.P, device=device, dtype=torch.float64),
+    }
+
+
+def alloc_workspace(nbytes: int, device="cuda"):
+    import torch
+
+    return torch.empty(max(int(nbytes), 1), device=device, dtype=torch.uint8)
+
+
+def forward(dims: Dims, layer: LayerTensors, x, ws=None, saved=None, y=None, stream=None):
+    """Runs ssm_forward; returns (y, saved dict)."""
+    import torch
+
+    nbytes = ssm_workspace_bytes(dims, 0, 0)
+    if nbytes == 0:
+        raise SsmError(4, "ssm_workspace_bytes")
+    ws = alloc_workspace(nbytes, x.device) if ws is None else ws
+    saved = alloc_saved(dims, x.device) if saved is None else saved
+    y = torch.empty(dims.T, dims.P, device=x.device, dtype=torch.float32) if y is None else y
+    ssm_forward(dims, layer.struct(), x, y, saved_struct(saved), ws, ws.numel(), stream)
+    return y, saved
+
+
+def alloc_grads(dims: Dims, want_dx=False, want_dalpha=True, want_dbias=True, device="cuda") -> dict:
+    import torch
+
+    f = dict(device=device, dtype=torch.float32)
+    g = {"dW_delta": torch.empty(dims.P, dims.P, **f), "dW_B": torch.empty(dims.N, dims.P, **f),
+         "dW_C": torch.empty(dims.N, dims.P, **f)}
+    if want_dalpha:
+        g["dalpha"] = torch.empty(dims.P, dims.N, **f)
+    if want_dbias:
+        g["dbias"] = torch.empty(dims.P, **f)
+    if want_dx:
+        g["dx"] = torch.empty(dims.T, dims.P, **f)
+    return g
+
+
+def adjoint_grad(dims: Dims, layer: LayerTensors, x, saved: dict, g, window: int, want_dx=False, ws=None,
+                 grads=None, stream=None) -> dict:
+    """Runs ssm_adjoint_grad; returns the gradient dict."""
+    nbytes = ssm_workspace_bytes(dims, window, 0)
+    if nbytes == 0:
+        raise SsmError(4, "ssm_workspace_bytes")
+    ws = alloc_workspace(nbytes, x.device) if ws is None else ws
+    grads = alloc_grads(dims, want_dx=want_dx, device=x.device) if grads is None else grads
+    ssm_adjoint_grad(dims, layer.struct(), x, saved_struct(saved), g, window, grads_struct(grads), ws,
+                     ws.numel(), stream)
+    return grads
+
+
+def stack_grad(dims: Dims, layers: list, x0, g, window: int, ws=None, want_dx0=True, want_xK=True,
+               stream=None):
+    """Runs ssm_stack_grad; returns (list of gradient dicts, dx0, xK)."""
+    import torch
+
+    K = len(layers)
+    nbytes = ssm_workspace_bytes(dims, window, K)
+    if nbytes == 0:
+        raise SsmError(4, "ssm_workspace_bytes")
+    ws = alloc_workspace(nbytes, x0.device) if ws is None else ws
+    grads = [alloc_grads(dims, device=x0.device) for _ in range(K)]
+    f = dict(device=x0.device, dtype=torch.float32)
+    dx0 = torch.empty(dims.T, dims.P, **f) if want_dx0 else None
+    xK = torch.empty(dims.T, dims.P, **f) if want_xK else None
+    ssm_stack_grad(K, dims, [lay.struct() for lay in layers], x0, g, window, [grads_struct(gr) for gr in grads],
+                   dx0, xK, ws, ws.numel(), stream)
+    return grads, dx0, xK

@@ -1,0 +1,389 @@
+// api.hip -- the C ABI declared in include/ssm_adjoint.h.
+//
+// Every entry point validates its arguments completely before the first
+// enqueue, carves its scratch buffers out of the caller's workspace (no
+// allocation, no synchronisation) and launches the kernels on the caller's
+// stream.  The launch order is the method's data flow:
+//   forward:  pack W_cat -> projection GEMM (s, b, c) -> chunk-local scan ->
+//             chunk carry (checkpoints) -> final scan (y)
+//   gradient: reverse local aggregates -> reverse carry -> fused reverse
+//             adjoint + local VJPs -> db/dc channel sums -> split-K weight
+//             gradient GEMM -> reduction (+ input-cotangent GEMM)
+//   stack:    K forwards with the residual update, then the layers in reverse
+//             with the total cotangent (Proposition 3 of the review of
+//             "Adjoint sharding for very long context training of state space
+//             models", Core claim).
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/ssm_adjoint.h"
+#include "ssm_kernels.hpp"
+
+namespace {
+
+using ssm::BwdArgs;
+using ssm::BwdPlan;
+using ssm::FwdArgs;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Sequential carve-out of a workspace; in "plan" mode only sizes are summed.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T> T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+bool supported_N(int64_t N) {
+  return N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64;
+}
+
+ssm_status check_dims(const ssm_dims* d) {
+  if (!d) return SSM_ERR_ARG;
+  if (d->T < 1 || d->P < 1 || d->N < 1 || d->chunk < 1) return SSM_ERR_ARG;
+  if (d->io != SSM_F32 && d->io != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (!supported_N(d->N) || d->chunk > 512) return SSM_ERR_UNSUPPORTED;
+  if (d->T > (int64_t(1) << 31) || d->P > (int64_t(1) << 20)) return SSM_ERR_UNSUPPORTED;
+  BwdPlan pl;
+  if (!ssm::bwd_plan(d->P, d->N, d->chunk, &pl)) return SSM_ERR_UNSUPPORTED;
+  return SSM_OK;
+}
+
+int64_t nchunks(const ssm_dims* d) { return (d->T + d->chunk - 1) / d->chunk; }
+size_t io_size(const ssm_dims* d) { return d->io == SSM_BF16 ? 2 : 4; }
+
+ssm_status check_layer(const ssm_layer* L) {
+  if (!L || !L->W_delta || !L->W_B || !L->W_C || !L->alpha) return SSM_ERR_ARG;
+  if (!aligned16(L->W_delta) || !aligned16(L->W_B) || !aligned16(L->W_C) || !aligned16(L->alpha))
+    return SSM_ERR_ARG;
+  if (L->delta_bias && !aligned16(L->delta_bias)) return SSM_ERR_ARG;
+  return SSM_OK;
+}
+
+ssm_status check_saved(const ssm_saved* s) {
+  if (!s || !s->s || !s->b || !s->c || !s->h_ckpt || !s->s_sum) return SSM_ERR_ARG;
+  if (!aligned16(s->s) || !aligned16(s->b) || !aligned16(s->c) || !aligned16(s->h_ckpt) || !aligned16(s->s_sum))
+    return SSM_ERR_ARG;
+  return SSM_OK;
+}
+
+ssm_status check_grads(const ssm_grads* g) {
+  if (!g || !g->dW_delta || !g->dW_B || !g->dW_C) return SSM_ERR_ARG;
+  const void* ps[] = {g->dW_delta, g->dW_B, g->dW_C, g->dalpha, g->dbias, g->dx};
+  for (const void* p : ps)
+    if (p && !aligned16(p)) return SSM_ERR_ARG;
+  return SSM_OK;
+}
+
+ssm_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return SSM_OK;
+  if (!ws) return SSM_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return SSM_ERR_WORKSPACE;
+  if (have < need) return SSM_ERR_WORKSPACE;
+  return SSM_OK;
+}
+
+// ---------------------------------------------------------------- workspace plans
+
+struct FwdWs {
+  void* wcat;
+  float* hloc;
+};
+
+FwdWs carve_fwd(Carver& cv, const ssm_dims* d) {
+  FwdWs w;
+  const int64_t M = d->P + 2 * d->N;
+  w.wcat = cv.take<char>(static_cast<size_t>(M * d->P) * io_size(d));
+  w.hloc = cv.take<float>(static_cast<size_t>(nchunks(d) * d->P * d->N));
+  return w;
+}
+
+int splitk_for(const ssm_dims* d) {
+  const int64_t M = d->P + 2 * d->N;
+  const int64_t tiles = ((M + 127) / 128) * ((d->P + 127) / 128);
+  int64_t s = 2048 / (tiles > 0 ? tiles : 1);
+  const int64_t cap = d->T / 512;
+  if (s > cap) s = cap;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  return static_cast<int>(s);
+}
+
+struct BwdWs {
+  void* wcat;      // only when dx is needed
+  void* dY;
+  float* dxdir;    // only when dx is needed
+  float* part;
+  float* umu;
+  float* carry;
+  double* ps64;
+  double* hwin;
+  float* dal_part;
+  float* dbias_part;
+  float* wpart;
+  int splits;
+};
+
+BwdWs carve_bwd(Carver& cv, const ssm_dims* d, int64_t W, bool need_dx) {
+  BwdWs w;
+  BwdPlan pl;
+  ssm::bwd_plan(d->P, d->N, d->chunk, &pl);
+  const int64_t T = d->T, P = d->P, N = d->N, K = nchunks(d);
+  const int64_t M = P + 2 * N;
+  const bool win = W < T;
+  w.wcat = need_dx ? cv.take<char>(static_cast<size_t>(M * P) * io_size(d)) : nullptr;
+  w.dY = cv.take<char>(static_cast<size_t>(T * M) * io_size(d));
+  w.dxdir = need_dx ? cv.take<float>(static_cast<size_t>(T * P)) : nullptr;
+  w.part = cv.take<float>(static_cast<size_t>(T * pl.NBW * 2 * N));
+  w.umu = cv.take<float>(static_cast<size_t>(K * P * N));
+  w.carry = cv.take<float>(static_cast<size_t>(K * P * N));
+  w.ps64 = win ? cv.take<double>(static_cast<size_t>((K + 1) * P)) : nullptr;
+  w.hwin = win ? cv.take<double>(static_cast<size_t>(K * P)) : nullptr;
+  w.dal_part = cv.take<float>(static_cast<size_t>(K * P * N));
+  w.dbias_part = cv.take<float>(static_cast<size_t>(K * P));
+  w.splits = splitk_for(d);
+  w.wpart = cv.take<float>(static_cast<size_t>(w.splits) * M * P);
+  return w;
+}
+
+ssm_saved carve_saved(Carver& cv, const ssm_dims* d) {
+  ssm_saved s;
+  const int64_t T = d->T, P = d->P, N = d->N, K = nchunks(d);
+  s.s = cv.take<float>(static_cast<size_t>(T * P));
+  s.b = cv.take<float>(static_cast<size_t>(T * N));
+  s.c = cv.take<float>(static_cast<size_t>(T * N));
+  s.h_ckpt = cv.take<float>(static_cast<size_t>(K * P * N));
+  s.s_sum = cv.take<double>(static_cast<size_t>(K * P));
+  return s;
+}
+
+size_t fwd_ws_bytes(const ssm_dims* d) {
+  Carver cv(nullptr);
+  carve_fwd(cv, d);
+  return cv.off;
+}
+
+size_t bwd_ws_bytes(const ssm_dims* d, int64_t W, bool need_dx) {
+  Carver cv(nullptr);
+  carve_bwd(cv, d, W, need_dx);
+  return cv.off;
+}
+
+size_t stack_ws_bytes(const ssm_dims* d, int64_t W, int32_t K) {
+  Carver cv(nullptr);
+  for (int32_t k = 0; k < K; k++) carve_saved(cv, d);
+  cv.take<char>(static_cast<size_t>(K) * d->T * d->P * io_size(d));
+  cv.take<float>(static_cast<size_t>(d->T * d->P));
+  cv.take<float>(static_cast<size_t>(d->T * d->P));
+  cv.take<float>(static_cast<size_t>(d->T * d->P));
+  const size_t f = fwd_ws_bytes(d), b = bwd_ws_bytes(d, W, true);
+  return cv.off + (f > b ? f : b);
+}
+
+// ---------------------------------------------------------------- internal passes
+
+hipError_t pack_wcat(const ssm_dims* d, const ssm_layer* L, void* wcat, hipStream_t st) {
+  const size_t es = io_size(d);
+  const size_t rowb = static_cast<size_t>(d->P) * es;
+  char* dst = static_cast<char*>(wcat);
+  hipError_t e = hipMemcpyAsync(dst, L->W_delta, rowb * d->P, hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return e;
+  e = hipMemcpyAsync(dst + rowb * d->P, L->W_B, rowb * d->N, hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return e;
+  return hipMemcpyAsync(dst + rowb * (d->P + d->N), L->W_C, rowb * d->N, hipMemcpyDeviceToDevice, st);
+}
+
+hipError_t run_forward(const ssm_dims* d, const ssm_layer* L, const void* x, float* y, const ssm_saved* sv,
+                       const FwdWs& w, hipStream_t st) {
+  const bool bf = d->io == SSM_BF16;
+  hipError_t e = pack_wcat(d, L, w.wcat, st);
+  if (e != hipSuccess) return e;
+  ssm::GemmOperands op{d->T, d->P + 2 * d->N, d->P, x, d->P, true, w.wcat, d->P, true};
+  ssm::EpiProjArgs ep{d->P, d->N, L->delta_bias, sv->s, sv->b, sv->c};
+  e = ssm::gemm_projection(op, bf, ep, st);
+  if (e != hipSuccess) return e;
+  FwdArgs fa{d->T, d->P, d->N, d->chunk, sv->s, x, sv->b, sv->c, L->alpha, w.hloc, sv->s_sum, sv->h_ckpt, y};
+  return ssm::launch_forward_scan(fa, bf, st);
+}
+
+// Gradient of one layer.  If delta_io is set (stack), dx is folded into it:
+// delta_io <- delta_io + dx; otherwise dx goes to grads->dx when requested.
+hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, const ssm_saved* sv,
+                        const float* g, int64_t W, const ssm_grads* gr, float* delta_io, const BwdWs& w,
+                        hipStream_t st) {
+  const bool bf = d->io == SSM_BF16;
+  const int64_t T = d->T, P = d->P, N = d->N;
+  const int64_t M = P + 2 * N;
+  const bool need_dx = (delta_io != nullptr) || (gr->dx != nullptr);
+  BwdArgs a{};
+  a.T = T; a.P = P; a.N = N; a.W = W; a.C = d->chunk;
+  a.s = sv->s; a.x = x; a.b = sv->b; a.c = sv->c; a.alpha = L->alpha; a.h_ckpt = sv->h_ckpt;
+  a.ssum = sv->s_sum; a.g = g;
+  a.ps64 = w.ps64; a.hwin = w.hwin; a.umu = w.umu; a.carry = w.carry; a.part = w.part;
+  a.dal_part = w.dal_part; a.dbias_part = w.dbias_part;
+  a.dY = w.dY; a.ldy = M;
+  a.dxdir = need_dx ? w.dxdir : nullptr;
+  a.dalpha = gr->dalpha; a.dbias = gr->dbias;
+  hipError_t e = ssm::launch_backward_scan(a, bf, st);
+  if (e != hipSuccess) return e;
+  // dW_cat = dY^T X  (K = T, both operands token-major)
+  ssm::GemmOperands op{M, P, T, w.dY, M, false, x, P, false};
+  e = ssm::gemm_splitk(op, bf, w.splits, w.wpart, st);
+  if (e != hipSuccess) return e;
+  e = ssm::reduce_weight_grads(w.wpart, w.splits, P, N, gr->dW_delta, gr->dW_B, gr->dW_C, st);
+  if (e != hipSuccess) return e;
+  if (need_dx) {
+    e = pack_wcat(d, L, w.wcat, st);
+    if (e != hipSuccess) return e;
+    // dx = dY W_cat + dxdir  (+ delta for the stack, in place)
+    ssm::GemmOperands opx{T, P, M, w.dY, M, true, w.wcat, P, false};
+    ssm::EpiAddArgs ea{w.dxdir, delta_io, delta_io ? delta_io : gr->dx};
+    e = ssm::gemm_add(opx, bf, ea, st);
+  }
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ssm_version(void) { return 100; }
+
+const char* ssm_status_str(ssm_status s) {
+  switch (s) {
+    case SSM_OK: return "SSM_OK";
+    case SSM_ERR_ARG: return "SSM_ERR_ARG: invalid argument";
+    case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case SSM_ERR_HIP: return "SSM_ERR_HIP: kernel launch failed";
+    case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: shape or dtype not supported";
+    default: return "SSM_ERR_UNKNOWN";
+  }
+}
+
+size_t ssm_saved_bytes(const ssm_dims* d) {
+  if (check_dims(d) != SSM_OK) return 0;
+  Carver cv(nullptr);
+  carve_saved(cv, d);
+  return cv.off;
+}
+
+size_t ssm_workspace_bytes(const ssm_dims* d, int64_t window, int32_t K) {
+  if (check_dims(d) != SSM_OK) return 0;
+  if (K < 0 || window < 0) return 0;
+  if (K >= 1) {
+    if (window < 1) return 0;
+    return stack_ws_bytes(d, window, K);
+  }
+  if (window == 0) return fwd_ws_bytes(d);
+  return bwd_ws_bytes(d, window, true);
+}
+
+ssm_status ssm_forward(const ssm_dims* d, const ssm_layer* L, const void* x, float* y, const ssm_saved* sv,
+                       void* ws, size_t ws_bytes, void* stream) {
+  ssm_status s = check_dims(d);
+  if (s != SSM_OK) return s;
+  if ((s = check_layer(L)) != SSM_OK) return s;
+  if ((s = check_saved(sv)) != SSM_OK) return s;
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return SSM_ERR_ARG;
+  if ((s = check_ws(ws, ws_bytes, fwd_ws_bytes(d))) != SSM_OK) return s;
+  Carver cv(ws);
+  FwdWs w = carve_fwd(cv, d);
+  hipError_t e = run_forward(d, L, x, y, sv, w, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status ssm_adjoint_grad(const ssm_dims* d, const ssm_layer* L, const void* x, const ssm_saved* sv,
+                            const float* g, int64_t window, const ssm_grads* gr, void* ws, size_t ws_bytes,
+                            void* stream) {
+  ssm_status s = check_dims(d);
+  if (s != SSM_OK) return s;
+  if ((s = check_layer(L)) != SSM_OK) return s;
+  if ((s = check_saved(sv)) != SSM_OK) return s;
+  if ((s = check_grads(gr)) != SSM_OK) return s;
+  if (!x || !g || !aligned16(x) || !aligned16(g)) return SSM_ERR_ARG;
+  if (window < 1) return SSM_ERR_ARG;
+  const int64_t W = window < d->T ? window : d->T;
+  const bool need_dx = gr->dx != nullptr;
+  if ((s = check_ws(ws, ws_bytes, bwd_ws_bytes(d, W, need_dx))) != SSM_OK) return s;
+  Carver cv(ws);
+  BwdWs w = carve_bwd(cv, d, W, need_dx);
+  hipError_t e = run_backward(d, L, x, sv, g, W, gr, nullptr, w, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status ssm_stack_grad(int32_t K, const ssm_dims* d, const ssm_layer* layers, const void* x0, const float* g,
+                          int64_t window, const ssm_grads* grads, float* dx0, float* xK, void* ws,
+                          size_t ws_bytes, void* stream) {
+  ssm_status s = check_dims(d);
+  if (s != SSM_OK) return s;
+  if (K < 1 || !layers || !grads) return SSM_ERR_ARG;
+  for (int32_t k = 0; k < K; k++) {
+    if ((s = check_layer(&layers[k])) != SSM_OK) return s;
+    if ((s = check_grads(&grads[k])) != SSM_OK) return s;
+    if (grads[k].dx) return SSM_ERR_ARG;  // per-layer dx is internal to the stack; use dx0
+  }
+  if (!x0 || !g || !aligned16(x0) || !aligned16(g)) return SSM_ERR_ARG;
+  if ((dx0 && !aligned16(dx0)) || (xK && !aligned16(xK))) return SSM_ERR_ARG;
+  if (window < 1) return SSM_ERR_ARG;
+  const int64_t W = window < d->T ? window : d->T;
+  if ((s = check_ws(ws, ws_bytes, stack_ws_bytes(d, W, K))) != SSM_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = d->io == SSM_BF16;
+  const int64_t TP = d->T * d->P;
+  const size_t xbytes = static_cast<size_t>(TP) * io_size(d);
+
+  Carver cv(ws);
+  ssm_saved saved[64];
+  ssm_saved* sv = saved;
+  if (K > 64) return SSM_ERR_UNSUPPORTED;
+  for (int32_t k = 0; k < K; k++) sv[k] = carve_saved(cv, d);
+  char* xs = cv.take<char>(static_cast<size_t>(K) * xbytes);
+  float* r = cv.take<float>(static_cast<size_t>(TP));
+  float* y = cv.take<float>(static_cast<size_t>(TP));
+  float* delta = cv.take<float>(static_cast<size_t>(TP));
+  const size_t shared_off = cv.off;
+
+  hipError_t e = ssm::residual_init(TP, x0, bf, r, st);
+  if (e != hipSuccess) return SSM_ERR_HIP;
+  // x^0 = io(r^0)
+  if ((e = ssm::residual_update(TP, r, nullptr, xs, bf, st)) != hipSuccess) return SSM_ERR_HIP;
+  for (int32_t k = 0; k < K; k++) {
+    void* xk = xs + static_cast<size_t>(k) * xbytes;
+    Carver fc(static_cast<char*>(ws) + shared_off);
+    FwdWs fw = carve_fwd(fc, d);
+    if ((e = run_forward(d, &layers[k], xk, y, &sv[k], fw, st)) != hipSuccess) return SSM_ERR_HIP;
+    // r^{k+1} = r^k + y^k and x^{k+1} = io(r^{k+1})
+    void* xnext = (k + 1 < K) ? xs + static_cast<size_t>(k + 1) * xbytes : nullptr;
+    if ((e = ssm::residual_update(TP, r, y, xnext, bf, st)) != hipSuccess) return SSM_ERR_HIP;
+  }
+  if (xK) {
+    if ((e = hipMemcpyAsync(xK, r, static_cast<size_t>(TP) * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess)
+      return SSM_ERR_HIP;
+  }
+  if ((e = hipMemcpyAsync(delta, g, static_cast<size_t>(TP) * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess)
+    return SSM_ERR_HIP;
+  for (int32_t k = K - 1; k >= 0; k--) {
+    void* xk = xs + static_cast<size_t>(k) * xbytes;
+    Carver bc(static_cast<char*>(ws) + shared_off);
+    BwdWs bw = carve_bwd(bc, d, W, true);
+    // layer k is driven by delta^{k+1}; then delta^k = delta^{k+1} + dx^k
+    if ((e = run_backward(d, &layers[k], xk, &sv[k], delta, W, &grads[k], delta, bw, st)) != hipSuccess)
+      return SSM_ERR_HIP;
+  }
+  if (dx0) {
+    if ((e = hipMemcpyAsync(dx0, delta, static_cast<size_t>(TP) * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess)
+      return SSM_ERR_HIP;
+  }
+  return SSM_OK;
+}
+
+}  // extern "C"

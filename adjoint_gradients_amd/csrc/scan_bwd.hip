@@ -1,0 +1,501 @@
+// scan_bwd.hip -- windowed reverse adjoint scan fused with the local VJPs, on gfx950.
+//
+// Source: review of "Adjoint sharding for very long context training of state
+// space models" -- "What carries the argument" (adjoint state
+// lambda_{t,i} = C_t A_t ... A_{i+1}; Proposition 1) and "Core claim"
+// (Proposition 2 and truncated adjoint sharding over the last W tokens).
+//
+// For one channel p and state n, every VJP term of token i is multiplied by
+//   mu_i = sum_{t=i}^{min(T,i+W)-1} g_t c_t prod_{j=i+1}^{t} a_j ,
+// the cotangent-weighted sum of adjoint states.  mu obeys the reverse
+// recurrence
+//   mu_i = a_{i+1} mu_{i+1} + g_i c_i - g_{i+W} c_{i+W} D_i,
+//   D_i  = prod_{j=i+1}^{i+W} a_j = exp(-alpha sum_{j=i+1}^{i+W} s_j)
+// (the last term drops the token leaving the window; it is absent when
+// W >= T or i+W >= T).  The recurrence is Proposition 1 with df/dh = diag(a)
+// and a source that is local in time, so it parallelises over chunks exactly
+// like the forward scan: affine chunk maps, a carry pass, then a final pass.
+// The window sums of s are kept in fp64, so D needs no subtraction of
+// rounded products.
+//
+// The local VJPs of token i (Proposition 2's vjp^{A_i}, vjp^{B_i}, vjp^{C_t}):
+//   da_i     = mu_i h_{i-1}                  dDelta_i = sigmoid(Delta_i) sum_n da_i (-alpha a_i)
+//   dalpha  += da_i (-s_i a_i)               dbias   += dDelta_i
+//   db_i[n]  = sum_p mu_i x_i[p]             dxdir_i = sum_n mu_i b_i[n]
+//   dc_i[n]  = sum_p g_i h_i[p]   (no time sum, hence no window)
+// h_{i-1} is recomputed inside each chunk from the checkpoint h_{kC-1}
+// (review of "Training Deep Nets with Sublinear Memory Cost": recompute
+// inside segments): a forward walk stores h at every S-token sub-chunk in
+// LDS, then each sub-chunk is recomputed into registers and walked in reverse.
+// Sums over channels (db, dc) go through an LDS transpose per wavefront, an
+// LDS sum over the wavefronts of the workgroup, and a deterministic final sum
+// over workgroups in a separate kernel.
+#include "ssm_common.hpp"
+#include "ssm_kernels.hpp"
+
+namespace ssm {
+
+namespace {
+
+template <int NL>
+__device__ __forceinline__ void load_row(const float* __restrict__ src, float (&dst)[NL]) {
+  if constexpr (NL % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < NL; j += 4) {
+      float4 v = *reinterpret_cast<const float4*>(src + j);
+      dst[j] = v.x; dst[j + 1] = v.y; dst[j + 2] = v.z; dst[j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NL; j++) dst[j] = src[j];
+  }
+}
+
+// Orders this wavefront's LDS writes before its following LDS reads of other
+// lanes' data (and prevents the compiler from moving accesses across it).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+constexpr int kSub = 16;  // tokens per recomputed sub-chunk (registers hold S x NL states)
+
+}  // namespace
+
+// Exclusive prefix over chunks of the per-chunk sums of s, in fp64.
+__global__ __launch_bounds__(256) void k_bwd_prefix(int64_t K, int64_t P, const double* __restrict__ ssum,
+                                                    double* __restrict__ ps64) {
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (p >= P) return;
+  double acc = 0.0;
+  ps64[p] = 0.0;
+#pragma unroll 8
+  for (int64_t k = 0; k < K; k++) {
+    acc += ssum[k * P + p];
+    ps64[(k + 1) * P + p] = acc;
+  }
+}
+
+// Local reverse scan of every chunk with zero carry: writes
+//   umu[k] = a_{t0} mu^loc_{t0}   (the chunk's contribution to the carry leaving it),
+// and for a window W < T the fp64 sum of s over the W tokens after the chunk.
+template <typename IO, int NL, int G, bool WIN>
+__global__ __launch_bounds__(64) void k_bwd_local(BwdArgs a) {
+  constexpr int CH = 64 / G;
+  constexpr int NN = NL * G;
+  const int lane = threadIdx.x;
+  const int grp = lane / CH, pl = lane % CH;
+  const int64_t T = a.T, P = a.P, W = a.W;
+  const int C = a.C;
+  const int64_t K = (T + C - 1) / C;
+  const int64_t k = blockIdx.x;
+  const int64_t p = static_cast<int64_t>(blockIdx.y) * CH + pl;
+  const bool valid = p < P;
+  const int64_t pc = valid ? p : P - 1;
+  const int n0 = grp * NL;
+  float al2[NL], inc[NL];
+#pragma unroll
+  for (int j = 0; j < NL; j++) {
+    al2[j] = a.alpha[pc * NN + n0 + j] * kLog2e;
+    inc[j] = 0.0f;
+  }
+  const int64_t t0 = k * C;
+  const int64_t t1 = (t0 + C < T) ? t0 + C : T;
+  double H = 0.0, sigma = 0.0, suffix = 0.0;
+  if constexpr (WIN) {
+    // H = sum of s over tokens (t1 .. t1+W-1) clipped to T: whole chunks
+    // k+1 .. k+q, then the first w0 tokens of chunk k+q+1.
+    const int64_t q = W / C, w0 = W % C;
+    const int64_t kb = (k + q + 1 < K) ? k + q + 1 : K;
+    const int64_t ka = (k + 1 < K) ? k + 1 : K;
+    H = a.ps64[kb * P + pc] - a.ps64[ka * P + pc];
+    if (k + q + 1 < K) {
+      const int64_t h0 = (k + q + 1) * C;
+      const int64_t h1 = (h0 + w0 < T) ? h0 + w0 : T;
+      for (int64_t t = h0; t < h1; t++) H += static_cast<double>(a.s[t * P + pc]);
+    }
+    if (valid && grp == 0) a.hwin[k * P + p] = H;
+  }
+  const IO* x = static_cast<const IO*>(a.x);
+  (void)x;
+  for (int64_t i = t1 - 1; i >= t0; i--) {
+    const float s = a.s[i * P + pc];
+    const float gv = a.g[i * P + pc];
+    float ct[NL];
+    load_row<NL>(a.c + i * NN + n0, ct);
+    float mu[NL], av[NL];
+#pragma unroll
+    for (int j = 0; j < NL; j++) {
+      av[j] = fast_exp2(-s * al2[j]);
+      mu[j] = fmaf(gv, ct[j], inc[j]);
+    }
+    if constexpr (WIN) {
+      const int64_t m = i + W;
+      if (m < T) {
+        const float sm = a.s[m * P + pc];
+        const float gm = a.g[m * P + pc];
+        float cm[NL];
+        load_row<NL>(a.c + m * NN + n0, cm);
+        const float E = static_cast<float>(sigma + H - suffix);
+#pragma unroll
+        for (int j = 0; j < NL; j++) {
+          const float D = fast_exp2(-E * al2[j]);
+          mu[j] = fmaf(-gm * cm[j], D, mu[j]);
+        }
+        suffix += static_cast<double>(sm);
+      }
+      sigma += static_cast<double>(s);
+    }
+#pragma unroll
+    for (int j = 0; j < NL; j++) inc[j] = av[j] * mu[j];
+  }
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < NL; j++) a.umu[(k * P + p) * NN + n0 + j] = inc[j];
+  }
+}
+
+// Carry of the adjoint sums between chunks, right to left:
+//   carry[K-1] = 0,  carry[k-1] = A_k carry[k] + umu[k],  A_k = exp(-alpha sum_{t in k} s_t).
+// carry[k] is a_{e+1} mu_{e+1} for the last token e of chunk k.
+__global__ __launch_bounds__(256) void k_bwd_carry(int64_t K, int64_t P, int64_t N,
+                                                   const float* __restrict__ alpha,
+                                                   const double* __restrict__ ssum,
+                                                   const float* __restrict__ umu,
+                                                   float* __restrict__ carry) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t PN = P * N;
+  if (e >= PN) return;
+  const int64_t p = e / N;
+  const float al2 = alpha[e] * kLog2e;
+  float cin = 0.0f;
+#pragma unroll 8
+  for (int64_t k = K - 1; k >= 0; k--) {
+    carry[k * PN + e] = cin;
+    const float A = fast_exp2(-static_cast<float>(ssum[k * P + p]) * al2);
+    cin = fmaf(A, cin, umu[k * PN + e]);
+  }
+}
+
+// Main backward kernel: one workgroup = `wpb` wavefronts = wpb channel blocks
+// of the same chunk k.
+template <typename IO, int NL, int G, bool WIN>
+__global__ __launch_bounds__(256) void k_bwd_main(BwdArgs a, int64_t NBW) {
+  constexpr int CH = 64 / G;
+  constexpr int NN = NL * G;
+  constexpr int S = kSub;
+  constexpr int OUT = 2 * NN;  // db | dc outputs per token
+  extern __shared__ float lds[];
+  const int wpb = blockDim.x / 64;
+  const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int grp = lane / CH, pl = lane % CH;
+  const int64_t T = a.T, P = a.P, W = a.W;
+  const int C = a.C;
+  const int64_t k = blockIdx.x;
+  const int64_t cb = static_cast<int64_t>(blockIdx.y) * wpb + w;
+  const int64_t p = cb * CH + pl;
+  const bool valid = p < P;
+  const int64_t pc = valid ? p : P - 1;
+  const int n0 = grp * NL;
+  const int nsub_max = (C + S - 1) / S;  // LDS is sized for a full chunk
+  float* hsub = lds + static_cast<size_t>(w) * nsub_max * NL * 64;                     // [nsub][NL][64]
+  float* red = lds + static_cast<size_t>(wpb) * nsub_max * NL * 64 + w * (OUT * CH);   // [OUT][CH]
+  float* xw = lds + static_cast<size_t>(wpb) * (nsub_max * NL * 64 + OUT * CH);        // [wpb][S][OUT]
+  const IO* x = static_cast<const IO*>(a.x);
+
+  float al2[NL];
+#pragma unroll
+  for (int j = 0; j < NL; j++) al2[j] = a.alpha[pc * NN + n0 + j] * kLog2e;
+  const int64_t t0 = k * C;
+  const int64_t t1 = (t0 + C < T) ? t0 + C : T;
+  // sub-chunks of this chunk (the last chunk may be partial)
+  const int nsub = static_cast<int>((t1 - t0 + S - 1) / S);
+
+  // Phase 1: forward walk from the checkpoint, keep h at every sub-chunk start.
+  {
+    float h[NL];
+#pragma unroll
+    for (int j = 0; j < NL; j++) h[j] = a.h_ckpt[(k * P + pc) * NN + n0 + j];
+    for (int u = 0; u < nsub; u++) {
+#pragma unroll
+      for (int j = 0; j < NL; j++) hsub[(u * NL + j) * 64 + lane] = h[j];
+      if (u == nsub - 1) break;
+      const int64_t ta = t0 + static_cast<int64_t>(u) * S;
+      for (int64_t t = ta; t < ta + S; t++) {
+        const float ns = -a.s[t * P + pc];
+        const float xv = load_io(x + t * P + pc);
+        float bt[NL];
+        load_row<NL>(a.b + t * NN + n0, bt);
+#pragma unroll
+        for (int j = 0; j < NL; j++) h[j] = fmaf(fast_exp2(ns * al2[j]), h[j], bt[j] * xv);
+      }
+    }
+  }
+
+  // Phase 2: sub-chunks right to left.
+  float inc[NL], dal[NL];
+#pragma unroll
+  for (int j = 0; j < NL; j++) {
+    inc[j] = a.carry[(k * P + pc) * NN + n0 + j];
+    dal[j] = 0.0f;
+  }
+  float dbias_acc = 0.0f;
+  double H = 0.0, sigma = 0.0, suffix = 0.0;
+  if constexpr (WIN) H = a.hwin[k * P + pc];
+  const float inv_log2e = 1.0f / kLog2e;
+
+  for (int u = nsub - 1; u >= 0; u--) {
+    const int64_t ta = t0 + static_cast<int64_t>(u) * S;
+    const int len = static_cast<int>((t1 - ta < S) ? t1 - ta : S);
+    float hs[NL];
+#pragma unroll
+    for (int j = 0; j < NL; j++) hs[j] = hsub[(u * NL + j) * 64 + lane];
+    // recompute the sub-chunk's states into registers
+    float hr[S][NL];
+    {
+      float hh[NL];
+#pragma unroll
+      for (int j = 0; j < NL; j++) hh[j] = hs[j];
+#pragma unroll
+      for (int tau = 0; tau < S; tau++) {
+        if (tau < len) {
+          const int64_t t = ta + tau;
+          const float ns = -a.s[t * P + pc];
+          const float xv = load_io(x + t * P + pc);
+          float bt[NL];
+          load_row<NL>(a.b + t * NN + n0, bt);
+#pragma unroll
+          for (int j = 0; j < NL; j++) {
+            hh[j] = fmaf(fast_exp2(ns * al2[j]), hh[j], bt[j] * xv);
+            hr[tau][j] = hh[j];
+          }
+        }
+      }
+    }
+    // reverse walk with the local VJPs
+#pragma unroll
+    for (int tau = S - 1; tau >= 0; tau--) {
+      if (tau < len) {
+        const int64_t i = ta + tau;
+        const float s = a.s[i * P + pc];
+        const float xv = load_io(x + i * P + pc);
+        const float gv = a.g[i * P + pc];
+        float bt[NL], ct[NL];
+        load_row<NL>(a.b + i * NN + n0, bt);
+        load_row<NL>(a.c + i * NN + n0, ct);
+        float av[NL], mu[NL];
+#pragma unroll
+        for (int j = 0; j < NL; j++) {
+          av[j] = fast_exp2(-s * al2[j]);
+          mu[j] = fmaf(gv, ct[j], inc[j]);
+        }
+        if constexpr (WIN) {
+          const int64_t m = i + W;
+          if (m < T) {
+            const float sm = a.s[m * P + pc];
+            const float gm = a.g[m * P + pc];
+            float cm[NL];
+            load_row<NL>(a.c + m * NN + n0, cm);
+            const float E = static_cast<float>(sigma + H - suffix);
+#pragma unroll
+            for (int j = 0; j < NL; j++) {
+              const float D = fast_exp2(-E * al2[j]);
+              mu[j] = fmaf(-gm * cm[j], D, mu[j]);
+            }
+            suffix += static_cast<double>(sm);
+          }
+          sigma += static_cast<double>(s);
+        }
+        float ds = 0.0f, dxd = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NL; j++) {
+          const float hp = (tau > 0) ? hr[tau > 0 ? tau - 1 : 0][j] : hs[j];
+          const float tt = mu[j] * hp * av[j];
+          ds = fmaf(tt, al2[j], ds);
+          dal[j] = fmaf(tt, s, dal[j]);
+          dxd = fmaf(mu[j], bt[j], dxd);
+          inc[j] = av[j] * mu[j];
+        }
+        if constexpr (G > 1) {
+          ds = group_sum<G, CH>(ds);
+          dxd = group_sum<G, CH>(dxd);
+        }
+        const float dD = -(ds * inv_log2e) * one_minus_exp_neg(s);
+        if (valid && grp == 0) {
+          store_io(static_cast<IO*>(a.dY) + i * a.ldy + p, dD);
+          if (a.dxdir) a.dxdir[i * P + p] = dxd;
+        }
+        dbias_acc += dD;
+        // channel sums of db = mu x and dc = g h through an LDS transpose
+#pragma unroll
+        for (int j = 0; j < NL; j++) {
+          red[(n0 + j) * CH + pl] = valid ? mu[j] * xv : 0.0f;
+          red[(NN + n0 + j) * CH + pl] = valid ? gv * hr[tau][j] : 0.0f;
+        }
+        wave_lds_sync();
+        if constexpr (OUT <= 64) {
+          constexpr int LPO = 64 / OUT;  // lanes per output
+          constexpr int V = CH / LPO;    // values summed per lane
+          const int o = lane / LPO, r = lane % LPO;
+          const float* src = red + o * CH + r * V;
+          float sum = 0.0f;
+#pragma unroll
+          for (int v = 0; v < V; v++) sum += src[v];
+#pragma unroll
+          for (int d = 1; d < LPO; d <<= 1) sum += __shfl_xor(sum, d, 64);
+          if (r == 0) xw[(w * S + tau) * OUT + o] = sum;
+        } else {
+#pragma unroll
+          for (int q = 0; q < OUT / 64; q++) {
+            const int o = lane + 64 * q;
+            const float* src = red + o * CH;
+            float sum = 0.0f;
+#pragma unroll
+            for (int v = 0; v < CH; v++) sum += src[v];
+            xw[(w * S + tau) * OUT + o] = sum;
+          }
+        }
+        wave_lds_sync();
+      }
+    }
+    __syncthreads();
+    // sum over the workgroup's wavefronts -> one partial per (token, workgroup)
+    const int tot = len * OUT;
+    for (int idx = threadIdx.x; idx < tot; idx += blockDim.x) {
+      const int tau = idx / OUT, o = idx % OUT;
+      float v = 0.0f;
+      for (int ww = 0; ww < wpb; ww++) v += xw[(ww * S + tau) * OUT + o];
+      a.part[((ta + tau) * NBW + blockIdx.y) * OUT + o] = v;
+    }
+    __syncthreads();
+  }
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < NL; j++) a.dal_part[(k * P + p) * NN + n0 + j] = -dal[j];
+    if (grp == 0) a.dbias_part[k * P + p] = dbias_acc;
+  }
+}
+
+// db, dc: deterministic sum of the per-workgroup partials, written as the
+// io-typed columns [P, P+2N) of dY (the weight-gradient GEMM operand).
+template <typename IO>
+__global__ __launch_bounds__(256) void k_bwd_reduce_dbdc(int64_t T, int64_t P, int OUT, int64_t NBW,
+                                                         const float* __restrict__ part, IO* __restrict__ dY,
+                                                         int64_t ldy) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= T * OUT) return;
+  const int64_t t = e / OUT;
+  const int o = static_cast<int>(e % OUT);
+  const float* src = part + t * NBW * OUT + o;
+  float v = 0.0f;
+  for (int64_t wb = 0; wb < NBW; wb++) v += src[wb * OUT];
+  store_io(dY + t * ldy + P + o, v);
+}
+
+// dalpha = sum over chunks; dbias = sum over chunks (fixed order).
+__global__ __launch_bounds__(256) void k_bwd_reduce_chunks(int64_t K, int64_t P, int64_t N,
+                                                           const float* __restrict__ dal_part,
+                                                           const float* __restrict__ dbias_part,
+                                                           float* __restrict__ dalpha, float* __restrict__ dbias) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t PN = P * N;
+  if (dalpha && e < PN) {
+    float v = 0.0f;
+    for (int64_t k = 0; k < K; k++) v += dal_part[k * PN + e];
+    dalpha[e] = v;
+  }
+  if (dbias && e < P) {
+    float v = 0.0f;
+    for (int64_t k = 0; k < K; k++) v += dbias_part[k * P + e];
+    dbias[e] = v;
+  }
+}
+
+// ----------------------------------------------------------------- planning
+
+static void nl_g_for(int64_t N, int* NL, int* G) {
+  if (N <= 8) { *NL = static_cast<int>(N); *G = 1; }
+  else { *NL = 8; *G = static_cast<int>(N / 8); }
+}
+
+bool bwd_plan(int64_t P, int64_t N, int C, BwdPlan* pl) {
+  int NL, G;
+  nl_g_for(N, &NL, &G);
+  const int CH = 64 / G;
+  const int S = kSub;
+  const int nsub = (C + S - 1) / S;
+  const size_t per_wave = (static_cast<size_t>(nsub) * NL * 64 + 2 * N * CH + static_cast<size_t>(S) * 2 * N) * 4;
+  const size_t budget = 160 * 1024;
+  int wpb = static_cast<int>(budget / per_wave);
+  if (wpb > 4) wpb = 4;
+  if (wpb < 1) return false;
+  const int64_t NB = (P + CH - 1) / CH;
+  if (wpb > NB) wpb = static_cast<int>(NB);
+  pl->NL = NL; pl->G = G; pl->CH = CH; pl->S = S; pl->wpb = wpb;
+  pl->NB = NB;
+  pl->NBW = (NB + wpb - 1) / wpb;
+  pl->lds_bytes = per_wave * wpb;
+  return true;
+}
+
+// ----------------------------------------------------------------- launchers
+
+template <typename IO, int NL, int G, bool WIN>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+  constexpr int CH = 64 / G;
+  BwdPlan pl;
+  if (!bwd_plan(a.P, a.N, a.C, &pl)) return hipErrorInvalidValue;
+  const int64_t K = (a.T + a.C - 1) / a.C;
+  const int64_t NB = pl.NB;
+  hipError_t e;
+  if constexpr (WIN) {
+    k_bwd_prefix<<<static_cast<unsigned>((a.P + 255) / 256), 256, 0, st>>>(K, a.P, a.ssum, a.ps64);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  k_bwd_local<IO, NL, G, WIN><<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(NB)), 64, 0, st>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t PN = a.P * a.N;
+  k_bwd_carry<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, a.alpha, a.ssum, a.umu,
+                                                                      a.carry);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  auto kern = k_bwd_main<IO, NL, G, WIN>;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(pl.lds_bytes));
+  if (e != hipSuccess) return e;
+  kern<<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(pl.NBW)), pl.wpb * 64, pl.lds_bytes, st>>>(a, pl.NBW);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int OUT = 2 * static_cast<int>(a.N);
+  k_bwd_reduce_dbdc<IO><<<static_cast<unsigned>((a.T * OUT + 255) / 256), 256, 0, st>>>(
+      a.T, a.P, OUT, pl.NBW, a.part, static_cast<IO*>(a.dY), a.ldy);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.dalpha || a.dbias) {
+    k_bwd_reduce_chunks<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, a.dal_part,
+                                                                                a.dbias_part, a.dalpha, a.dbias);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  (void)CH;
+  return hipSuccess;
+}
+
+template <typename IO, bool WIN>
+static hipError_t launch_bwd_w(const BwdArgs& a, hipStream_t st) {
+  switch (a.N) {
+    case 1: return launch_bwd_t<IO, 1, 1, WIN>(a, st);
+    case 2: return launch_bwd_t<IO, 2, 1, WIN>(a, st);
+    case 4: return launch_bwd_t<IO, 4, 1, WIN>(a, st);
+    case 8: return launch_bwd_t<IO, 8, 1, WIN>(a, st);
+    case 16: return launch_bwd_t<IO, 8, 2, WIN>(a, st);
+    case 32: return launch_bwd_t<IO, 8, 4, WIN>(a, st);
+    case 64: return launch_bwd_t<IO, 8, 8, WIN>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_backward_scan(const BwdArgs& a, bool bf16, hipStream_t st) {
+  const bool win = a.W < a.T;
+  if (bf16) return win ? launch_bwd_w<bf16_t, true>(a, st) : launch_bwd_w<bf16_t, false>(a, st);
+  return win ? launch_bwd_w<float, true>(a, st) : launch_bwd_w<float, false>(a, st);
+}
+
+}  // namespace ssm

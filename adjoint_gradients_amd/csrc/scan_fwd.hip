@@ -1,0 +1,180 @@
+// scan_fwd.hip -- chunked, time-parallel forward scan of the selective SSM
+// recurrence on gfx950.
+//
+// Recurrence (review of "Adjoint sharding for very long context training of
+// state space models", Assumptions / Section 3.1), diagonal per channel p:
+//   a_t[p][n] = exp(-s_t[p] alpha[p][n]),   s = softplus(Delta)
+//   h_t[p][n] = a_t[p][n] h_{t-1}[p][n] + b_t[n] x_t[p]
+//   y_t[p]    = sum_n c_t[n] h_t[p][n]
+// Time is cut into chunks of C tokens.  Three launches:
+//   1. k_fwd_local : every (chunk, channel block) scans its chunk from h = 0
+//                    and records the end state and sum_t s_t (fp64).
+//   2. k_fwd_carry : one thread per (p, n) walks the chunks in order and
+//                    composes the affine chunk maps h -> A_k h + hloc_k with
+//                    A_k = exp(-alpha sum_{t in k} s_t); it writes the state
+//                    entering every chunk, h_{kC-1}, which is also the saved
+//                    checkpoint (store at segment boundaries, recompute inside:
+//                    review of "Training Deep Nets with Sublinear Memory Cost",
+//                    What carries the argument).
+//   3. k_fwd_final : every (chunk, channel block) rescans its chunk from the
+//                    exact entering state and writes y.
+#include "ssm_common.hpp"
+#include "ssm_kernels.hpp"
+
+namespace ssm {
+
+template <int NL>
+__device__ __forceinline__ void load_row(const float* __restrict__ src, float (&dst)[NL]) {
+  if constexpr (NL % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < NL; j += 4) {
+      float4 v = *reinterpret_cast<const float4*>(src + j);
+      dst[j] = v.x; dst[j + 1] = v.y; dst[j + 2] = v.z; dst[j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NL; j++) dst[j] = src[j];
+  }
+}
+
+template <typename IO, int NL, int G>
+__global__ __launch_bounds__(64) void k_fwd_local(int64_t T, int64_t P, int64_t N, int C,
+                                                  const float* __restrict__ sp, const IO* __restrict__ x,
+                                                  const float* __restrict__ b, const float* __restrict__ alpha,
+                                                  float* __restrict__ hloc, double* __restrict__ ssum) {
+  constexpr int CH = 64 / G;
+  const int lane = threadIdx.x;
+  const int grp = lane / CH, pl = lane % CH;
+  const int64_t k = blockIdx.x;
+  const int64_t p = static_cast<int64_t>(blockIdx.y) * CH + pl;
+  const bool valid = p < P;
+  const int64_t pc = valid ? p : P - 1;
+  const int n0 = grp * NL;
+  float al2[NL];
+#pragma unroll
+  for (int j = 0; j < NL; j++) al2[j] = alpha[pc * N + n0 + j] * kLog2e;
+  float h[NL];
+#pragma unroll
+  for (int j = 0; j < NL; j++) h[j] = 0.0f;
+  double ss = 0.0;
+  const int64_t t0 = k * C;
+  const int64_t t1 = (t0 + C < T) ? t0 + C : T;
+  for (int64_t t = t0; t < t1; t++) {
+    const float ns = -sp[t * P + pc];
+    const float xv = load_io(x + t * P + pc);
+    float bt[NL];
+    load_row<NL>(b + t * N + n0, bt);
+#pragma unroll
+    for (int j = 0; j < NL; j++) {
+      const float a = fast_exp2(ns * al2[j]);
+      h[j] = fmaf(a, h[j], bt[j] * xv);
+    }
+    ss -= static_cast<double>(ns);
+  }
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < NL; j++) hloc[(k * P + p) * N + n0 + j] = h[j];
+    if (grp == 0) ssum[k * P + p] = ss;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fwd_carry(int64_t K, int64_t P, int64_t N,
+                                                   const float* __restrict__ alpha,
+                                                   const double* __restrict__ ssum,
+                                                   const float* __restrict__ hloc,
+                                                   float* __restrict__ h_ckpt) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t PN = P * N;
+  if (e >= PN) return;
+  const int64_t p = e / N;
+  const float al2 = alpha[e] * kLog2e;
+  float hin = 0.0f;
+#pragma unroll 8
+  for (int64_t k = 0; k < K; k++) {
+    h_ckpt[k * PN + e] = hin;
+    const float A = fast_exp2(-static_cast<float>(ssum[k * P + p]) * al2);
+    hin = fmaf(A, hin, hloc[k * PN + e]);
+  }
+}
+
+template <typename IO, int NL, int G>
+__global__ __launch_bounds__(64) void k_fwd_final(int64_t T, int64_t P, int64_t N, int C,
+                                                  const float* __restrict__ sp, const IO* __restrict__ x,
+                                                  const float* __restrict__ b, const float* __restrict__ c,
+                                                  const float* __restrict__ alpha,
+                                                  const float* __restrict__ h_ckpt, float* __restrict__ y) {
+  constexpr int CH = 64 / G;
+  const int lane = threadIdx.x;
+  const int grp = lane / CH, pl = lane % CH;
+  const int64_t k = blockIdx.x;
+  const int64_t p = static_cast<int64_t>(blockIdx.y) * CH + pl;
+  const bool valid = p < P;
+  const int64_t pc = valid ? p : P - 1;
+  const int n0 = grp * NL;
+  float al2[NL], h[NL];
+#pragma unroll
+  for (int j = 0; j < NL; j++) {
+    al2[j] = alpha[pc * N + n0 + j] * kLog2e;
+    h[j] = h_ckpt[(k * P + pc) * N + n0 + j];
+  }
+  const int64_t t0 = k * C;
+  const int64_t t1 = (t0 + C < T) ? t0 + C : T;
+  for (int64_t t = t0; t < t1; t++) {
+    const float ns = -sp[t * P + pc];
+    const float xv = load_io(x + t * P + pc);
+    float bt[NL], ct[NL];
+    load_row<NL>(b + t * N + n0, bt);
+    load_row<NL>(c + t * N + n0, ct);
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NL; j++) {
+      const float a = fast_exp2(ns * al2[j]);
+      h[j] = fmaf(a, h[j], bt[j] * xv);
+      acc = fmaf(ct[j], h[j], acc);
+    }
+    acc = group_sum<G, CH>(acc);
+    if (valid && grp == 0) y[t * P + p] = acc;
+  }
+}
+
+// ----------------------------------------------------------------- launchers
+
+template <typename IO, int NL, int G>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  constexpr int CH = 64 / G;
+  const int64_t NB = (a.P + CH - 1) / CH;
+  const int64_t K = (a.T + a.C - 1) / a.C;
+  dim3 grid(static_cast<unsigned>(K), static_cast<unsigned>(NB));
+  k_fwd_local<IO, NL, G><<<grid, 64, 0, st>>>(a.T, a.P, a.N, a.C, a.s, static_cast<const IO*>(a.x), a.b,
+                                              a.alpha, a.hloc, a.ssum);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t PN = a.P * a.N;
+  k_fwd_carry<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, a.alpha, a.ssum, a.hloc,
+                                                                      a.h_ckpt);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_fwd_final<IO, NL, G><<<grid, 64, 0, st>>>(a.T, a.P, a.N, a.C, a.s, static_cast<const IO*>(a.x), a.b, a.c,
+                                              a.alpha, a.h_ckpt, a.y);
+  return hipGetLastError();
+}
+
+template <typename IO>
+static hipError_t launch_fwd_io(const FwdArgs& a, hipStream_t st) {
+  switch (a.N) {
+    case 1: return launch_fwd_t<IO, 1, 1>(a, st);
+    case 2: return launch_fwd_t<IO, 2, 1>(a, st);
+    case 4: return launch_fwd_t<IO, 4, 1>(a, st);
+    case 8: return launch_fwd_t<IO, 8, 1>(a, st);
+    case 16: return launch_fwd_t<IO, 8, 2>(a, st);
+    case 32: return launch_fwd_t<IO, 8, 4>(a, st);
+    case 64: return launch_fwd_t<IO, 8, 8>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_forward_scan(const FwdArgs& a, bool bf16, hipStream_t st) {
+  return bf16 ? launch_fwd_io<bf16_t>(a, st) : launch_fwd_io<float>(a, st);
+}
+
+}  // namespace ssm

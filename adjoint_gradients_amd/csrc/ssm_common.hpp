@@ -1,0 +1,77 @@
+// ssm_common.hpp -- device helpers shared by the gfx950 kernels of the
+// selective-SSM adjoint-gradient library.
+//
+// Lane layout of every scan kernel (one 64-wide wavefront):
+//   G  = N / NL lane groups, each group holds NL consecutive states n;
+//   CH = 64 / G channels per wavefront;
+//   lane = grp * CH + pl  (grp in [0,G), pl in [0,CH)),  channel p = cb*CH + pl.
+// Per-channel values (s, x, g) are therefore read by G lanes at the same
+// address (served by L1 as a broadcast), per-token state values (b_t, c_t)
+// by the CH lanes of a group.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// float -> bfloat16, round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return static_cast<bf16_t>((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_io(const T* p);
+template <> __device__ __forceinline__ float load_io<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load_io<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
+
+template <typename T> __device__ __forceinline__ void store_io(T* p, float v);
+template <> __device__ __forceinline__ void store_io<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void store_io<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+
+// 2^x on the hardware transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// softplus(d) = max(d,0) + log(1 + e^{-|d|}), computed in float.
+__device__ __forceinline__ float softplus_f(float d) {
+  float e = __expf(-fabsf(d));
+  return fmaxf(d, 0.0f) + log1pf(e);
+}
+
+// 1 - e^{-s} for s >= 0, i.e. the logistic sigmoid of Delta when s = softplus(Delta).
+// Taylor series below 0.5 avoids the cancellation of 1 - e^{-s} for small s.
+__device__ __forceinline__ float one_minus_exp_neg(float s) {
+  if (s > 0.5f) return 1.0f - fast_exp2(-s * kLog2e);
+  // s - s^2/2! + s^3/3! - ... (truncation < s^10/10! < 3e-10)
+  float t = s;
+  float sum = s;
+#pragma unroll
+  for (int k = 2; k <= 9; k++) {
+    t *= -s / static_cast<float>(k);
+    sum += t;
+  }
+  return sum;
+}
+
+// Sum over the G lane groups of one channel (lanes pl, pl+CH, pl+2CH, ...).
+template <int G, int CH>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int d = CH; d < 64; d <<= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+}  // namespace ssm

@@ -1,0 +1,96 @@
+// ssm_kernels.hpp -- internal launch interface between the C ABI (api.hip)
+// and the kernel files.  Host-side declarations only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+struct FwdArgs {
+  int64_t T, P, N;
+  int C;
+  const float* s;       // [T][P] softplus(Delta)
+  const void* x;        // [T][P] io
+  const float* b;       // [T][N]
+  const float* c;       // [T][N]
+  const float* alpha;   // [P][N]
+  float* hloc;          // [K][P][N] workspace
+  double* ssum;         // [K][P]   per-chunk sum of s (saved)
+  float* h_ckpt;        // [K][P][N] saved
+  float* y;             // [T][P]
+};
+
+struct BwdArgs {
+  int64_t T, P, N, W;   // W: window (>= T means exact)
+  int C;
+  const float* s;       // [T][P]
+  const void* x;        // [T][P] io
+  const float* b;       // [T][N]
+  const float* c;       // [T][N]
+  const float* alpha;   // [P][N]
+  const float* h_ckpt;  // [K][P][N]
+  const double* ssum;   // [K][P]
+  const float* g;       // [T][P]
+  // workspace
+  double* ps64;         // [K+1][P] prefix sums of ssum over chunks (windowed)
+  double* hwin;         // [K][P]   sum of s over the W tokens after each chunk (windowed)
+  float* umu;           // [K][P][N] local adjoint aggregates
+  float* carry;         // [K][P][N] adjoint carry entering each chunk from the right
+  float* part;          // [T][NBW][2N] per-workgroup partial sums of db | dc
+  float* dal_part;      // [K][P][N]
+  float* dbias_part;    // [K][P]
+  // outputs of the scan
+  void* dY;             // [T][ldy] io: columns [0,P) = dDelta, [P,P+N) = db, [P+N,P+2N) = dc
+  int64_t ldy;
+  float* dxdir;         // [T][P] or nullptr
+  float* dalpha;        // [P][N] or nullptr
+  float* dbias;         // [P] or nullptr
+};
+
+// Layout queries of the backward scan (shared by the workspace planner).
+struct BwdPlan {
+  int NL, G, CH, S;
+  int wpb;              // waves per workgroup of the main kernel
+  int64_t NB;           // channel blocks (of CH channels)
+  int64_t NBW;          // workgroups along channels = ceil(NB / wpb)
+  size_t lds_bytes;     // dynamic LDS of the main kernel
+};
+bool bwd_plan(int64_t P, int64_t N, int C, BwdPlan* plan);
+
+hipError_t launch_forward_scan(const FwdArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_backward_scan(const BwdArgs& a, bool bf16, hipStream_t st);
+
+// ---------------------------------------------------------------- GEMMs
+// C[M][Nc] = sum_k A(m,k) B(k,n) on MFMA, with one of three epilogues.
+//   A(m,k) = a_kc ? A[m*lda + k] : A[k*lda + m]
+//   B(k,n) = b_kc ? B[n*ldb + k] : B[k*ldb + n]
+struct GemmOperands {
+  int64_t M, Nc, K;
+  const void* A; int64_t lda; bool a_kc;
+  const void* B; int64_t ldb; bool b_kc;
+};
+
+// Projection epilogue: columns [0,P) -> s = softplus(v + bias), [P,P+N) -> b, [P+N,P+2N) -> c.
+struct EpiProjArgs { int64_t P, N; const float* bias; float* s; float* b; float* c; };
+hipError_t gemm_projection(const GemmOperands& op, bool bf16, const EpiProjArgs& e, hipStream_t st);
+
+// Split-K partial sums: part[z][M][Nc] for z < splits.
+hipError_t gemm_splitk(const GemmOperands& op, bool bf16, int splits, float* part, hipStream_t st);
+
+// Input-cotangent epilogue: out[m][n] = v + add0[m][n] (+ add1[m][n]); ld = Nc.
+struct EpiAddArgs { const float* add0; const float* add1; float* out; };
+hipError_t gemm_add(const GemmOperands& op, bool bf16, const EpiAddArgs& e, hipStream_t st);
+
+// Sum of the split-K partials into the three weight-gradient outputs
+// (rows [0,P) -> dW_delta, [P,P+N) -> dW_B, [P+N,P+2N) -> dW_C).
+hipError_t reduce_weight_grads(const float* part, int splits, int64_t P, int64_t N, float* dWd, float* dWb,
+                               float* dWc, hipStream_t st);
+
+// ---------------------------------------------------------------- stack helpers
+// r += y (if y) ; xio = io(r)
+hipError_t residual_update(int64_t n, float* r, const float* y, void* xio, bool bf16, hipStream_t st);
+// r = io value of x0 (float32 residual stream initialised from the io input)
+hipError_t residual_init(int64_t n, const void* x0, bool bf16, float* r, hipStream_t st);
+
+}  // namespace ssm

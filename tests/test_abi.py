@@ -1,0 +1,159 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, sizes its buffers, and rejects bad arguments before any
+HIP call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_adjoint.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def agm():
+    lib = os.path.join(ROOT, "adjoint_gradients_amd", "libssm_adjoint.so")
+    if not os.path.exists(lib):
+        pytest.fail("libssm_adjoint.so not built (run __graft_entry__.build())")
+    import adjoint_gradients_amd as agm
+
+    return agm
+
+
+def test_header_functions_are_exported(agm):
+    names = _declared_functions()
+    assert set(names) == set(agm.EXPORTED), names
+    for n in names:
+        assert hasattr(agm.lib, n), n
+
+
+def test_version_and_status_strings(agm):
+    assert agm.ssm_version() >= 100
+    for code, name in agm.STATUS.items():
+        assert agm.ssm_status_str(code).startswith(name)
+    assert agm.ssm_status_str(99) == "SSM_ERR_UNKNOWN"
+
+
+def test_sizes(agm):
+    d = agm.make_dims(1000, 48, 16, 64, "bf16")
+    K = (1000 + 63) // 64
+    saved = agm.ssm_saved_bytes(d)
+    # s [T][P] f32, b and c [T][N] f32, h_ckpt [K][P][N] f32, s_sum [K][P] f64 (each 256-byte aligned)
+    raw = 1000 * 48 * 4 + 2 * 1000 * 16 * 4 + K * 48 * 16 * 4 + K * 48 * 8
+    assert raw <= saved <= raw + 5 * 256
+    fwd = agm.ssm_workspace_bytes(d, 0, 0)
+    bwd = agm.ssm_workspace_bytes(d, 100, 0)
+    stk = agm.ssm_workspace_bytes(d, 100, 3)
+    assert 0 < fwd < bwd < stk
+    assert stk > 3 * saved
+
+
+@pytest.mark.parametrize("T,P,N,C,io", [
+    (0, 8, 4, 16, 0), (8, 0, 4, 16, 0), (8, 8, 0, 16, 0), (8, 8, 4, 0, 0),
+])
+def test_sizes_reject_bad_dims(agm, T, P, N, C, io):
+    d = agm.Dims(T, P, N, C, io)
+    assert agm.ssm_saved_bytes(d) == 0
+    assert agm.ssm_workspace_bytes(d, 0, 0) == 0
+
+
+@pytest.mark.parametrize("N,C,io", [(3, 16, 0), (128, 16, 0), (16, 513, 0), (16, 16, 2)])
+def test_sizes_reject_unsupported(agm, N, C, io):
+    d = agm.Dims(64, 8, N, C, io)
+    assert agm.ssm_workspace_bytes(d, 0, 0) == 0
+
+
+def _fake(addr=0x100000):
+    """A non-null, 256-aligned fake device address (never dereferenced: every
+    call below fails validation before any launch)."""
+    return ctypes.c_void_p(addr)
+
+
+def _layer(agm, misalign=False):
+    a = 0x200000 + (4 if misalign else 0)
+    return agm.Layer(a, 0x300000, 0x400000, 0x500000, None)
+
+
+def _saved(agm, null_field=None):
+    vals = dict(s=0x600000, b=0x700000, c=0x800000, h_ckpt=0x900000, s_sum=0xA00000)
+    if null_field:
+        vals[null_field] = None
+    return agm.Saved(**vals)
+
+
+def _grads(agm, null_field=None):
+    vals = dict(dW_delta=0xB00000, dW_B=0xC00000, dW_C=0xD00000, dalpha=None, dbias=None, dx=None)
+    if null_field:
+        vals[null_field] = None
+    return agm.Grads(**vals)
+
+
+def _fwd(agm, d, layer, x, y, saved, ws, nbytes):
+    return agm.lib.ssm_forward(ctypes.byref(d), ctypes.byref(layer) if layer is not None else None, x, y,
+                               ctypes.byref(saved) if saved is not None else None, ws, nbytes, None)
+
+
+def test_forward_validation(agm):
+    d = agm.make_dims(64, 8, 4, 16)
+    need = agm.ssm_workspace_bytes(d, 0, 0)
+    L, S = _layer(agm), _saved(agm)
+    x, y, ws = 0x1000000, 0x2000000, 0x3000000
+    assert _fwd(agm, agm.Dims(0, 8, 4, 16, 0), L, x, y, S, ws, need) == 1
+    assert _fwd(agm, agm.Dims(64, 8, 5, 16, 0), L, x, y, S, ws, need) == 4
+    assert _fwd(agm, d, None, x, y, S, ws, need) == 1
+    assert _fwd(agm, d, _layer(agm, misalign=True), x, y, S, ws, need) == 1
+    assert _fwd(agm, d, L, None, y, S, ws, need) == 1
+    assert _fwd(agm, d, L, x, None, S, ws, need) == 1
+    assert _fwd(agm, d, L, x + 2, y, S, ws, need) == 1
+    for f in ("s", "b", "c", "h_ckpt", "s_sum"):
+        assert _fwd(agm, d, L, x, y, _saved(agm, f), ws, need) == 1, f
+    assert _fwd(agm, d, L, x, y, S, None, need) == 2
+    assert _fwd(agm, d, L, x, y, S, ws, need - 1) == 2
+    assert _fwd(agm, d, L, x, y, S, ws + 16, need) == 2
+
+
+def test_adjoint_validation(agm):
+    d = agm.make_dims(64, 8, 4, 16)
+    L, S = _layer(agm), _saved(agm)
+    x, g, ws = 0x1000000, 0x2000000, 0x3000000
+    need = agm.ssm_workspace_bytes(d, 8, 0)
+
+    def call(window=8, grads=None, nbytes=need, wsp=ws, gp=g):
+        G = grads if grads is not None else _grads(agm)
+        return agm.lib.ssm_adjoint_grad(ctypes.byref(d), ctypes.byref(L), x, ctypes.byref(S), gp, window,
+                                        ctypes.byref(G), wsp, nbytes, None)
+
+    assert call(window=0) == 1
+    assert call(window=-5) == 1
+    assert call(gp=None) == 1
+    for f in ("dW_delta", "dW_B", "dW_C"):
+        assert call(grads=_grads(agm, f)) == 1, f
+    assert call(nbytes=256) == 2
+    assert call(wsp=None) == 2
+
+
+def test_stack_validation(agm):
+    d = agm.make_dims(64, 8, 4, 16)
+    K = 2
+    layers = (agm.Layer * K)(_layer(agm), _layer(agm))
+    grads = (agm.Grads * K)(_grads(agm), _grads(agm))
+    need = agm.ssm_workspace_bytes(d, 8, K)
+    x0, g, ws = 0x1000000, 0x2000000, 0x3000000
+
+    def call(K=K, window=8, ls=layers, gs=grads, nbytes=need):
+        return agm.lib.ssm_stack_grad(K, ctypes.byref(d), ls, x0, g, window, gs, None, None, ws, nbytes, None)
+
+    assert call(K=0) == 1
+    assert call(window=0) == 1
+    bad = (agm.Layer * K)(_layer(agm), _layer(agm, misalign=True))
+    assert call(ls=bad) == 1
+    with_dx = (agm.Grads * K)(_grads(agm), agm.Grads(0xB00000, 0xC00000, 0xD00000, None, None, 0xE00000))
+    assert call(gs=with_dx) == 1
+    assert call(nbytes=256) == 2

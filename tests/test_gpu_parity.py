@@ -1,0 +1,145 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerance: per-tensor max|gpu - ref| / max|ref| <= 1e-4 for fp32 inputs and
+<= 2e-2 for bf16 inputs with fp32 state.  Every case prints its label before
+running so a failure names it.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import GRAD_KEYS, TOL, compare, gpu_layer, oracle_inputs, rel_err, say
+from ssm_inputs import CONFIGS, LayerCase, make_layer, make_stack, small_case, window_pin_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import adjoint_gradients_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+
+    oracle.build(force=False)
+    return oracle
+
+
+def _run_case(orc, inp, window, chunk, label, tol=None):
+    say(f"case {label}: T={inp['x'].shape[0]} P={inp['x'].shape[1]} N={inp['W_B'].shape[0]} "
+        f"io={inp['io']} W={window} C={chunk}")
+    tol = tol if tol is not None else TOL[inp["io"]]
+    got = gpu_layer(inp, window, chunk)
+    o = oracle_inputs(inp)
+    T = inp["x"].shape[0]
+    ref = orc.layer_grad(o, window=None if window >= T else window)
+    compare(got, ref, GRAD_KEYS, tol, label)
+    # saved state: s = softplus(Delta), b, c, checkpoints
+    s_ref = np.logaddexp(0.0, ref["delta"])
+    assert rel_err(got["saved_s"], s_ref) <= tol
+    assert rel_err(got["saved_b"], ref["b"]) <= tol
+    assert rel_err(got["saved_c"], ref["c"]) <= tol
+    hck = orc.forward(o, C=chunk)["h_ckpt"]
+    assert rel_err(got["saved_h_ckpt"], hck) <= tol
+    return got, ref
+
+
+def test_cfg0_exact(orc):
+    inp = make_layer(CONFIGS[0])
+    _run_case(orc, inp, 256, 256, "cfg0 W=T")
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 16, 100, 256, 512])
+def test_chunk_invariance_ragged(orc, chunk):
+    inp = make_layer(small_case(300, 40, 8, 5))
+    _run_case(orc, inp, 300, chunk, f"ragged C={chunk}")
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 16, 32, 64])
+def test_state_sizes(orc, N):
+    inp = make_layer(small_case(200, 70, N, 6 + N))
+    _run_case(orc, inp, 200, 32, f"N={N}")
+    _run_case(orc, inp, 37, 32, f"N={N} W=37")
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 7, 64, 255, 256, 511, 512, 513])
+def test_window_pinning(orc, W):
+    """Slow decay: adjacent windows differ by far more than the tolerance."""
+    inp = make_layer(window_pin_case(seed=100, T=512, P=8, N=4))
+    got, ref = _run_case(orc, inp, W, 64, f"winpin W={W}")
+    if W < 512:
+        exact = orc.layer_grad(oracle_inputs(inp), window=None)
+        gap = rel_err(ref["dx"], exact["dx"])
+        say(f"  window-vs-exact gap (dx) = {gap:.2e}")
+
+
+@pytest.mark.parametrize("chunk", [7, 64, 200])
+def test_window_chunk_not_dividing(orc, chunk):
+    inp = make_layer(window_pin_case(seed=101, T=700, P=8, N=4))
+    for W in (5, 130, 333):
+        _run_case(orc, inp, W, chunk, f"winpin C={chunk} W={W}")
+
+
+def test_bf16_small(orc):
+    c = small_case(1024, 96, 16, 9, io="bf16")
+    inp = make_layer(c)
+    _run_case(orc, inp, 1024, 256, "bf16 W=T")
+    _run_case(orc, inp, 200, 256, "bf16 W=200")
+
+
+def test_determinism_and_linearity():
+    import adjoint_gradients_amd as agm  # noqa: F401
+
+    inp = make_layer(small_case(500, 80, 16, 12))
+    a = gpu_layer(inp, 120, 64)
+    b = gpu_layer(inp, 120, 64)
+    for k in ("dW_delta", "dW_B", "dW_C", "dalpha", "dbias", "dx", "y"):
+        assert np.array_equal(a[k], b[k]), k
+    c = gpu_layer(inp, 120, 64, g=2.0 * inp["g"])
+    for k in ("dW_delta", "dW_B", "dW_C", "dalpha", "dbias", "dx"):
+        assert np.array_equal(c[k], 2.0 * a[k]), k
+
+
+def test_cfg1(orc):
+    inp = make_layer(CONFIGS[1])
+    for W in (16384, 2048):
+        _run_case(orc, inp, W, 256, f"cfg1 W={W}")
+
+
+def _gpu_stack(st, window, chunk):
+    import torch
+
+    import adjoint_gradients_amd as agm
+    from gpu_util import layer_tensors, to_dev
+
+    io = st["io"]
+    T, P = st["x"].shape
+    N = st["layers"][0]["W_B"].shape[0]
+    dims = agm.make_dims(T, P, N, chunk, io)
+    lays = [layer_tensors(lay, io) for lay in st["layers"]]
+    grads, dx0, xK = agm.stack_grad(dims, lays, to_dev(st["x"], io), to_dev(st["g"]), window)
+    torch.cuda.synchronize()
+    return ([{k: v.double().cpu().numpy() for k, v in g.items()} for g in grads],
+            dx0.double().cpu().numpy(), xK.double().cpu().numpy())
+
+
+@pytest.mark.parametrize("io,window", [("f32", 256), ("f32", 50), ("bf16", 256), ("bf16", 50)])
+def test_stack(orc, io, window):
+    c = LayerCase("stack_small", 256, 48, 16, io, (), K=3, seed=40)
+    st = make_stack(c)
+    say(f"case stack K=3 io={io} W={window}")
+    grads, dx0, xK = _gpu_stack(st, window, 64)
+    st64 = dict(st, x=np.asarray(st["x"], np.float64), g=np.asarray(st["g"], np.float64),
+                layers=[{k: np.asarray(v, np.float64) for k, v in lay.items()} for lay in st["layers"]])
+    ref = orc.stack_grad(st64, window=None if window >= 256 else window)
+    tol = TOL[io]
+    for k in range(3):
+        compare(grads[k], ref["layers"][k], [(n, n) for n in ("dW_delta", "dW_B", "dW_C", "dalpha", "dbias")],
+                tol, f"stack layer {k}")
+    assert rel_err(dx0, ref["dx0"]) <= tol
+    assert rel_err(xK, ref["forward"]["r_final"]) <= tol

@@ -32,6 +32,8 @@ EXPORTED = (
     "ssm_forward",
     "ssm_adjoint_grad",
     "ssm_stack_grad",
+    "ssm_forward_timed",
+    "ssm_adjoint_grad_timed",
 )
 
 
@@ -86,6 +88,11 @@ def _load():
                                    ctypes.c_int64, P(Grads), ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.ssm_stack_grad.restype = ctypes.c_int
+    VP = ctypes.POINTER(ctypes.c_void_p)
+    lib.ssm_forward_timed.argtypes = lib.ssm_forward.argtypes + [VP, ctypes.c_int32]
+    lib.ssm_forward_timed.restype = ctypes.c_int
+    lib.ssm_adjoint_grad_timed.argtypes = lib.ssm_adjoint_grad.argtypes + [VP, ctypes.c_int32]
+    lib.ssm_adjoint_grad_timed.restype = ctypes.c_int
     return lib
 
 
@@ -155,6 +162,30 @@ def ssm_adjoint_grad(dims: Dims, layer: Layer, x, saved: Saved, g, window: int, 
     _check(lib.ssm_adjoint_grad(ctypes.byref(dims), ctypes.byref(layer), _ptr(x), ctypes.byref(saved), _ptr(g),
                                 int(window), ctypes.byref(grads), _ptr(ws), int(ws_bytes), _stream(stream)),
            "ssm_adjoint_grad")
+
+
+def _event_array(events):
+    """torch.cuda.Event objects (or None) -> C array of hipEvent_t handles."""
+    arr = (ctypes.c_void_p * len(events))()
+    for i, ev in enumerate(events):
+        arr[i] = None if ev is None else int(ev.cuda_event)
+    return arr
+
+
+def ssm_forward_timed(dims: Dims, layer: Layer, x, y, saved: Saved, ws, ws_bytes: int, events, stream=None):
+    arr = _event_array(events)
+    _check(lib.ssm_forward_timed(ctypes.byref(dims), ctypes.byref(layer), _ptr(x), _ptr(y), ctypes.byref(saved),
+                                 _ptr(ws), int(ws_bytes), _stream(stream), arr, len(events)),
+           "ssm_forward_timed")
+
+
+def ssm_adjoint_grad_timed(dims: Dims, layer: Layer, x, saved: Saved, g, window: int, grads: Grads, ws,
+                           ws_bytes: int, events, stream=None):
+    arr = _event_array(events)
+    _check(lib.ssm_adjoint_grad_timed(ctypes.byref(dims), ctypes.byref(layer), _ptr(x), ctypes.byref(saved),
+                                      _ptr(g), int(window), ctypes.byref(grads), _ptr(ws), int(ws_bytes),
+                                      _stream(stream), arr, len(events)),
+           "ssm_adjoint_grad_timed")
 
 
 def ssm_stack_grad(K: int, dims: Dims, layers, x0, g, window: int, grads, dx0, xK, ws, ws_bytes: int,

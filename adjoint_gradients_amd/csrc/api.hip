@@ -203,15 +203,18 @@ hipError_t pack_wcat(const ssm_dims* d, const ssm_layer* L, void* wcat, hipStrea
 }
 
 hipError_t run_forward(const ssm_dims* d, const ssm_layer* L, const void* x, float* y, const ssm_saved* sv,
-                       const FwdWs& w, hipStream_t st) {
+                       const FwdWs& w, hipStream_t st, ssm::Marks mk = {}) {
   const bool bf = d->io == SSM_BF16;
+  mk.rec(0, st);
   hipError_t e = pack_wcat(d, L, w.wcat, st);
   if (e != hipSuccess) return e;
   ssm::GemmOperands op{d->T, d->P + 2 * d->N, d->P, x, d->P, true, w.wcat, d->P, true};
   ssm::EpiProjArgs ep{d->P, d->N, L->delta_bias, sv->s, sv->b, sv->c};
   e = ssm::gemm_projection(op, bf, ep, st);
   if (e != hipSuccess) return e;
+  mk.rec(1, st);
   FwdArgs fa{d->T, d->P, d->N, d->chunk, sv->s, x, sv->b, sv->c, L->alpha, w.hloc, sv->s_sum, sv->h_ckpt, y};
+  fa.marks = mk;
   return ssm::launch_forward_scan(fa, bf, st);
 }
 
@@ -219,7 +222,8 @@ hipError_t run_forward(const ssm_dims* d, const ssm_layer* L, const void* x, flo
 // delta_io <- delta_io + dx; otherwise dx goes to grads->dx when requested.
 hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, const ssm_saved* sv,
                         const float* g, int64_t W, const ssm_grads* gr, float* delta_io, const BwdWs& w,
-                        hipStream_t st) {
+                        hipStream_t st, ssm::Marks mk = {}) {
+  mk.rec(0, st);
   const bool bf = d->io == SSM_BF16;
   const int64_t T = d->T, P = d->P, N = d->N;
   const int64_t M = P + 2 * N;
@@ -233,6 +237,7 @@ hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, co
   a.dY = w.dY; a.ldy = M;
   a.dxdir = need_dx ? w.dxdir : nullptr;
   a.dalpha = gr->dalpha; a.dbias = gr->dbias;
+  a.marks = mk;
   hipError_t e = ssm::launch_backward_scan(a, bf, st);
   if (e != hipSuccess) return e;
   // dW_cat = dY^T X  (K = T, both operands token-major)
@@ -241,6 +246,7 @@ hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, co
   if (e != hipSuccess) return e;
   e = ssm::reduce_weight_grads(w.wpart, w.splits, P, N, gr->dW_delta, gr->dW_B, gr->dW_C, st);
   if (e != hipSuccess) return e;
+  mk.rec(5, st);
   if (need_dx) {
     e = pack_wcat(d, L, w.wcat, st);
     if (e != hipSuccess) return e;
@@ -249,6 +255,7 @@ hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, co
     ssm::EpiAddArgs ea{w.dxdir, delta_io, delta_io ? delta_io : gr->dx};
     e = ssm::gemm_add(opx, bf, ea, st);
   }
+  mk.rec(6, st);
   return e;
 }
 
@@ -287,23 +294,24 @@ size_t ssm_workspace_bytes(const ssm_dims* d, int64_t window, int32_t K) {
   return bwd_ws_bytes(d, window, true);
 }
 
-ssm_status ssm_forward(const ssm_dims* d, const ssm_layer* L, const void* x, float* y, const ssm_saved* sv,
-                       void* ws, size_t ws_bytes, void* stream) {
+static ssm_status forward_impl(const ssm_dims* d, const ssm_layer* L, const void* x, float* y,
+                               const ssm_saved* sv, void* ws, size_t ws_bytes, void* stream, ssm::Marks mk) {
   ssm_status s = check_dims(d);
   if (s != SSM_OK) return s;
   if ((s = check_layer(L)) != SSM_OK) return s;
   if ((s = check_saved(sv)) != SSM_OK) return s;
   if (!x || !y || !aligned16(x) || !aligned16(y)) return SSM_ERR_ARG;
+  if (mk.n < 0 || (mk.n > 0 && !mk.ev)) return SSM_ERR_ARG;
   if ((s = check_ws(ws, ws_bytes, fwd_ws_bytes(d))) != SSM_OK) return s;
   Carver cv(ws);
   FwdWs w = carve_fwd(cv, d);
-  hipError_t e = run_forward(d, L, x, y, sv, w, static_cast<hipStream_t>(stream));
+  hipError_t e = run_forward(d, L, x, y, sv, w, static_cast<hipStream_t>(stream), mk);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
-ssm_status ssm_adjoint_grad(const ssm_dims* d, const ssm_layer* L, const void* x, const ssm_saved* sv,
-                            const float* g, int64_t window, const ssm_grads* gr, void* ws, size_t ws_bytes,
-                            void* stream) {
+static ssm_status adjoint_impl(const ssm_dims* d, const ssm_layer* L, const void* x, const ssm_saved* sv,
+                               const float* g, int64_t window, const ssm_grads* gr, void* ws, size_t ws_bytes,
+                               void* stream, ssm::Marks mk) {
   ssm_status s = check_dims(d);
   if (s != SSM_OK) return s;
   if ((s = check_layer(L)) != SSM_OK) return s;
@@ -311,13 +319,42 @@ ssm_status ssm_adjoint_grad(const ssm_dims* d, const ssm_layer* L, const void* x
   if ((s = check_grads(gr)) != SSM_OK) return s;
   if (!x || !g || !aligned16(x) || !aligned16(g)) return SSM_ERR_ARG;
   if (window < 1) return SSM_ERR_ARG;
+  if (mk.n < 0 || (mk.n > 0 && !mk.ev)) return SSM_ERR_ARG;
   const int64_t W = window < d->T ? window : d->T;
   const bool need_dx = gr->dx != nullptr;
   if ((s = check_ws(ws, ws_bytes, bwd_ws_bytes(d, W, need_dx))) != SSM_OK) return s;
   Carver cv(ws);
   BwdWs w = carve_bwd(cv, d, W, need_dx);
-  hipError_t e = run_backward(d, L, x, sv, g, W, gr, nullptr, w, static_cast<hipStream_t>(stream));
+  hipError_t e = run_backward(d, L, x, sv, g, W, gr, nullptr, w, static_cast<hipStream_t>(stream), mk);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status ssm_forward(const ssm_dims* d, const ssm_layer* L, const void* x, float* y, const ssm_saved* sv,
+                       void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(d, L, x, y, sv, ws, ws_bytes, stream, ssm::Marks{});
+}
+
+ssm_status ssm_adjoint_grad(const ssm_dims* d, const ssm_layer* L, const void* x, const ssm_saved* sv,
+                            const float* g, int64_t window, const ssm_grads* gr, void* ws, size_t ws_bytes,
+                            void* stream) {
+  return adjoint_impl(d, L, x, sv, g, window, gr, ws, ws_bytes, stream, ssm::Marks{});
+}
+
+ssm_status ssm_forward_timed(const ssm_dims* d, const ssm_layer* L, const void* x, float* y, const ssm_saved* sv,
+                             void* ws, size_t ws_bytes, void* stream, void* const* events, int32_t n_events) {
+  ssm::Marks mk;
+  mk.ev = events;
+  mk.n = n_events;
+  return forward_impl(d, L, x, y, sv, ws, ws_bytes, stream, mk);
+}
+
+ssm_status ssm_adjoint_grad_timed(const ssm_dims* d, const ssm_layer* L, const void* x, const ssm_saved* sv,
+                                  const float* g, int64_t window, const ssm_grads* gr, void* ws, size_t ws_bytes,
+                                  void* stream, void* const* events, int32_t n_events) {
+  ssm::Marks mk;
+  mk.ev = events;
+  mk.n = n_events;
+  return adjoint_impl(d, L, x, sv, g, window, gr, ws, ws_bytes, stream, mk);
 }
 
 ssm_status ssm_stack_grad(int32_t K, const ssm_dims* d, const ssm_layer* layers, const void* x0, const float* g,

@@ -455,16 +455,19 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   }
   k_bwd_local<IO, NL, G, WIN><<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(NB)), 64, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  a.marks.rec(1, st);
   const int64_t PN = a.P * a.N;
   k_bwd_carry<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, a.alpha, a.ssum, a.umu,
                                                                       a.carry);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  a.marks.rec(2, st);
   auto kern = k_bwd_main<IO, NL, G, WIN>;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(pl.lds_bytes));
   if (e != hipSuccess) return e;
   kern<<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(pl.NBW)), pl.wpb * 64, pl.lds_bytes, st>>>(a, pl.NBW);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  a.marks.rec(3, st);
   const int OUT = 2 * static_cast<int>(a.N);
   k_bwd_reduce_dbdc<IO><<<static_cast<unsigned>((a.T * OUT + 255) / 256), 256, 0, st>>>(
       a.T, a.P, OUT, pl.NBW, a.part, static_cast<IO*>(a.dY), a.ldy);
@@ -475,6 +478,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   (void)CH;
+  a.marks.rec(4, st);
   return hipSuccess;
 }
 

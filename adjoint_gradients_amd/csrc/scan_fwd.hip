@@ -149,14 +149,18 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
                                               a.alpha, a.hloc, a.ssum);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  a.marks.rec(2, st);
   const int64_t PN = a.P * a.N;
   k_fwd_carry<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, a.alpha, a.ssum, a.hloc,
                                                                       a.h_ckpt);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  a.marks.rec(3, st);
   k_fwd_final<IO, NL, G><<<grid, 64, 0, st>>>(a.T, a.P, a.N, a.C, a.s, static_cast<const IO*>(a.x), a.b, a.c,
                                               a.alpha, a.h_ckpt, a.y);
-  return hipGetLastError();
+  e = hipGetLastError();
+  a.marks.rec(4, st);
+  return e;
 }
 
 template <typename IO>

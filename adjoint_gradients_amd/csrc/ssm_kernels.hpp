@@ -7,6 +7,16 @@
 
 namespace ssm {
 
+// Optional timing marks: caller-owned hipEvent_t handles recorded on the
+// stream at the boundaries of the internal phases (NULL entries skipped).
+struct Marks {
+  void* const* ev = nullptr;
+  int n = 0;
+  void rec(int i, hipStream_t st) const {
+    if (ev && i < n && ev[i]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), st);
+  }
+};
+
 struct FwdArgs {
   int64_t T, P, N;
   int C;
@@ -19,6 +29,7 @@ struct FwdArgs {
   double* ssum;         // [K][P]   per-chunk sum of s (saved)
   float* h_ckpt;        // [K][P][N] saved
   float* y;             // [T][P]
+  Marks marks{};        // phases 2..4: after local scan, carry, final scan
 };
 
 struct BwdArgs {
@@ -46,6 +57,7 @@ struct BwdArgs {
   float* dxdir;         // [T][P] or nullptr
   float* dalpha;        // [P][N] or nullptr
   float* dbias;         // [P] or nullptr
+  Marks marks{};        // phases 1..4: after local aggregates, carry, main, reductions
 };
 
 // Layout queries of the backward scan (shared by the workspace planner).

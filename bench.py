@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Throughput of the selective-SSM adjoint-gradient hot path on one MI355X.
+
+One step = ssm_forward (projection GEMM, chunked forward scan with h
+checkpoints, y) + ssm_adjoint_grad (windowed reverse adjoint scan fused with
+the local VJPs, channel/chunk reductions, weight-gradient GEMM) on a
+1,048,576-token, 2048-channel, N=16 layer with bf16 x and weights, fp32
+state, window 4096 and checkpoints every 256 tokens.  Inputs are synthetic,
+seeded and resident in HBM before the timed region.  Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+WORKLOADS = {
+    # name: (config index, window, chunk)
+    "cfg3": (3, 4096, 256),
+    "cfg2": (2, 8192, 256),
+    "cfg2w1k": (2, 1024, 256),
+    "cfg1": (1, 2048, 256),
+    "cfg1exact": (1, 16384, 256),
+}
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16
+MFMA_F32_PEAK_TFS = 157.3
+# VALU issue rate without packed-fp32 forms: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
+VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
+
+FWD_PHASES = ["proj_gemm", "fwd_local", "fwd_carry", "fwd_final"]
+BWD_PHASES = ["bwd_local", "bwd_carry", "bwd_main", "bwd_reduce", "wgrad_gemm", "dx_gemm"]
+
+
+def algorithmic(name, T, P, N, C, W, s_io):
+    """Per-launch algorithmic work of a phase: (bytes, flops, valu_ops).
+
+    Bytes count each compulsory HBM stream once; valu_ops counts the VALU
+    issue slots of the method's arithmetic per (t, p, n) element (a hardware
+    exp2 counts 2: it issues at half rate on gfx950)."""
+    E = T * P * N
+    K = (T + C - 1) // C
+    win = W < T
+    if name == "proj_gemm":
+        return (T * (P * s_io + 4 * P + 8 * N), 2.0 * T * P * (P + 2 * N), 0)
+    if name == "fwd_local":
+        return (T * (P * s_io + 4 * P + 4 * N) + K * P * N * 12, 0, 5 * E)
+    if name == "fwd_carry":
+        return (K * P * N * 8 + K * P * 8, 0, 4 * K * P * N)
+    if name == "fwd_final":
+        return (T * (P * s_io + 8 * P + 8 * N) + K * P * N * 4, 0, 6 * E)
+    if name == "bwd_local":
+        return (T * (8 * P + 4 * N) + K * P * N * 4, 0, (10 if win else 5) * E)
+    if name == "bwd_carry":
+        return (K * P * N * 8 + K * P * 8, 0, 4 * K * P * N)
+    if name == "bwd_main":
+        # survey per-token figure: x, s, g, b, c, h_ckpt, dDelta
+        return (T * (P * s_io + 4 * P + 4 * P + 8 * N + P * s_io + 8 * N) + K * P * N * 4, 0,
+                (24 if win else 16) * E)
+    if name == "bwd_reduce":
+        return (T * 2 * N * 4 * 2, 0, 0)
+    if name == "wgrad_gemm":
+        return (T * ((P + 2 * N) * s_io + P * s_io), 2.0 * T * P * (P + 2 * N), 0)
+    if name == "dx_gemm":
+        return (T * ((P + 2 * N) * s_io + 8 * P), 2.0 * T * P * (P + 2 * N), 0)
+    return (0, 0, 0)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (created through the HIP runtime) for the
+    library's phase marks; torch's Event objects cannot see records made
+    outside torch."""
+
+    def __init__(self):
+        import ctypes
+
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.all = []
+
+    def make(self, n):
+        out = []
+        for _ in range(n):
+            h = self.ct.c_void_p()
+            rc = self.hip.hipEventCreate(self.ct.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            out.append(_RawEvent(h.value))
+            self.all.append(h.value)
+        return out
+
+    def ms(self, a, b):
+        f = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(f), self.ct.c_void_p(a.cuda_event),
+                                          self.ct.c_void_p(b.cuda_event))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(f.value)
+
+    def destroy(self):
+        for h in self.all:
+            self.hip.hipEventDestroy(self.ct.c_void_p(h))
+        self.all = []
+
+
+class _RawEvent:
+    def __init__(self, handle):
+        self.cuda_event = handle
+
+
+def cpu_baseline(case, window, chunk, tokens):
+    """Times the fp64 oracle (as it stands) on a token prefix of the workload."""
+    import numpy as np
+
+    import oracle
+    from ssm_inputs import make_layer
+
+    oracle.build(force=False)
+    inp = make_layer(case, T=tokens)
+    o = {k: (np.asarray(v, dtype=np.float64) if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+    t0 = time.perf_counter()
+    oracle.layer_grad(o, window=window if window < tokens else None, want_dx=False)
+    wall = time.perf_counter() - t0
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle forward+adjoint+VJP+weight grads on the first {tokens} tokens of the "
+                      f"{case.name} workload (P={case.P}, N={case.N}, window={window}); wall {wall:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="cfg3", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--phases", action="store_true", help="print the per-phase breakdown to stderr")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "the time-sharded design is described in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import adjoint_gradients_amd as agm
+    from ssm_inputs import CONFIGS, make_layer_device
+
+    cfg_idx, window, chunk = WORKLOADS[args.workload]
+    case = CONFIGS[cfg_idx]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = make_layer_device(case, device=dev)
+    T, P, N, io = case.T, case.P, case.N, case.io
+    s_io = 2 if io == "bf16" else 4
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+
+    def dev_t(a, dtype=torch.float32):
+        return torch.from_numpy(a).to(dev).to(dtype)
+
+    lay = agm.LayerTensors(dev_t(inp["W_delta"], dt), dev_t(inp["W_B"], dt), dev_t(inp["W_C"], dt),
+                           dev_t(inp["alpha"]), dev_t(inp["delta_bias"]))
+    x, g = inp["x_dev"], inp["g_dev"]
+    dims = agm.make_dims(T, P, N, chunk, io)
+    ws_f = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, 0, 0), dev)
+    ws_b = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, window, 0), dev)
+    saved = agm.alloc_saved(dims, dev)
+    grads = agm.alloc_grads(dims, device=dev)
+    y = torch.empty(T, P, device=dev, dtype=torch.float32)
+    L = lay.struct()
+    S = agm.saved_struct(saved)
+    G = agm.grads_struct(grads)
+    stream = torch.cuda.current_stream()
+
+    hev = HipEvents()
+
+    def new_events(n):
+        return hev.make(n)
+
+    def step(evf=None, evb=None):
+        if evf is None:
+            agm.ssm_forward(dims, L, x, y, S, ws_f, ws_f.numel())
+            agm.ssm_adjoint_grad(dims, L, x, S, g, window, G, ws_b, ws_b.numel())
+        else:
+            agm.ssm_forward_timed(dims, L, x, y, S, ws_f, ws_f.numel(), evf)
+            agm.ssm_adjoint_grad_timed(dims, L, x, S, g, window, G, ws_b, ws_b.numel(), evb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, phase events recorded on the library's stream
+    evs = [(new_events(5), new_events(7)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for evf, evb in evs:
+        step(evf, evb)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+
+    phase_ms = {k: 0.0 for k in FWD_PHASES + BWD_PHASES}
+    for evf, evb in evs:
+        for i, k in enumerate(FWD_PHASES):
+            phase_ms[k] += hev.ms(evf[i], evf[i + 1]) / args.steps
+        for i, k in enumerate(BWD_PHASES):
+            phase_ms[k] += hev.ms(evb[i], evb[i + 1]) / args.steps
+    hev.destroy()
+
+    rows = []
+    for k, ms in phase_ms.items():
+        by, fl, ops = algorithmic(k, T, P, N, chunk, window, s_io)
+        rows.append((k, ms, by / (ms * 1e-3) / 1e9 if ms > 0 else 0.0, fl / (ms * 1e-3) / 1e12 if ms > 0 else 0.0,
+                     ops / (ms * 1e-3) / 1e9 if ms > 0 else 0.0))
+    if args.phases:
+        print(f"{'phase':12s} {'ms':>9s} {'GB/s':>9s} {'TFLOP/s':>9s} {'VALU Gop/s':>11s}", file=sys.stderr)
+        for k, ms, gbs, tfs, gops in rows:
+            print(f"{k:12s} {ms:9.3f} {gbs:9.1f} {tfs:9.1f} {gops:11.1f}", file=sys.stderr)
+        print(f"step {ms_per_step:.3f} ms (events), host wall {wall_ms / args.steps:.3f} ms/step", file=sys.stderr)
+
+    dom = max(rows, key=lambda r: r[1])
+    name, ms = dom[0], dom[1]
+    by, fl, ops = algorithmic(name, T, P, N, chunk, window, s_io)
+    if fl > 0:
+        peak = MFMA_BF16_PEAK_TFS if io == "bf16" else MFMA_F32_PEAK_TFS
+        ach = fl / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
+                "traffic": None}
+    else:
+        ach = ops / (ms * 1e-3) / 1e9
+        roof = {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_GOPS, "unit": "Gop/s", "frac": ach / VALU_PEAK_GOPS,
+                "traffic": None}
+    hbm_ach = by / (ms * 1e-3) / 1e9
+    roof.update(kernel=name, ms=ms, hbm_achieved_gbs=hbm_ach, hbm_frac=hbm_ach / HBM_PEAK_GBS)
+
+    out = {
+        "metric": "SSM adjoint-gradient tokens/s (fwd+adjoint+VJP) at T=1M; % HBM roofline",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if io == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{case.name}: one selective SSM layer, T={T}, P={P}, N={N}, io={io}, "
+                               f"fp32 state, window={window}, checkpoint every {chunk} tokens",
+                   "T": T, "P": P, "N": N, "window": window, "chunk": chunk},
+        "roofline": roof,
+        "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case, window, chunk, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

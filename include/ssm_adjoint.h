@@ -174,6 +174,28 @@ ssm_status ssm_stack_grad(int32_t K, const ssm_dims *dims, const ssm_layer *laye
                           const float *g, int64_t window, const ssm_grads *grads, float *dx0,
                           float *xK, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Instrumented variants for timing: identical to ssm_forward and
+ * ssm_adjoint_grad, and additionally record the caller's HIP events
+ * (hipEvent_t handles passed as void*; NULL entries and indices >= n_events
+ * are skipped) on `stream` at the phase boundaries:
+ *   forward : [0] start  [1] after the projection GEMM  [2] after the
+ *             chunk-local scan  [3] after the chunk carry  [4] after the final scan
+ *   gradient: [0] start  [1] after the chunk-local adjoint aggregates
+ *             [2] after the adjoint carry  [3] after the fused adjoint + VJP
+ *             kernel  [4] after the channel / chunk reductions  [5] after the
+ *             weight-gradient GEMM  [6] after the input-cotangent GEMM (or
+ *             its absence).
+ * events may be NULL only when n_events == 0.
+ */
+ssm_status ssm_forward_timed(const ssm_dims *dims, const ssm_layer *layer, const void *x, float *y,
+                             const ssm_saved *saved, void *ws, size_t ws_bytes, void *stream,
+                             void *const *events, int32_t n_events);
+ssm_status ssm_adjoint_grad_timed(const ssm_dims *dims, const ssm_layer *layer, const void *x,
+                                  const ssm_saved *saved, const float *g, int64_t window,
+                                  const ssm_grads *grads, void *ws, size_t ws_bytes, void *stream,
+                                  void *const *events, int32_t n_events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -172,6 +172,29 @@ def make_stack(c: LayerCase, K: int | None = None, T: int | None = None) -> dict
     return {"layers": layers, "x": x, "g": g, "T": T, "P": c.P, "N": c.N, "K": K, "io": c.io}
 
 
+def make_layer_device(c: LayerCase, device="cuda", T: int | None = None) -> dict:
+    """Large workloads: weights, bias and alpha from the numpy stream above
+    (same draws as make_layer), x and g drawn on the device with torch's
+    seeded Philox generator (standard normal float32, x then g; x rounded to
+    bfloat16 by round-to-nearest-even when io == bf16).  Returns torch
+    tensors on `device` plus the numpy weights."""
+    import torch
+
+    T = c.T if T is None else T
+    rng = np.random.Generator(np.random.PCG64(c.seed))
+    d = _weights(rng, c)
+    d["delta_bias"] = _bias(rng, c)
+    d["alpha"] = _alpha(c)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(1_000_003 * (c.seed + 1))
+    x = torch.randn(T, c.P, generator=gen, device=device, dtype=torch.float32)
+    if c.io == "bf16":
+        x = x.to(torch.bfloat16)
+    g = torch.randn(T, c.P, generator=gen, device=device, dtype=torch.float32)
+    d.update(x_dev=x, g_dev=g, T=T, P=c.P, N=c.N, io=c.io)
+    return d
+
+
 def small_case(T: int, P: int, N: int, seed: int, io: str = "f32", bias: str = "zero",
                wdelta: str = "normal") -> LayerCase:
     """Ad-hoc small case with the same distributions (tests of edge shapes)."""

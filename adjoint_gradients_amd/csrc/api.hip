@@ -129,6 +129,7 @@ struct BwdWs {
   double* hwin;
   float* dal_part;
   float* dbias_part;
+  float* hsub;
   float* wpart;
   int splits;
 };
@@ -150,6 +151,7 @@ BwdWs carve_bwd(Carver& cv, const ssm_dims* d, int64_t W, bool need_dx) {
   w.hwin = win ? cv.take<double>(static_cast<size_t>(K * P)) : nullptr;
   w.dal_part = cv.take<float>(static_cast<size_t>(K * P * N));
   w.dbias_part = cv.take<float>(static_cast<size_t>(K * P));
+  w.hsub = cv.take<float>(ssm::bwd_hsub_floats(T, P, N, d->chunk));
   w.splits = splitk_for(d);
   w.wpart = cv.take<float>(static_cast<size_t>(w.splits) * M * P);
   return w;
@@ -233,7 +235,7 @@ hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, co
   a.s = sv->s; a.x = x; a.b = sv->b; a.c = sv->c; a.alpha = L->alpha; a.h_ckpt = sv->h_ckpt;
   a.ssum = sv->s_sum; a.g = g;
   a.ps64 = w.ps64; a.hwin = w.hwin; a.umu = w.umu; a.carry = w.carry; a.part = w.part;
-  a.dal_part = w.dal_part; a.dbias_part = w.dbias_part;
+  a.dal_part = w.dal_part; a.dbias_part = w.dbias_part; a.hsub = w.hsub;
   a.dY = w.dY; a.ldy = M;
   a.dxdir = need_dx ? w.dxdir : nullptr;
   a.dalpha = gr->dalpha; a.dbias = gr->dbias;

@@ -59,7 +59,7 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-constexpr int kSub = 16;  // tokens per recomputed sub-chunk (registers hold S x NL states)
+constexpr int kSub = 8;  // tokens per recomputed sub-chunk (registers hold S x NL states)
 
 }  // namespace
 
@@ -178,204 +178,7 @@ __global__ __launch_bounds__(256) void k_bwd_carry(int64_t K, int64_t P, int64_t
   }
 }
 
-// Main backward kernel: one workgroup = `wpb` wavefronts = wpb channel blocks
-// of the same chunk k.
-template <typename IO, int NL, int G, bool WIN>
-__global__ __launch_bounds__(256) void k_bwd_main(BwdArgs a, int64_t NBW) {
-  constexpr int CH = 64 / G;
-  constexpr int NN = NL * G;
-  constexpr int S = kSub;
-  constexpr int OUT = 2 * NN;  // db | dc outputs per token
-  extern __shared__ float lds[];
-  const int wpb = blockDim.x / 64;
-  const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const int grp = lane / CH, pl = lane % CH;
-  const int64_t T = a.T, P = a.P, W = a.W;
-  const int C = a.C;
-  const int64_t k = blockIdx.x;
-  const int64_t cb = static_cast<int64_t>(blockIdx.y) * wpb + w;
-  const int64_t p = cb * CH + pl;
-  const bool valid = p < P;
-  const int64_t pc = valid ? p : P - 1;
-  const int n0 = grp * NL;
-  const int nsub_max = (C + S - 1) / S;  // LDS is sized for a full chunk
-  float* hsub = lds + static_cast<size_t>(w) * nsub_max * NL * 64;                     // [nsub][NL][64]
-  float* red = lds + static_cast<size_t>(wpb) * nsub_max * NL * 64 + w * (OUT * CH);   // [OUT][CH]
-  float* xw = lds + static_cast<size_t>(wpb) * (nsub_max * NL * 64 + OUT * CH);        // [wpb][S][OUT]
-  const IO* x = static_cast<const IO*>(a.x);
-
-  float al2[NL];
-#pragma unroll
-  for (int j = 0; j < NL; j++) al2[j] = a.alpha[pc * NN + n0 + j] * kLog2e;
-  const int64_t t0 = k * C;
-  const int64_t t1 = (t0 + C < T) ? t0 + C : T;
-  // sub-chunks of this chunk (the last chunk may be partial)
-  const int nsub = static_cast<int>((t1 - t0 + S - 1) / S);
-
-  // Phase 1: forward walk from the checkpoint, keep h at every sub-chunk start.
-  {
-    float h[NL];
-#pragma unroll
-    for (int j = 0; j < NL; j++) h[j] = a.h_ckpt[(k * P + pc) * NN + n0 + j];
-    for (int u = 0; u < nsub; u++) {
-#pragma unroll
-      for (int j = 0; j < NL; j++) hsub[(u * NL + j) * 64 + lane] = h[j];
-      if (u == nsub - 1) break;
-      const int64_t ta = t0 + static_cast<int64_t>(u) * S;
-      for (int64_t t = ta; t < ta + S; t++) {
-        const float ns = -a.s[t * P + pc];
-        const float xv = load_io(x + t * P + pc);
-        float bt[NL];
-        load_row<NL>(a.b + t * NN + n0, bt);
-#pragma unroll
-        for (int j = 0; j < NL; j++) h[j] = fmaf(fast_exp2(ns * al2[j]), h[j], bt[j] * xv);
-      }
-    }
-  }
-
-  // Phase 2: sub-chunks right to left.
-  float inc[NL], dal[NL];
-#pragma unroll
-  for (int j = 0; j < NL; j++) {
-    inc[j] = a.carry[(k * P + pc) * NN + n0 + j];
-    dal[j] = 0.0f;
-  }
-  float dbias_acc = 0.0f;
-  double H = 0.0, sigma = 0.0, suffix = 0.0;
-  if constexpr (WIN) H = a.hwin[k * P + pc];
-  const float inv_log2e = 1.0f / kLog2e;
-
-  for (int u = nsub - 1; u >= 0; u--) {
-    const int64_t ta = t0 + static_cast<int64_t>(u) * S;
-    const int len = static_cast<int>((t1 - ta < S) ? t1 - ta : S);
-    float hs[NL];
-#pragma unroll
-    for (int j = 0; j < NL; j++) hs[j] = hsub[(u * NL + j) * 64 + lane];
-    // recompute the sub-chunk's states into registers
-    float hr[S][NL];
-    {
-      float hh[NL];
-#pragma unroll
-      for (int j = 0; j < NL; j++) hh[j] = hs[j];
-#pragma unroll
-      for (int tau = 0; tau < S; tau++) {
-        if (tau < len) {
-          const int64_t t = ta + tau;
-          const float ns = -a.s[t * P + pc];
-          const float xv = load_io(x + t * P + pc);
-          float bt[NL];
-          load_row<NL>(a.b + t * NN + n0, bt);
-#pragma unroll
-          for (int j = 0; j < NL; j++) {
-            hh[j] = fmaf(fast_exp2(ns * al2[j]), hh[j], bt[j] * xv);
-            hr[tau][j] = hh[j];
-          }
-        }
-      }
-    }
-    // reverse walk with the local VJPs
-#pragma unroll
-    for (int tau = S - 1; tau >= 0; tau--) {
-      if (tau < len) {
-        const int64_t i = ta + tau;
-        const float s = a.s[i * P + pc];
-        const float xv = load_io(x + i * P + pc);
-        const float gv = a.g[i * P + pc];
-        float bt[NL], ct[NL];
-        load_row<NL>(a.b + i * NN + n0, bt);
-        load_row<NL>(a.c + i * NN + n0, ct);
-        float av[NL], mu[NL];
-#pragma unroll
-        for (int j = 0; j < NL; j++) {
-          av[j] = fast_exp2(-s * al2[j]);
-          mu[j] = fmaf(gv, ct[j], inc[j]);
-        }
-        if constexpr (WIN) {
-          const int64_t m = i + W;
-          if (m < T) {
-            const float sm = a.s[m * P + pc];
-            const float gm = a.g[m * P + pc];
-            float cm[NL];
-            load_row<NL>(a.c + m * NN + n0, cm);
-            const float E = static_cast<float>(sigma + H - suffix);
-#pragma unroll
-            for (int j = 0; j < NL; j++) {
-              const float D = fast_exp2(-E * al2[j]);
-              mu[j] = fmaf(-gm * cm[j], D, mu[j]);
-            }
-            suffix += static_cast<double>(sm);
-          }
-          sigma += static_cast<double>(s);
-        }
-        float ds = 0.0f, dxd = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NL; j++) {
-          const float hp = (tau > 0) ? hr[tau > 0 ? tau - 1 : 0][j] : hs[j];
-          const float tt = mu[j] * hp * av[j];
-          ds = fmaf(tt, al2[j], ds);
-          dal[j] = fmaf(tt, s, dal[j]);
-          dxd = fmaf(mu[j], bt[j], dxd);
-          inc[j] = av[j] * mu[j];
-        }
-        if constexpr (G > 1) {
-          ds = group_sum<G, CH>(ds);
-          dxd = group_sum<G, CH>(dxd);
-        }
-        const float dD = -(ds * inv_log2e) * one_minus_exp_neg(s);
-        if (valid && grp == 0) {
-          store_io(static_cast<IO*>(a.dY) + i * a.ldy + p, dD);
-          if (a.dxdir) a.dxdir[i * P + p] = dxd;
-        }
-        dbias_acc += dD;
-        // channel sums of db = mu x and dc = g h through an LDS transpose
-#pragma unroll
-        for (int j = 0; j < NL; j++) {
-          red[(n0 + j) * CH + pl] = valid ? mu[j] * xv : 0.0f;
-          red[(NN + n0 + j) * CH + pl] = valid ? gv * hr[tau][j] : 0.0f;
-        }
-        wave_lds_sync();
-        if constexpr (OUT <= 64) {
-          constexpr int LPO = 64 / OUT;  // lanes per output
-          constexpr int V = CH / LPO;    // values summed per lane
-          const int o = lane / LPO, r = lane % LPO;
-          const float* src = red + o * CH + r * V;
-          float sum = 0.0f;
-#pragma unroll
-          for (int v = 0; v < V; v++) sum += src[v];
-#pragma unroll
-          for (int d = 1; d < LPO; d <<= 1) sum += __shfl_xor(sum, d, 64);
-          if (r == 0) xw[(w * S + tau) * OUT + o] = sum;
-        } else {
-#pragma unroll
-          for (int q = 0; q < OUT / 64; q++) {
-            const int o = lane + 64 * q;
-            const float* src = red + o * CH;
-            float sum = 0.0f;
-#pragma unroll
-            for (int v = 0; v < CH; v++) sum += src[v];
-            xw[(w * S + tau) * OUT + o] = sum;
-          }
-        }
-        wave_lds_sync();
-      }
-    }
-    __syncthreads();
-    // sum over the workgroup's wavefronts -> one partial per (token, workgroup)
-    const int tot = len * OUT;
-    for (int idx = threadIdx.x; idx < tot; idx += blockDim.x) {
-      const int tau = idx / OUT, o = idx % OUT;
-      float v = 0.0f;
-      for (int ww = 0; ww < wpb; ww++) v += xw[(ww * S + tau) * OUT + o];
-      a.part[((ta + tau) * NBW + blockIdx.y) * OUT + o] = v;
-    }
-    __syncthreads();
-  }
-  if (valid) {
-#pragma unroll
-    for (int j = 0; j < NL; j++) a.dal_part[(k * P + p) * NN + n0 + j] = -dal[j];
-    if (grp == 0) a.dbias_part[k * P + p] = dbias_acc;
-  }
-}
+#include "bwd_main.inl"
 
 // db, dc: deterministic sum of the per-workgroup partials, written as the
 // io-typed columns [P, P+2N) of dY (the weight-gradient GEMM operand).
@@ -424,19 +227,26 @@ bool bwd_plan(int64_t P, int64_t N, int C, BwdPlan* pl) {
   nl_g_for(N, &NL, &G);
   const int CH = 64 / G;
   const int S = kSub;
-  const int nsub = (C + S - 1) / S;
-  const size_t per_wave = (static_cast<size_t>(nsub) * NL * 64 + 2 * N * CH + static_cast<size_t>(S) * 2 * N) * 4;
-  const size_t budget = 160 * 1024;
-  int wpb = static_cast<int>(budget / per_wave);
-  if (wpb > 4) wpb = 4;
-  if (wpb < 1) return false;
+  const int wpb = kWpb;
+  // LDS: two staging buffers of 3 rows x S tokens x N states, the per-wave
+  // transpose area [2N][CH] and the per-wave token sums [S][2N]
+  const size_t floats = 2 * 3 * static_cast<size_t>(S) * N + static_cast<size_t>(wpb) * (2 * N * CH + S * 2 * N);
+  if (floats * 4 > 160 * 1024) return false;
+  (void)C;
   const int64_t NB = (P + CH - 1) / CH;
-  if (wpb > NB) wpb = static_cast<int>(NB);
   pl->NL = NL; pl->G = G; pl->CH = CH; pl->S = S; pl->wpb = wpb;
   pl->NB = NB;
   pl->NBW = (NB + wpb - 1) / wpb;
-  pl->lds_bytes = per_wave * wpb;
+  pl->lds_bytes = floats * 4;
   return true;
+}
+
+size_t bwd_hsub_floats(int64_t T, int64_t P, int64_t N, int C) {
+  BwdPlan pl;
+  if (!bwd_plan(P, N, C, &pl)) return 0;
+  const int64_t K = (T + C - 1) / C;
+  const int64_t nsub = (C + pl.S - 1) / pl.S;
+  return static_cast<size_t>(K * pl.NB * nsub) * pl.NL * 64;
 }
 
 // ----------------------------------------------------------------- launchers
@@ -465,7 +275,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(pl.lds_bytes));
   if (e != hipSuccess) return e;
-  kern<<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(pl.NBW)), pl.wpb * 64, pl.lds_bytes, st>>>(a, pl.NBW);
+  kern<<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(pl.NBW)), pl.wpb * 64, pl.lds_bytes, st>>>(a, pl.NB,
+                                                                                                    pl.NBW);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.marks.rec(3, st);
   const int OUT = 2 * static_cast<int>(a.N);

@@ -52,18 +52,22 @@ __device__ __forceinline__ float softplus_f(float d) {
 }
 
 // 1 - e^{-s} for s >= 0, i.e. the logistic sigmoid of Delta when s = softplus(Delta).
-// Taylor series below 0.5 avoids the cancellation of 1 - e^{-s} for small s.
+// Below 0.5 a Taylor series (truncation < s^10/10! < 3e-10 relative) avoids
+// the cancellation of 1 - e^{-s}; both branches are evaluated and selected
+// (no divergence, no divisions).
 __device__ __forceinline__ float one_minus_exp_neg(float s) {
-  if (s > 0.5f) return 1.0f - fast_exp2(-s * kLog2e);
-  // s - s^2/2! + s^3/3! - ... (truncation < s^10/10! < 3e-10)
-  float t = s;
-  float sum = s;
-#pragma unroll
-  for (int k = 2; k <= 9; k++) {
-    t *= -s / static_cast<float>(k);
-    sum += t;
-  }
-  return sum;
+  const float big = 1.0f - fast_exp2(-s * kLog2e);
+  // s (1 - s/2 (1 - s/3 (1 - s/4 (... (1 - s/9)))))
+  float t = 1.0f - s * (1.0f / 9.0f);
+  t = 1.0f - s * (1.0f / 8.0f) * t;
+  t = 1.0f - s * (1.0f / 7.0f) * t;
+  t = 1.0f - s * (1.0f / 6.0f) * t;
+  t = 1.0f - s * (1.0f / 5.0f) * t;
+  t = 1.0f - s * (1.0f / 4.0f) * t;
+  t = 1.0f - s * (1.0f / 3.0f) * t;
+  t = 1.0f - s * 0.5f * t;
+  const float small = s * t;
+  return s > 0.5f ? big : small;
 }
 
 // Sum over the G lane groups of one channel (lanes pl, pl+CH, pl+2CH, ...).

@@ -51,6 +51,7 @@ struct BwdArgs {
   float* part;          // [T][NBW][2N] per-workgroup partial sums of db | dc
   float* dal_part;      // [K][P][N]
   float* dbias_part;    // [K][P]
+  float* hsub;          // per-wavefront sub-chunk start states (bwd_hsub_floats)
   // outputs of the scan
   void* dY;             // [T][ldy] io: columns [0,P) = dDelta, [P,P+N) = db, [P+N,P+2N) = dc
   int64_t ldy;
@@ -69,6 +70,7 @@ struct BwdPlan {
   size_t lds_bytes;     // dynamic LDS of the main kernel
 };
 bool bwd_plan(int64_t P, int64_t N, int C, BwdPlan* plan);
+size_t bwd_hsub_floats(int64_t T, int64_t P, int64_t N, int C);
 
 hipError_t launch_forward_scan(const FwdArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_backward_scan(const BwdArgs& a, bool bf16, hipStream_t st);

@@ -35,6 +35,9 @@ template <> struct Tr<float> {
   static constexpr int PAD = 1;
 };
 
+// Epilogues: operator() for the small-tile kernel; prep(col) + apply() for the
+// large-tile kernel (the column-dependent choice is made once per column, so
+// the unrolled per-element code has no branches).
 struct EpiProj {
   EpiProjArgs e;
   __device__ __forceinline__ void operator()(int64_t row, int64_t col, float v, int) const {
@@ -46,6 +49,28 @@ struct EpiProj {
       e.c[row * e.N + (col - e.P - e.N)] = v;
     }
   }
+  struct Prep {
+    float* base;
+    int64_t ld;
+    float bias;
+    bool sp;
+  };
+  __device__ __forceinline__ Prep prep(int64_t col, int) const {
+    Prep q;
+    if (col < e.P) {
+      q.base = e.s + col; q.ld = e.P; q.bias = e.bias ? e.bias[col] : 0.0f; q.sp = true;
+    } else if (col < e.P + e.N) {
+      q.base = e.b + (col - e.P); q.ld = e.N; q.bias = 0.0f; q.sp = false;
+    } else {
+      q.base = e.c + (col - e.P - e.N); q.ld = e.N; q.bias = 0.0f; q.sp = false;
+    }
+    return q;
+  }
+  __device__ __forceinline__ void apply(const Prep& q, int64_t row, float v) const {
+    const float w = v + q.bias;
+    const float sp = softplus_f(w);
+    q.base[row * q.ld] = q.sp ? sp : w;
+  }
 };
 
 struct EpiPart {
@@ -54,6 +79,13 @@ struct EpiPart {
   __device__ __forceinline__ void operator()(int64_t row, int64_t col, float v, int z) const {
     part[(static_cast<int64_t>(z) * M + row) * Nc + col] = v;
   }
+  struct Prep {
+    float* base;
+  };
+  __device__ __forceinline__ Prep prep(int64_t col, int z) const {
+    return Prep{part + static_cast<int64_t>(z) * M * Nc + col};
+  }
+  __device__ __forceinline__ void apply(const Prep& q, int64_t row, float v) const { q.base[row * Nc] = v; }
 };
 
 struct EpiAdd {
@@ -61,6 +93,16 @@ struct EpiAdd {
   int64_t Nc;
   __device__ __forceinline__ void operator()(int64_t row, int64_t col, float v, int) const {
     const int64_t idx = row * Nc + col;
+    float r = v + e.add0[idx];
+    if (e.add1) r += e.add1[idx];
+    e.out[idx] = r;
+  }
+  struct Prep {
+    int64_t col;
+  };
+  __device__ __forceinline__ Prep prep(int64_t col, int) const { return Prep{col}; }
+  __device__ __forceinline__ void apply(const Prep& q, int64_t row, float v) const {
+    const int64_t idx = row * Nc + q.col;
     float r = v + e.add0[idx];
     if (e.add1) r += e.add1[idx];
     e.out[idx] = r;
@@ -202,6 +244,12 @@ hipError_t run(const GemmOperands& op, int splits, int64_t kps, Epi epi, hipStre
   return hipGetLastError();
 }
 
+}  // namespace
+
+#include "gemm_bf16.inl"
+
+namespace {
+
 __global__ __launch_bounds__(256) void k_reduce_wgrad(const float* __restrict__ part, int splits, int64_t P,
                                                       int64_t N, float* __restrict__ dWd, float* __restrict__ dWb,
                                                       float* __restrict__ dWc) {
@@ -241,19 +289,24 @@ __global__ __launch_bounds__(256) void k_residual_init(int64_t n, const void* __
 
 hipError_t gemm_projection(const GemmOperands& op, bool bf16, const EpiProjArgs& e, hipStream_t st) {
   EpiProj epi{e};
-  return bf16 ? run<bf16_t>(op, 1, op.K, epi, st) : run<float>(op, 1, op.K, epi, st);
+  return bf16 ? gbf::run(op, 1, op.K, epi, st) : run<float>(op, 1, op.K, epi, st);
 }
 
 hipError_t gemm_splitk(const GemmOperands& op, bool bf16, int splits, float* part, hipStream_t st) {
   int64_t kps = (op.K + splits - 1) / splits;
   kps = ((kps + BK - 1) / BK) * BK;
   EpiPart epi{part, op.M, op.Nc};
-  return bf16 ? run<bf16_t>(op, splits, kps, epi, st) : run<float>(op, splits, kps, epi, st);
+  if (bf16) {
+    int64_t kpb = (op.K + splits - 1) / splits;
+    kpb = ((kpb + gbf::BK - 1) / gbf::BK) * gbf::BK;
+    return gbf::run(op, splits, kpb, epi, st);
+  }
+  return run<float>(op, splits, kps, epi, st);
 }
 
 hipError_t gemm_add(const GemmOperands& op, bool bf16, const EpiAddArgs& e, hipStream_t st) {
   EpiAdd epi{e, op.Nc};
-  return bf16 ? run<bf16_t>(op, 1, op.K, epi, st) : run<float>(op, 1, op.K, epi, st);
+  return bf16 ? gbf::run(op, 1, op.K, epi, st) : run<float>(op, 1, op.K, epi, st);
 }
 
 hipError_t reduce_weight_grads(const float* part, int splits, int64_t P, int64_t N, float* dWd, float* dWb,

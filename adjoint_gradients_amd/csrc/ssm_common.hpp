@@ -45,10 +45,15 @@ template <> __device__ __forceinline__ void store_io<bf16_t>(bf16_t* p, float v)
 // 2^x on the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// softplus(d) = max(d,0) + log(1 + e^{-|d|}), computed in float.
+// softplus(d) = max(d,0) + log(1 + e) with e = e^{-|d|} in (0, 1], on the
+// hardware exp2/log2 units.  For e < 1/16 the series e - e^2/2 + e^3/3 - e^4/4
+// (relative truncation < e^4/5 < 2e-6 of the smallest term kept... overall
+// < 1e-7) keeps full relative accuracy where 1 + e would round away e.
 __device__ __forceinline__ float softplus_f(float d) {
-  float e = __expf(-fabsf(d));
-  return fmaxf(d, 0.0f) + log1pf(e);
+  const float e = __builtin_amdgcn_exp2f(-fabsf(d) * kLog2e);
+  const float big = __builtin_amdgcn_logf(1.0f + e) * 0.69314718055994531f;
+  const float small = e * (1.0f - e * (0.5f - e * ((1.0f / 3.0f) - e * 0.25f)));
+  return fmaxf(d, 0.0f) + (e < 0.0625f ? small : big);
 }
 
 // 1 - e^{-s} for s >= 0, i.e. the logistic sigmoid of Delta when s = softplus(Delta).

@@ -145,7 +145,7 @@ BwdWs carve_bwd(Carver& cv, const ssm_dims* d, int64_t W, bool need_dx) {
   w.dY = cv.take<char>(static_cast<size_t>(T * M) * io_size(d));
   w.dxdir = need_dx ? cv.take<float>(static_cast<size_t>(T * P)) : nullptr;
   w.part = cv.take<float>(static_cast<size_t>(T * pl.NBW * 2 * N));
-  w.umu = cv.take<float>(static_cast<size_t>(K * P * N));
+  w.umu = cv.take<float>(static_cast<size_t>(K * P * N + P));  // + P: also the chunk-reduction scratch
   w.carry = cv.take<float>(static_cast<size_t>(K * P * N));
   w.ps64 = win ? cv.take<double>(static_cast<size_t>((K + 1) * P)) : nullptr;
   w.hwin = win ? cv.take<double>(static_cast<size_t>(K * P)) : nullptr;

@@ -125,30 +125,35 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
     if (a.dxdir) row_ptr(a.dxdir, i, a.P)[off] = dxd;
   }
   st.dbias += dD;
-  // channel sums of db = mu x and dc = g h through an LDS transpose
+  // channel sums of db = mu x and dc = g h through an LDS transpose; rows
+  // are padded to CH+1 floats so the row-wise reads spread over the banks
+  constexpr int RS = CH + 1;
   const int n0 = grp * NL;
 #pragma unroll
   for (int j = 0; j < NL; j++) {
-    red[(n0 + j) * CH + pl] = valid ? mu[j] * tk.x : 0.0f;
-    red[(NN + n0 + j) * CH + pl] = valid ? tk.g * hc[j] : 0.0f;
+    red[(n0 + j) * RS + pl] = valid ? mu[j] * tk.x : 0.0f;
+    red[(NN + n0 + j) * RS + pl] = valid ? tk.g * hc[j] : 0.0f;
   }
   lds_wait();
   if constexpr (OUT <= 64) {
     constexpr int LPO = 64 / OUT;  // lanes per output
     constexpr int V = CH / LPO;    // values summed per lane
     const int o = lane / LPO, r = lane % LPO;
-    const float* src = red + o * CH + r * V;
+    const float* src = red + o * RS + r * V;
     float sum = 0.0f;
 #pragma unroll
     for (int v = 0; v < V; v++) sum += src[v];
-#pragma unroll
-    for (int d = 1; d < LPO; d <<= 1) sum += __shfl_xor(sum, d, 64);
+    if constexpr (LPO >= 2) sum = xor_sum<1>(sum);
+    if constexpr (LPO >= 4) sum = xor_sum<2>(sum);
+    if constexpr (LPO >= 8) sum = xor_sum<4>(sum);
+    if constexpr (LPO >= 16) sum = xor_sum<8>(sum);
+    if constexpr (LPO >= 32) sum = xor_sum<16>(sum);
     if (r == 0) xw_tau[o] = sum;
   } else {
 #pragma unroll
     for (int q = 0; q < OUT / 64; q++) {
       const int o = lane + 64 * q;
-      const float* src = red + o * CH;
+      const float* src = red + o * RS;
       float sum = 0.0f;
 #pragma unroll
       for (int v = 0; v < CH; v++) sum += src[v];
@@ -184,8 +189,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   const uint32_t off = static_cast<uint32_t>(pc);  // lane offset within a token row
   const int n0 = grp * NL;
   const int nsub_max = (C + S - 1) / S;
-  float* red = lds + 2 * STG + w * (OUT * CH);     // [OUT][CH] per wavefront
-  float* xw = lds + 2 * STG + kWpb * OUT * CH;      // [kWpb][S][OUT]
+  float* red = lds + 2 * STG + w * (OUT * (CH + 1));  // [OUT][CH+1] per wavefront
+  float* xw = lds + 2 * STG + kWpb * OUT * (CH + 1);   // [kWpb][S][OUT]
   float* hsg = a.hsub + ((k * NB + (wave_live ? cb : 0)) * nsub_max) * (NL * 64);
   const IO* xp = static_cast<const IO*>(a.x);
   const int64_t t0 = k * C;

@@ -196,22 +196,40 @@ __global__ __launch_bounds__(256) void k_bwd_reduce_dbdc(int64_t T, int64_t P, i
   store_io(dY + t * ldy + P + o, v);
 }
 
-// dalpha = sum over chunks; dbias = sum over chunks (fixed order).
-__global__ __launch_bounds__(256) void k_bwd_reduce_chunks(int64_t K, int64_t P, int64_t N,
-                                                           const float* __restrict__ dal_part,
-                                                           const float* __restrict__ dbias_part,
-                                                           float* __restrict__ dalpha, float* __restrict__ dbias) {
+// dalpha and dbias: sums over chunks in a fixed order, in two stages so the
+// loads are spread over many threads: stage 1 sums KS slices of the chunk
+// range into tmp[KS][P*N + P], stage 2 adds the KS slice sums.
+__global__ __launch_bounds__(256) void k_bwd_reduce_chunks1(int64_t K, int64_t P, int64_t N, int KS,
+                                                            const float* __restrict__ dal_part,
+                                                            const float* __restrict__ dbias_part,
+                                                            float* __restrict__ tmp) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int s = blockIdx.y;
+  const int64_t PN = P * N;
+  const int64_t k0 = (K * s) / KS, k1 = (K * (s + 1)) / KS;
+  if (e < PN) {
+    float v = 0.0f;
+    for (int64_t k = k0; k < k1; k++) v += dal_part[k * PN + e];
+    tmp[static_cast<int64_t>(s) * (PN + P) + e] = v;
+  } else if (e < PN + P) {
+    const int64_t q = e - PN;
+    float v = 0.0f;
+    for (int64_t k = k0; k < k1; k++) v += dbias_part[k * P + q];
+    tmp[static_cast<int64_t>(s) * (PN + P) + e] = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_bwd_reduce_chunks2(int64_t P, int64_t N, int KS, const float* __restrict__ tmp,
+                                                            float* __restrict__ dalpha, float* __restrict__ dbias) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t PN = P * N;
-  if (dalpha && e < PN) {
-    float v = 0.0f;
-    for (int64_t k = 0; k < K; k++) v += dal_part[k * PN + e];
-    dalpha[e] = v;
-  }
-  if (dbias && e < P) {
-    float v = 0.0f;
-    for (int64_t k = 0; k < K; k++) v += dbias_part[k * P + e];
-    dbias[e] = v;
+  if (e >= PN + P) return;
+  float v = 0.0f;
+  for (int s = 0; s < KS; s++) v += tmp[static_cast<int64_t>(s) * (PN + P) + e];
+  if (e < PN) {
+    if (dalpha) dalpha[e] = v;
+  } else if (dbias) {
+    dbias[e - PN] = v;
   }
 }
 
@@ -230,7 +248,7 @@ bool bwd_plan(int64_t P, int64_t N, int C, BwdPlan* pl) {
   const int wpb = kWpb;
   // LDS: two staging buffers of 3 rows x S tokens x N states, the per-wave
   // transpose area [2N][CH] and the per-wave token sums [S][2N]
-  const size_t floats = 2 * 3 * static_cast<size_t>(S) * N + static_cast<size_t>(wpb) * (2 * N * CH + S * 2 * N);
+  const size_t floats = 2 * 3 * static_cast<size_t>(S) * N + static_cast<size_t>(wpb) * (2 * N * (CH + 1) + S * 2 * N);
   if (floats * 4 > 160 * 1024) return false;
   (void)C;
   const int64_t NB = (P + CH - 1) / CH;
@@ -284,8 +302,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
       a.T, a.P, OUT, pl.NBW, a.part, static_cast<IO*>(a.dY), a.ldy);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.dalpha || a.dbias) {
-    k_bwd_reduce_chunks<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, a.dal_part,
-                                                                                a.dbias_part, a.dalpha, a.dbias);
+    // the chunk aggregates (umu) are dead after the carry pass: reuse them as scratch
+    int KS = static_cast<int>(K < 64 ? K : 64);
+    while (KS > 1 && static_cast<int64_t>(KS) * (PN + a.P) > K * PN + a.P) KS--;
+    const unsigned nb = static_cast<unsigned>((PN + a.P + 255) / 256);
+    k_bwd_reduce_chunks1<<<dim3(nb, static_cast<unsigned>(KS)), 256, 0, st>>>(K, a.P, a.N, KS, a.dal_part,
+                                                                             a.dbias_part, a.umu);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_bwd_reduce_chunks2<<<nb, 256, 0, st>>>(a.P, a.N, KS, a.umu, a.dalpha, a.dbias);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   (void)CH;

@@ -75,11 +75,29 @@ __device__ __forceinline__ float one_minus_exp_neg(float s) {
   return s > 0.5f ? big : small;
 }
 
+// v + v(lane ^ D) for a compile-time lane distance D: DPP for 1 and 2,
+// v_permlane32_swap for 32 (it exchanges the two 32-lane halves: the sum of
+// its two results is the pairwise sum on every lane), ds_bpermute otherwise.
+template <int D>
+__device__ __forceinline__ float xor_sum(float v) {
+  if constexpr (D == 1) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  } else if constexpr (D == 2) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  } else if constexpr (D == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    return v + __shfl_xor(v, D, 64);
+  }
+}
+
 // Sum over the G lane groups of one channel (lanes pl, pl+CH, pl+2CH, ...).
 template <int G, int CH>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int d = CH; d < 64; d <<= 1) v += __shfl_xor(v, d, 64);
+  if constexpr (CH <= 32 && G >= 2) v = xor_sum<CH>(v);
+  if constexpr (CH <= 16 && G >= 4) v = xor_sum<2 * CH>(v);
+  if constexpr (CH <= 8 && G >= 8) v = xor_sum<4 * CH>(v);
   return v;
 }
 

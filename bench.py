@@ -143,6 +143,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--phases", action="store_true", help="print the per-phase breakdown to stderr")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of MIB MiB three times (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -150,6 +153,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, device="cuda:0", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3}), flush=True)
+        return
 
     import adjoint_gradients_amd as agm
     from ssm_inputs import CONFIGS, make_layer_device

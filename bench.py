@@ -11,6 +11,7 @@ seeded and resident in HBM before the timed region.  Prints one JSON line.
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -40,9 +41,20 @@ BWD_PHASES = ["bwd_local", "bwd_carry", "bwd_main", "bwd_reduce", "wgrad_gemm", 
 def algorithmic(name, T, P, N, C, W, s_io):
     """Per-launch algorithmic work of a phase: (bytes, flops, valu_ops).
 
-    Bytes count each compulsory HBM stream once; valu_ops counts the VALU
-    issue slots of the method's arithmetic per (t, p, n) element (a hardware
-    exp2 counts 2: it issues at half rate on gfx950)."""
+    Bytes count each compulsory HBM stream once.  valu_ops counts the VALU
+    issue slots of the method's own arithmetic per (t, p, n) element, a
+    hardware exp2 counting 2 (it issues at half rate on gfx950):
+      a_t = exp(-alpha s_t)                          mul + exp        3
+      h_t = a_t h_{t-1} + b_t x_t                    mul + fma        2
+      y_t += c_t h_t                                 fma              1
+      mu_i = a_{i+1} mu_{i+1} + g_i c_i              mul + fma        2
+      window term - g_{i+W} c_{i+W} D_i,
+        D_i = exp(-alpha (S_{i+W} - S_i))            mul + exp + mul + fma   5
+      da = mu h_{i-1}; da a; dDelta and dalpha sums  mul, mul, fma, fma      4
+      db = sum_p mu x ; dc = sum_p g h               (mul + add) x 2         4
+      dx_dir = sum_n mu b                            fma              1
+    Per-(t, p) work (softplus, sigma, the dDelta scale) is amortised over N
+    and left out."""
     E = T * P * N
     K = (T + C - 1) // C
     win = W < T
@@ -59,9 +71,9 @@ def algorithmic(name, T, P, N, C, W, s_io):
     if name == "bwd_carry":
         return (K * P * N * 8 + K * P * 8, 0, 4 * K * P * N)
     if name == "bwd_main":
-        # survey per-token figure: x, s, g, b, c, h_ckpt, dDelta
+        # per token: x, s, g, b, c, dDelta (io) and db/dc, plus h_ckpt once per chunk
         return (T * (P * s_io + 4 * P + 4 * P + 8 * N + P * s_io + 8 * N) + K * P * N * 4, 0,
-                (24 if win else 16) * E)
+                (21 if win else 16) * E)
     if name == "bwd_reduce":
         return (T * 2 * N * 4 * 2, 0, 0)
     if name == "wgrad_gemm":
@@ -69,6 +81,50 @@ def algorithmic(name, T, P, N, C, W, s_io):
     if name == "dx_gemm":
         return (T * ((P + 2 * N) * s_io + 8 * P), 2.0 * T * P * (P + 2 * N), 0)
     return (0, 0, 0)
+
+
+# Sources each phase's kernels are compiled from: a stored counter reading is
+# only used while these files are byte-identical to when it was taken.
+CSRC = os.path.join(ROOT, "adjoint_gradients_amd", "csrc")
+PHASE_SOURCES = {
+    "bwd_main": ["scan_bwd.hip", "bwd_main.inl", "ssm_common.hpp", "ssm_kernels.hpp"],
+    "bwd_local": ["scan_bwd.hip", "bwd_main.inl", "ssm_common.hpp", "ssm_kernels.hpp"],
+    "fwd_final": ["scan_fwd.hip", "ssm_common.hpp", "ssm_kernels.hpp"],
+    "fwd_local": ["scan_fwd.hip", "ssm_common.hpp", "ssm_kernels.hpp"],
+    "proj_gemm": ["gemm.hip", "gemm_bf16.inl", "ssm_kernels.hpp"],
+    "wgrad_gemm": ["gemm.hip", "gemm_bf16.inl", "ssm_kernels.hpp"],
+}
+
+
+def source_hash(phase):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in PHASE_SOURCES.get(phase, []):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(phase, workload):
+    """HBM bytes per launch from profiles/traffic_<phase>_<workload>.md (FETCH_SIZE
+    and WRITE_SIZE, calibrated against a plain copy), or None when there is no
+    such summary or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{phase}_{workload}.md")
+    if phase not in PHASE_SOURCES or not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            m = re.match(r"^- (\w+): `?([^`\s]+)`?", line.strip())
+            if m:
+                fields[m.group(1)] = m.group(2)
+    if fields.get("source_sha256") != source_hash(phase):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 class HipEvents:
@@ -141,12 +197,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="cfg3", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-tokens", type=int, default=65536,
+                    help="tokens of the workload the fp64 oracle is timed on (the CPU baseline sample)")
+    ap.add_argument("--source-hash", metavar="PHASE", default=None,
+                    help="print the hash of the sources a phase's kernels are built from and exit")
     ap.add_argument("--phases", action="store_true", help="print the per-phase breakdown to stderr")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB three times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     args = ap.parse_args()
+    if args.source_hash:
+        print(source_hash(args.source_hash))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
               "the time-sharded design is described in DESIGN.md.", file=sys.stderr)
@@ -249,14 +311,17 @@ def main():
     if fl > 0:
         peak = MFMA_BF16_PEAK_TFS if io == "bf16" else MFMA_F32_PEAK_TFS
         ach = fl / (ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
-                "traffic": None}
+        roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak}
     else:
         ach = ops / (ms * 1e-3) / 1e9
-        roof = {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_GOPS, "unit": "Gop/s", "frac": ach / VALU_PEAK_GOPS,
-                "traffic": None}
+        roof = {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_GOPS, "unit": "Gop/s",
+                "frac": ach / VALU_PEAK_GOPS}
+    # HBM bytes per launch from the stored counter reading (None if the kernel changed since)
+    roof["traffic"] = stored_traffic(name, args.workload)
+    roof["traffic_unit"] = "bytes/launch"
     hbm_ach = by / (ms * 1e-3) / 1e9
-    roof.update(kernel=name, ms=ms, hbm_achieved_gbs=hbm_ach, hbm_frac=hbm_ach / HBM_PEAK_GBS)
+    roof.update(kernel=name, ms=ms, algorithmic_bytes=by, hbm_achieved_gbs=hbm_ach,
+                hbm_frac=hbm_ach / HBM_PEAK_GBS)
 
     out = {
         "metric": "SSM adjoint-gradient tokens/s (fwd+adjoint+VJP) at T=1M; % HBM roofline",

@@ -207,13 +207,15 @@ def layer_grad(inp: dict, window: int | None = None, method: str = "auto",
     return out
 
 
-def channel_grad(inp: dict, chans, window: int | None = None, method: str = "auto") -> dict:
+def channel_grad(inp: dict, chans, window: int | None = None, method: str = "auto",
+                 g_cols: np.ndarray | None = None) -> dict:
     """Per-channel results for a subset of channels (large workloads).
 
     Channels are independent once b and c (which need every channel of x) are
     known, so Delta, y, dDelta, dxdir, dalpha, dbias and the dW_delta rows of
     the listed channels are exact; db and dc returned here are only the
-    contributions of these channels.
+    contributions of these channels.  g_cols, if given, is g restricted to
+    the listed channels ([T][len(chans)]); otherwise inp["g"] is sliced.
     """
     chans = np.asarray(chans, dtype=np.int64)
     x = inp["x"]
@@ -224,7 +226,7 @@ def channel_grad(inp: dict, chans, window: int | None = None, method: str = "aut
     pr = projections(inp, x=x, chans=chans)
     nc = len(chans)
     xc = _f64(x[:, chans])
-    gc = _f64(np.asarray(inp["g"])[:, chans])
+    gc = _f64(np.asarray(inp["g"])[:, chans] if g_cols is None else g_cols)
     alc = _f64(np.asarray(inp["alpha"])[chans])
     y = np.empty((T, nc))
     dD = np.empty((T, nc))

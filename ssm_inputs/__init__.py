@@ -15,7 +15,8 @@ standard normals unless stated:
     W_delta, W_B, W_C   (scaled by 1/sqrt(P))   -- repeated per layer for stacks
     u ~ U(1e-3, 1e-1) [P]                        -- only when bias="softplus_uniform"
     x [T][P], then g [T][P]                      -- drawn in row blocks
-alpha[p, n] = n + 1.  Inputs of io dtype bf16 are rounded from float32 by
+alpha[p, n] = n + 1.  x is multiplied by the case's x_scale (1 unless
+stated) before rounding.  Inputs of io dtype bf16 are rounded from float32 by
 round-to-nearest-even; g always stays float32.
 """
 from __future__ import annotations
@@ -45,6 +46,11 @@ class LayerCase:
              "softplus_values"   -> softplus(delta_bias) cycles through `bias_u`
     wdelta : "normal" (W ~ N(0, 1/P)) or "zero" (W_delta = 0; then softplus(Delta)
              equals softplus(delta_bias) exactly).
+    x_scale: standard deviation of x (x = x_scale * N(0, 1)).  The 4-layer
+             N=64 stack uses 1/sqrt(N): a layer's output is cubic in its input
+             (b, x and c are each linear in it), and with unit-variance x the
+             residual stream of that stack passes the float32 range by the
+             third layer.
     """
 
     name: str
@@ -58,6 +64,7 @@ class LayerCase:
     bias_u: tuple = ()
     wdelta: str = "normal"
     seed: int = 0
+    x_scale: float = 1.0
 
 
 # The five workloads of the hot path (sizes from the method's problem
@@ -68,7 +75,8 @@ CONFIGS = {
     2: LayerCase("cfg2_128k_bf16", 131072, 2048, 16, "bf16", (1024, 8192), seed=2),
     3: LayerCase("cfg3_1m_bf16", 1048576, 2048, 16, "bf16", (4096,),
                  bias="softplus_uniform", seed=3),
-    4: LayerCase("cfg4_stack4_bf16", 262144, 1536, 64, "bf16", (262144, 4096), K=4, seed=4),
+    4: LayerCase("cfg4_stack4_bf16", 262144, 1536, 64, "bf16", (262144, 4096), K=4, seed=4,
+                 x_scale=0.125),
 }
 
 
@@ -147,6 +155,8 @@ def make_layer(c: LayerCase, T: int | None = None) -> dict:
     d = _weights(rng, c)
     d["delta_bias"] = _bias(rng, c)
     x = _normal_rows(rng, T, c.P)
+    if c.x_scale != 1.0:
+        x *= np.float32(c.x_scale)
     if c.io == "bf16":
         x = bf16_round(x)
     g = _normal_rows(rng, T, c.P)
@@ -166,6 +176,8 @@ def make_stack(c: LayerCase, K: int | None = None, T: int | None = None) -> dict
         w["alpha"] = _alpha(c)
         layers.append(w)
     x = _normal_rows(rng, T, c.P)
+    if c.x_scale != 1.0:
+        x *= np.float32(c.x_scale)
     if c.io == "bf16":
         x = bf16_round(x)
     g = _normal_rows(rng, T, c.P)
@@ -188,6 +200,8 @@ def make_layer_device(c: LayerCase, device="cuda", T: int | None = None) -> dict
     gen = torch.Generator(device=device)
     gen.manual_seed(1_000_003 * (c.seed + 1))
     x = torch.randn(T, c.P, generator=gen, device=device, dtype=torch.float32)
+    if c.x_scale != 1.0:
+        x *= c.x_scale
     if c.io == "bf16":
         x = x.to(torch.bfloat16)
     g = torch.randn(T, c.P, generator=gen, device=device, dtype=torch.float32)

@@ -1,0 +1,39 @@
+"""CPU checks behind readings of the method's workload descriptions.
+
+The 4-layer stack (P=1536, N=64) states the weight distribution but not the
+input scale.  A layer's output is cubic in its input (b, x and c are each
+linear in it), so unit-variance inputs leave the float32 range by the third
+layer; x0 ~ N(0, 1/N) keeps the residual stream of the same order as its
+input with each layer still adding a visible share.  Both facts are checked
+here with the oracle's forward on a token prefix.
+"""
+import dataclasses
+
+import numpy as np
+
+import oracle
+from ssm_inputs import CONFIGS, make_stack
+
+F32_MAX = float(np.finfo(np.float32).max)
+
+
+def _rms(a):
+    return float(np.sqrt(np.mean(np.square(a))))
+
+
+def test_stack_unit_inputs_overflow_f32():
+    case = dataclasses.replace(CONFIGS[4], x_scale=1.0)
+    fw = oracle.stack_forward(make_stack(case, T=48))
+    assert np.max(np.abs(fw["r_final"])) > F32_MAX
+
+
+def test_stack_scaled_inputs_stay_in_range():
+    case = CONFIGS[4]
+    assert case.x_scale == 1.0 / np.sqrt(case.N)
+    fw = oracle.stack_forward(make_stack(case, T=48))
+    r = [_rms(x) for x in fw["x_layers"]] + [_rms(fw["r_final"])]
+    y = [_rms(v) for v in fw["y_layers"]]
+    assert all(np.isfinite(r))
+    assert max(r) < 4 * r[0]
+    # each layer's output is a visible share of its input
+    assert all(0.01 * rk < yk for rk, yk in zip(r, y))

@@ -109,6 +109,24 @@ FwdWs carve_fwd(Carver& cv, const ssm_dims* d) {
 
 int splitk_for(const ssm_dims* d) {
   const int64_t M = d->P + 2 * d->N;
+  if (d->io == SSM_BF16) {
+    // 256 x 256 tiles, one workgroup per CU at a time on 256 CUs: pick the
+    // split count (8..64, at least 512 tokens each) whose workgroup count
+    // fills the last round best; ties go to fewer splits
+    const int64_t tiles = ((M + 255) / 256) * ((d->P + 255) / 256);
+    int best = 1;
+    double best_eff = -1.0;
+    for (int s = 8; s <= 64; s++) {
+      if (d->T / s < 512) break;
+      const int64_t wg = tiles * s;
+      const double eff = static_cast<double>(wg) / (256.0 * static_cast<double>((wg + 255) / 256));
+      if (eff > best_eff + 1e-9) {
+        best_eff = eff;
+        best = s;
+      }
+    }
+    return best;
+  }
   const int64_t tiles = ((M + 127) / 128) * ((d->P + 127) / 128);
   int64_t s = 2048 / (tiles > 0 ? tiles : 1);
   const int64_t cap = d->T / 512;

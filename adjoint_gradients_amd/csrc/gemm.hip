@@ -247,6 +247,7 @@ hipError_t run(const GemmOperands& op, int splits, int64_t kps, Epi epi, hipStre
 }  // namespace
 
 #include "gemm_bf16.inl"
+#include "gemm_dl.inl"
 
 namespace {
 
@@ -287,9 +288,17 @@ __global__ __launch_bounds__(256) void k_residual_init(int64_t n, const void* __
 
 }  // namespace
 
+// bf16 GEMMs take the direct-to-LDS kernel where its shape conditions hold,
+// the register-staged one otherwise.
+template <class Epi>
+static hipError_t run_bf16(const GemmOperands& op, int splits, int64_t kps, Epi epi, hipStream_t st) {
+  if (gdl::supports(op, kps)) return gdl::run(op, splits, kps, epi, st);
+  return gbf::run(op, splits, kps, epi, st);
+}
+
 hipError_t gemm_projection(const GemmOperands& op, bool bf16, const EpiProjArgs& e, hipStream_t st) {
   EpiProj epi{e};
-  return bf16 ? gbf::run(op, 1, op.K, epi, st) : run<float>(op, 1, op.K, epi, st);
+  return bf16 ? run_bf16(op, 1, op.K, epi, st) : run<float>(op, 1, op.K, epi, st);
 }
 
 hipError_t gemm_splitk(const GemmOperands& op, bool bf16, int splits, float* part, hipStream_t st) {
@@ -299,14 +308,14 @@ hipError_t gemm_splitk(const GemmOperands& op, bool bf16, int splits, float* par
   if (bf16) {
     int64_t kpb = (op.K + splits - 1) / splits;
     kpb = ((kpb + gbf::BK - 1) / gbf::BK) * gbf::BK;
-    return gbf::run(op, splits, kpb, epi, st);
+    return run_bf16(op, splits, kpb, epi, st);
   }
   return run<float>(op, splits, kps, epi, st);
 }
 
 hipError_t gemm_add(const GemmOperands& op, bool bf16, const EpiAddArgs& e, hipStream_t st) {
   EpiAdd epi{e, op.Nc};
-  return bf16 ? gbf::run(op, 1, op.K, epi, st) : run<float>(op, 1, op.K, epi, st);
+  return bf16 ? run_bf16(op, 1, op.K, epi, st) : run<float>(op, 1, op.K, epi, st);
 }
 
 hipError_t reduce_weight_grads(const float* part, int splits, int64_t P, int64_t N, float* dWd, float* dWb,

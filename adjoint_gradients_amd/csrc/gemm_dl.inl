@@ -1,0 +1,255 @@
+// gemm_dl.inl -- bf16 MFMA GEMM with direct-to-LDS operand loads for gfx950
+// (included by gemm.hip after gemm_bf16.inl).
+//
+// C[m][n] = sum_k A[m][k] B[n][k], fp32 accumulation, each element handed to
+// an epilogue.  Operands may be K-contiguous (X[r][k]) or K-outer (X[k][r]).
+//
+// Macro tile 256 x 256 per 256-thread workgroup, one wavefront per SIMD, each
+// owning 128 x 128 = 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 (256 fp32
+// accumulators per lane).  K advances in stages of 32: every operand tile of a
+// stage (256 x 32 bf16, 16 KB) is fetched by 16 wave-wide
+// global_load_lds_dwordx4 instructions straight into LDS, so no register
+// holds operands in flight and no VALU work moves them.  Four LDS stages
+// (128 KB) let the loads run three stages ahead of the MFMAs; each stage is
+// consumed after a vmcnt wait on the wave's own loads and one barrier.
+// Tile layouts, swizzles and the operand fetches (ds_read_b128 for
+// K-contiguous tiles, the transposing ds_read_b64_tr_b16 for K-outer ones)
+// are defined in gemm_dl_index.hpp, where a host test checks them
+// exhaustively.
+//
+// Edges: rows of a K-contiguous operand beyond the matrix are clamped to its
+// last row, and 8-column chunks of a K-outer operand beyond it to its last
+// chunk: the loads stay inside the matrix and the values they bring only
+// reach output rows / columns that the epilogue discards.  The K range of
+// every split must be a multiple of 32, the leading dimensions multiples of
+// 8, and K-outer operands must have a multiple of 8 columns; other shapes use
+// the register-staged kernel.
+
+#include "gemm_dl_index.hpp"
+
+namespace gdl {
+
+constexpr int NT = 256;
+constexpr int NS = 4;                          // LDS stages
+constexpr int kStageBytes = 2 * kTileBytes;    // A tile, then B tile
+constexpr size_t kLdsBytes = static_cast<size_t>(NS) * kStageBytes;
+constexpr int kLoadsPerWave = 2 * kInstrPerTile / 4;  // both operands, per stage
+constexpr int kXcds = 8;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// The operand loads, the waits on them and the barrier are written as inline
+// assembly.  The compiler's wait insertion does not follow LDS written by
+// DMA through one dynamically indexed LDS array: given the builtin it waits
+// for every outstanding load before each LDS read, and a workgroup fence
+// adds a full wait before each barrier, which would serialise the pipeline.
+// Here the waits are placed by hand (vmcnt counts this wave's loads in issue
+// order), and the "memory" clobbers keep the compiler from moving LDS
+// accesses across a wait or a barrier.
+
+// 16 bytes from global address g (per lane) to LDS address lds + 16 * lane
+// (lds wave-uniform).  M0 carries the LDS base; it is saved and restored.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(g)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(n): at most n of this wave's loads still outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+}
+
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <bool KC>
+struct Operand {
+  const bf16_t* base;  // wave-uniform: the tile corner at k = 0
+  int64_t ld;
+  uint32_t off[4];     // per-lane element offsets of this wave's 4 load instructions
+  int rd[2];           // per-lane byte offsets of the operand fetches (see read())
+
+  __device__ __forceinline__ void init(const bf16_t* X, int64_t ldx, int64_t R, int64_t r0, int wave, int lane,
+                                       int rb) {
+    ld = ldx;
+    base = X + (KC ? r0 * ldx : r0);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int gi = wave * 4 + j;
+      if constexpr (KC) {
+        const int64_t row = r0 + kc_load_row(gi, lane);
+        const int64_t rr = (row < R ? row : R - 1) - r0;
+        off[j] = static_cast<uint32_t>(rr * ldx + 8 * kc_load_chunk(gi, lane));
+      } else {
+        const int64_t col = 8 * static_cast<int64_t>(ko_load_chunk(gi, lane));
+        const int64_t cc = (r0 + col + 8 <= R) ? col : R - 8 - r0;
+        off[j] = static_cast<uint32_t>(ko_load_krow(gi, lane) * ldx + cc);
+      }
+    }
+    if constexpr (KC) {
+      rd[0] = kc_read_off(lane, rb, 0);  // + 2048 per further 32-row block, + 32 for q = 1
+      rd[1] = kc_read_off(lane, rb, 1);
+    } else {
+      rd[0] = ko_read_off(lane, rb, 0, 0);       // even 32-row blocks (+128 bytes per 2 blocks)
+      rd[1] = ko_read_off(lane, rb + 32, 0, 0);  // odd blocks
+    }
+  }
+
+  // Stage loads for K offset k0 into the tile at LDS address `tile`.
+  __device__ __forceinline__ void issue(uint32_t tile, int64_t k0, int wave) const {
+    const bf16_t* src = base + (KC ? k0 : k0 * ld);
+#pragma unroll
+    for (int j = 0; j < 4; j++) dma16(src + off[j], tile + static_cast<uint32_t>((wave * 4 + j) * 1024));
+  }
+
+  // MFMA operand (8 bf16) of 32-row block i of this wave, k sub-step q.
+  __device__ __forceinline__ bf16x8_t read(const lds_char* tile, int i, int q) const {
+    if constexpr (KC) {
+      const int o = rd[q] + i * 2048;
+      return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const __attribute__((address_space(3))) uint4*>(tile + o));
+    } else {
+      const int o = rd[i & 1] + (i >> 1) * 128 + q * 8192;
+      typedef __attribute__((address_space(3))) v4s lv4s;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s*)(tile + o));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s*)(tile + o + 2048));
+      struct Pair { v4s a, b; } pr{lo, hi};
+      return __builtin_bit_cast(bf16x8_t, pr);
+    }
+  }
+};
+
+template <class Epi, bool a_kc, bool b_kc>
+__global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_t K, const bf16_t* __restrict__ A,
+                                                   int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
+                                                   int64_t k_per_split, int64_t tilesM, int64_t tilesN, Epi epi) {
+  extern __shared__ __attribute__((aligned(1024))) char smem_dl[];
+  lds_char* const lds = (lds_char*)(smem_dl);  // generic -> LDS address space
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // XCD-aware bijection of the workgroup id onto (split, tile row, tile column)
+  const int64_t nwg = gridDim.x;
+  const int64_t pid = blockIdx.x;
+  const int64_t xcd = pid % kXcds, loc = pid / kXcds;
+  const int64_t full = nwg / kXcds, rem = nwg % kXcds;
+  const int64_t vid = xcd < rem ? xcd * (full + 1) + loc : rem * (full + 1) + (xcd - rem) * full + loc;
+  const int64_t tn = vid % tilesN;
+  const int64_t tm = (vid / tilesN) % tilesM;
+  const int z = static_cast<int>(vid / (tilesN * tilesM));
+  const int64_t m0 = tm * kRows, n0 = tn * kRows;
+  const int64_t kbeg = static_cast<int64_t>(z) * k_per_split;
+  const int64_t kend = (kbeg + k_per_split < K) ? kbeg + k_per_split : K;
+  const int64_t nsteps = kbeg < kend ? (kend - kbeg) / kBK : 0;
+
+  Operand<a_kc> oa;
+  Operand<b_kc> ob;
+  oa.init(A, lda, M, m0, wave, l, wm * 128);
+  ob.init(B, ldb, Nc, n0, wave, l, wn * 128);
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  auto issue = [&](int64_t step) {
+    const uint32_t st = lds_base + static_cast<uint32_t>((step % NS) * kStageBytes);
+    oa.issue(st, kbeg + step * kBK, wave);
+    ob.issue(st + kTileBytes, kbeg + step * kBK, wave);
+  };
+
+#pragma unroll
+  for (int p = 0; p < NS - 1; p++)
+    if (p < nsteps) issue(p);
+
+  for (int64_t s = 0; s < nsteps; s++) {
+    // the wave's own loads of step s are done once only later steps' loads
+    // (at most NS - 2 of them, kLoadsPerWave each) are still outstanding
+    const int64_t later = nsteps - 1 - s;
+    if (later >= NS - 2) wait_vm<(NS - 2) * kLoadsPerWave>();
+    else if (later == 1) wait_vm<kLoadsPerWave>();
+    else wait_vm<0>();
+    barrier();  // every wave's loads of step s are in LDS; step s - 1 is consumed
+    if (s + NS - 1 < nsteps) issue(s + NS - 1);
+    const lds_char* st = lds + (s % NS) * kStageBytes;
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      bf16x8_t af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) af[i] = oa.read(st, i, q);
+#pragma unroll
+      for (int j = 0; j < 4; j++) bfr[j] = ob.read(st + kTileBytes, j, q);
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int64_t col = n0 + wn * 128 + j * 32 + (l & 31);
+    if (col < Nc) {
+      const auto q = epi.prep(col, z);
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int64_t row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
+          if (row < M) epi.apply(q, row, acc[i][j][r]);
+        }
+    }
+  }
+}
+
+// Whether the direct-to-LDS kernel takes this GEMM (see the header comment).
+inline bool supports(const GemmOperands& op, int64_t kps) {
+  if (op.M < 1 || op.Nc < 1 || op.K < 1) return false;
+  if (op.lda % 8 != 0 || op.ldb % 8 != 0) return false;
+  if (kps % kBK != 0 || op.K % kBK != 0) return false;
+  if (!op.a_kc && op.M % 8 != 0) return false;
+  if (!op.b_kc && op.Nc % 8 != 0) return false;
+  // per-lane 32-bit element offsets
+  const int64_t span_a = op.a_kc ? kRows * op.lda : kBK * op.lda;
+  const int64_t span_b = op.b_kc ? kRows * op.ldb : kBK * op.ldb;
+  return span_a < (int64_t(1) << 31) && span_b < (int64_t(1) << 31);
+}
+
+template <class Epi, bool AKC, bool BKC>
+hipError_t run_t(const GemmOperands& op, int splits, int64_t kps, Epi epi, hipStream_t st) {
+  const int64_t tilesM = (op.M + kRows - 1) / kRows, tilesN = (op.Nc + kRows - 1) / kRows;
+  const int64_t nwg = tilesM * tilesN * splits;
+  auto kern = k_gemm_dl<Epi, AKC, BKC>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+  if (e != hipSuccess) return e;
+  kern<<<static_cast<unsigned>(nwg), NT, kLdsBytes, st>>>(op.M, op.Nc, op.K, static_cast<const bf16_t*>(op.A),
+                                                         op.lda, static_cast<const bf16_t*>(op.B), op.ldb, kps,
+                                                         tilesM, tilesN, epi);
+  return hipGetLastError();
+}
+
+template <class Epi>
+hipError_t run(const GemmOperands& op, int splits, int64_t kps, Epi epi, hipStream_t st) {
+  if (op.a_kc && op.b_kc) return run_t<Epi, true, true>(op, splits, kps, epi, st);
+  if (!op.a_kc && !op.b_kc) return run_t<Epi, false, false>(op, splits, kps, epi, st);
+  if (op.a_kc && !op.b_kc) return run_t<Epi, true, false>(op, splits, kps, epi, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdl

@@ -66,10 +66,12 @@ struct EpiProj {
     }
     return q;
   }
-  __device__ __forceinline__ void apply(const Prep& q, int64_t row, float v) const {
+  __device__ __forceinline__ void apply(const Prep& q, int64_t row, float v) const { at(q, row * q.ld, v); }
+  // element at row offset `off` (= row * q.ld) of the prepared column
+  __device__ __forceinline__ void at(const Prep& q, int64_t off, float v) const {
     const float w = v + q.bias;
     const float sp = softplus_f(w);
-    q.base[row * q.ld] = q.sp ? sp : w;
+    q.base[off] = q.sp ? sp : w;
   }
 };
 
@@ -81,11 +83,13 @@ struct EpiPart {
   }
   struct Prep {
     float* base;
+    int64_t ld;
   };
   __device__ __forceinline__ Prep prep(int64_t col, int z) const {
-    return Prep{part + static_cast<int64_t>(z) * M * Nc + col};
+    return Prep{part + static_cast<int64_t>(z) * M * Nc + col, Nc};
   }
   __device__ __forceinline__ void apply(const Prep& q, int64_t row, float v) const { q.base[row * Nc] = v; }
+  __device__ __forceinline__ void at(const Prep& q, int64_t off, float v) const { q.base[off] = v; }
 };
 
 struct EpiAdd {
@@ -99,10 +103,12 @@ struct EpiAdd {
   }
   struct Prep {
     int64_t col;
+    int64_t ld;
   };
-  __device__ __forceinline__ Prep prep(int64_t col, int) const { return Prep{col}; }
-  __device__ __forceinline__ void apply(const Prep& q, int64_t row, float v) const {
-    const int64_t idx = row * Nc + q.col;
+  __device__ __forceinline__ Prep prep(int64_t col, int) const { return Prep{col, Nc}; }
+  __device__ __forceinline__ void apply(const Prep& q, int64_t row, float v) const { at(q, row * Nc, v); }
+  __device__ __forceinline__ void at(const Prep& q, int64_t off, float v) const {
+    const int64_t idx = off + q.col;
     float r = v + e.add0[idx];
     if (e.add1) r += e.add1[idx];
     e.out[idx] = r;

@@ -25,6 +25,8 @@
 // 8, and K-outer operands must have a multiple of 8 columns; other shapes use
 // the register-staged kernel.
 
+#include <type_traits>
+
 #include "gemm_dl_index.hpp"
 
 namespace gdl {
@@ -45,8 +47,11 @@ typedef __attribute__((address_space(3))) char lds_char;
 // for every outstanding load before each LDS read, and a workgroup fence
 // adds a full wait before each barrier, which would serialise the pipeline.
 // Here the waits are placed by hand (vmcnt counts this wave's loads in issue
-// order), and the "memory" clobbers keep the compiler from moving LDS
-// accesses across a wait or a barrier.
+// order).  The waits and the barrier carry "memory" clobbers, so no LDS
+// access moves across them; the loads themselves do not, so the compiler may
+// interleave them with the operand reads and MFMAs of the current stage (they
+// write a stage nobody reads until the loads have been waited for), while
+// volatile asm statements keep their order among themselves.
 
 // 16 bytes from global address g (per lane) to LDS address lds + 16 * lane
 // (lds wave-uniform).  M0 carries the LDS base; it is saved and restored.
@@ -59,8 +64,7 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
       "global_load_lds_dwordx4 %2, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds), "v"(g)
-      : "memory");
+      : "s"(lds), "v"(g));
 }
 
 // s_waitcnt vmcnt(n): at most n of this wave's loads still outstanding.
@@ -77,7 +81,7 @@ struct Operand {
   const bf16_t* base;  // wave-uniform: the tile corner at k = 0
   int64_t ld;
   uint32_t off[4];     // per-lane element offsets of this wave's 4 load instructions
-  int rd[2];           // per-lane byte offsets of the operand fetches (see read())
+  int rd[KC ? 2 : 4];  // per-lane byte offsets of the operand fetches (see read())
 
   __device__ __forceinline__ void init(const bf16_t* X, int64_t ldx, int64_t R, int64_t r0, int wave, int lane,
                                        int rb) {
@@ -100,16 +104,20 @@ struct Operand {
       rd[0] = kc_read_off(lane, rb, 0);  // + 2048 per further 32-row block, + 32 for q = 1
       rd[1] = kc_read_off(lane, rb, 1);
     } else {
-      rd[0] = ko_read_off(lane, rb, 0, 0);       // even 32-row blocks (+128 bytes per 2 blocks)
-      rd[1] = ko_read_off(lane, rb + 32, 0, 0);  // odd blocks
+#pragma unroll
+      for (int i = 0; i < 4; i++) rd[i] = ko_read_off(lane, rb + 32 * i, 0, 0);  // + 8192 q, + 2048 h
     }
   }
 
-  // Stage loads for K offset k0 into the tile at LDS address `tile`.
-  __device__ __forceinline__ void issue(uint32_t tile, int64_t k0, int wave) const {
+  // Stage loads for K offset k0 into the tile at LDS address `tile`: this
+  // wave's 4 load instructions (issue) or its j-th one (issue_one).
+  __device__ __forceinline__ void issue_one(uint32_t tile, int64_t k0, int wave, int j) const {
     const bf16_t* src = base + (KC ? k0 : k0 * ld);
+    dma16(src + off[j], tile + static_cast<uint32_t>((wave * 4 + j) * 1024));
+  }
+  __device__ __forceinline__ void issue(uint32_t tile, int64_t k0, int wave) const {
 #pragma unroll
-    for (int j = 0; j < 4; j++) dma16(src + off[j], tile + static_cast<uint32_t>((wave * 4 + j) * 1024));
+    for (int j = 0; j < 4; j++) issue_one(tile, k0, wave, j);
   }
 
   // MFMA operand (8 bf16) of 32-row block i of this wave, k sub-step q.
@@ -118,7 +126,7 @@ struct Operand {
       const int o = rd[q] + i * 2048;
       return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const __attribute__((address_space(3))) uint4*>(tile + o));
     } else {
-      const int o = rd[i & 1] + (i >> 1) * 128 + q * 8192;
+      const int o = rd[i] + q * 8192;
       typedef __attribute__((address_space(3))) v4s lv4s;
       const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s*)(tile + o));
       const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s*)(tile + o + 2048));
@@ -176,43 +184,96 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_
   for (int p = 0; p < NS - 1; p++)
     if (p < nsteps) issue(p);
 
-  for (int64_t s = 0; s < nsteps; s++) {
-    // the wave's own loads of step s are done once only later steps' loads
-    // (at most NS - 2 of them, kLoadsPerWave each) are still outstanding
+  // One stage: multiply LDS stage s % NS; with REFILL, also load stage
+  // s + NS - 1 (into the stage consumed in step s - 1).  Fragments of both k
+  // sub-steps are held in two register sets.  The volatile load statements
+  // are scheduling boundaries, so the order written here is the issue order:
+  // sub-step 0's operand reads first, the eight loads spread over sub-step
+  // 0's MFMAs, sub-step 1's reads in between.
+  auto stage_step = [&](int64_t s, auto refill_tag) {
+    constexpr bool REFILL = decltype(refill_tag)::value;
+    const lds_char* st = lds + (s % NS) * kStageBytes;
+    const int64_t kn = kbeg + (s + NS - 1) * kBK;
+    const uint32_t stn = lds_base + static_cast<uint32_t>(((s + NS - 1) % NS) * kStageBytes);
+    bf16x8_t af[2][4], bfr[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) af[0][i] = oa.read(st, i, 0);
+#pragma unroll
+    for (int j = 0; j < 4; j++) bfr[0][j] = ob.read(st + kTileBytes, j, 0);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[0][j], acc[i][j], 0, 0, 0);
+        if constexpr (REFILL) {
+          if (j == 1) oa.issue_one(stn, kn, wave, i);
+          if (j == 3) ob.issue_one(stn + kTileBytes, kn, wave, i);
+        }
+      }
+      af[1][i] = oa.read(st, i, 1);
+      bfr[1][i] = ob.read(st + kTileBytes, i, 1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[1][j], acc[i][j], 0, 0, 0);
+  };
+
+  // Steady state: step s needs its own loads done while the loads of the
+  // NS - 2 later stages already issued may still be in flight.
+  int64_t s = 0;
+  for (; s + NS - 1 < nsteps; s++) {
+    wait_vm<(NS - 2) * kLoadsPerWave>();
+    barrier();  // every wave's loads of step s are in LDS; step s - 1 is consumed
+    stage_step(s, std::true_type{});
+  }
+  // Drain: no more loads to issue; fewer later stages outstanding.
+  for (; s < nsteps; s++) {
     const int64_t later = nsteps - 1 - s;
-    if (later >= NS - 2) wait_vm<(NS - 2) * kLoadsPerWave>();
+    if (later >= 2) wait_vm<2 * kLoadsPerWave>();
     else if (later == 1) wait_vm<kLoadsPerWave>();
     else wait_vm<0>();
-    barrier();  // every wave's loads of step s are in LDS; step s - 1 is consumed
-    if (s + NS - 1 < nsteps) issue(s + NS - 1);
-    const lds_char* st = lds + (s % NS) * kStageBytes;
-#pragma unroll
-    for (int q = 0; q < 2; q++) {
-      bf16x8_t af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) af[i] = oa.read(st, i, q);
-#pragma unroll
-      for (int j = 0; j < 4; j++) bfr[j] = ob.read(st + kTileBytes, j, q);
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
+    barrier();
+    stage_step(s, std::false_type{});
   }
 
+  // Epilogue.  Lane l holds, in acc[i][j][r], row m0 + 128 wm + 32 i +
+  // 8 (r / 4) + 4 (l / 32) + r % 4 of column n0 + 128 wn + 32 j + l % 32.  The
+  // element offsets (row * ld) are stepped by additions; interior tiles skip
+  // the row bound.
+  const bool full_rows = m0 + kRows <= M;
+  const int64_t row0 = m0 + wm * 128 + (l >> 5) * 4;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int64_t col = n0 + wn * 128 + j * 32 + (l & 31);
-    if (col < Nc) {
-      const auto q = epi.prep(col, z);
+    if (col >= Nc) continue;
+    const auto q = epi.prep(col, z);
+    const int64_t ld = q.ld;
+    int64_t oi = row0 * ld;
+    if (full_rows) {
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int i = 0; i < 4; i++, oi += 32 * ld) {
+        int64_t orr = oi;
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int64_t row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
-          if (row < M) epi.apply(q, row, acc[i][j][r]);
+        for (int rr = 0; rr < 4; rr++, orr += 8 * ld) {
+          int64_t o = orr;
+#pragma unroll
+          for (int r3 = 0; r3 < 4; r3++, o += ld) epi.at(q, o, acc[i][j][rr * 4 + r3]);
         }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; i++, oi += 32 * ld) {
+        int64_t orr = oi;
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++, orr += 8 * ld) {
+          int64_t o = orr;
+#pragma unroll
+          for (int r3 = 0; r3 < 4; r3++, o += ld)
+            if (row0 + i * 32 + rr * 8 + r3 < M) epi.at(q, o, acc[i][j][rr * 4 + r3]);
+        }
+      }
     }
   }
 }

@@ -13,15 +13,17 @@
 // banks.  Operand fetch: one ds_read_b128 per 8 values.
 //
 // K-outer operand (X[k][r], r fastest): LDS tile [32 k-rows][32 chunks of
-// 8 r] (512 bytes a k-row).  Chunk c of k-row p sits in slot c ^ (2 (p & 3)).
+// 8 r] (512 bytes a k-row).  Chunk c of k-row p sits in slot c ^ (4 (p & 3)).
 // Operand fetch: two ds_read_b64_tr_b16 per 8 values.  That instruction
 // works on 16-lane groups: lane j of a group receives element j % 4 of the
 // 8-byte pieces addressed by lanes j / 4, j / 4 + 4, j / 4 + 8, j / 4 + 12 of
 // its group, in that order.  So in group g (lanes 16 g .. 16 g + 15) lane
 // s supplies the address of the 4 values (k-row kb + s / 4, r = 16 (g % 2) +
 // 4 (s % 4) .. + 3), where kb = 8 (g / 2) + 4 h for the two halves h; lane
-// l then holds (r = l % 32, k = 8 (l / 32) + 4 h .. + 3).  The swizzle makes
-// the four k-rows of one read land on distinct banks.
+// l then holds (r = l % 32, k = 8 (l / 32) + 4 h .. + 3).  An 8-byte LDS read
+// is served 32 lanes at a time over the 64 banks: those lanes read the same
+// four k-rows, 64 bytes of each; the swizzle moves each k-row's 64 bytes to
+// its own quarter of the 256-byte bank window.
 #pragma once
 
 #include <stdint.h>
@@ -52,7 +54,7 @@ constexpr int kc_read_off(int l, int rb, int q) {
 // ---- K-outer tiles -----------------------------------------------------
 
 // Slot of chunk c (8 r) in LDS k-row p.
-constexpr int ko_slot(int p, int c) { return c ^ (2 * (p & 3)); }
+constexpr int ko_slot(int p, int c) { return c ^ (4 * (p & 3)); }
 
 // Load instruction gi (0..15), lane i: the k-row and the r-chunk it fetches.
 constexpr int ko_load_krow(int gi, int i) { return 2 * gi + i / 32; }

@@ -6,8 +6,10 @@
 // The transposed LDS read is modelled as measured on gfx950: in each 16-lane
 // group, lane j receives element j % 4 of the 8-byte pieces addressed by
 // lanes j / 4 + 4 r (r = 0..3) of the group.  Also checks that the loads
-// write every LDS byte exactly once and that the operand fetches of one
-// quarter-wave (16 lanes) touch distinct banks.
+// write every LDS byte exactly once and that the operand fetches served in
+// one LDS pass touch distinct banks (64 banks of 4 bytes; 16-byte reads are
+// served 16 lanes per pass, 8-byte reads 32 lanes per pass, as the bank
+// conflict counters on gfx950 show).
 #include <cstdio>
 #include <cstring>
 #include <set>
@@ -60,13 +62,15 @@ int main() {
               off[l] = ko_read_off(l, rb, q, h);
               CHECK(off[l] % 8 == 0 && off[l] >= 0 && off[l] + 8 <= kTileBytes, "ko offset %d", off[l]);
             }
-            for (int g = 0; g < 4; g++) {
+            for (int half = 0; half < 2; half++) {
               std::set<int> banks;
-              for (int s = 0; s < 16; s++) {
-                banks.insert((off[16 * g + s] / 4) % 64);
-                banks.insert((off[16 * g + s] / 4 + 1) % 64);
+              for (int s = 0; s < 32; s++) {
+                banks.insert((off[32 * half + s] / 4) % 64);
+                banks.insert((off[32 * half + s] / 4 + 1) % 64);
               }
-              CHECK(banks.size() == 32, "ko rb %d q %d h %d group %d: bank conflict (%zu banks)", rb, q, h, g, banks.size());
+              CHECK(banks.size() == 64, "ko rb %d q %d h %d half %d: bank conflict (%zu banks)", rb, q, h, half, banks.size());
+            }
+            for (int g = 0; g < 4; g++) {
               for (int j = 0; j < 16; j++) {
                 const int l = 16 * g + j;
                 for (int r = 0; r < 4; r++) {
@@ -82,17 +86,15 @@ int main() {
       }
   }
   // offsets the kernel derives instead of recomputing: K-contiguous fetches
-  // move by 2048 bytes per 32-row block; K-outer fetches by 128 bytes per two
-  // blocks (odd blocks keep their own base), 8192 per k sub-step and 2048 for
-  // the second transposed half
+  // move by 2048 bytes per 32-row block; K-outer fetches (one base per block)
+  // by 8192 per k sub-step and 2048 for the second transposed half
   for (int l = 0; l < 64; l++)
     for (int rb = 0; rb <= 128; rb += 128)
       for (int i = 0; i < 4; i++)
         for (int q = 0; q < 2; q++) {
           CHECK(kc_read_off(l, rb + 32 * i, q) == kc_read_off(l, rb, q) + 2048 * i, "kc linear l %d rb %d i %d q %d", l, rb, i, q);
           for (int h = 0; h < 2; h++)
-            CHECK(ko_read_off(l, rb + 32 * i, q, h) ==
-                      ko_read_off(l, rb + 32 * (i & 1), 0, 0) + 128 * (i >> 1) + 8192 * q + 2048 * h,
+            CHECK(ko_read_off(l, rb + 32 * i, q, h) == ko_read_off(l, rb + 32 * i, 0, 0) + 8192 * q + 2048 * h,
                   "ko linear l %d rb %d i %d q %d h %d", l, rb, i, q, h);
         }
   printf(fails ? "FAILED (%d)\n" : "layout OK\n", fails);

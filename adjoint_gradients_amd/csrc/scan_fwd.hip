@@ -137,27 +137,164 @@ __global__ __launch_bounds__(64) void k_fwd_final(int64_t T, int64_t P, int64_t 
   }
 }
 
+// ---------------------------------------------------------- staged variants
+// For N >= 4 and chunks whose rows fit in LDS: a 4-wavefront workgroup takes
+// 4 channel blocks of one chunk.  The chunk's per-token rows (b, and c for
+// the final pass), shared by all channels, are staged once into LDS by the
+// whole workgroup; the per-lane s and x come through an 8-token register
+// ring, so every load is issued 7 tokens before its use.
+constexpr int kFwdWpb = 4;
+constexpr int kFwdRing = 8;
+constexpr size_t kFwdRowLds = 32 * 1024;  // LDS bytes for staged rows
+
+template <int NQ>
+__device__ __forceinline__ void stage_rows(float* rows, const float* __restrict__ const (&src)[NQ], int64_t t0,
+                                          int len, int NN, int C, int tid) {
+  // rows[q][tau][n] = src[q][(t0 + tau) * NN + n], tau < len; float4 granularity
+  const int per = len * NN / 4;
+#pragma unroll
+  for (int q = 0; q < NQ; q++) {
+    const float4* s4 = reinterpret_cast<const float4*>(src[q] + t0 * NN);
+    float4* d4 = reinterpret_cast<float4*>(rows + static_cast<size_t>(q) * C * NN);
+    for (int e = tid; e < per; e += 64 * kFwdWpb) d4[e] = s4[e];
+  }
+}
+
+template <typename IO, int NL, int G, bool FINAL>
+__global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_t N, int C, int64_t NB,
+                                                    const float* __restrict__ sp, const IO* __restrict__ x,
+                                                    const float* __restrict__ b, const float* __restrict__ c,
+                                                    const float* __restrict__ alpha,
+                                                    const float* __restrict__ h_ckpt, float* __restrict__ y,
+                                                    float* __restrict__ hloc, double* __restrict__ ssum) {
+  constexpr int CH = 64 / G;
+  constexpr int NN = NL * G;
+  constexpr int D = kFwdRing;
+  extern __shared__ float rows[];  // [FINAL ? 2 : 1][C][NN]
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+  const int grp = lane / CH, pl = lane % CH;
+  const int64_t k = blockIdx.x;
+  const int64_t cb = static_cast<int64_t>(blockIdx.y) * kFwdWpb + w;
+  const int64_t p = cb * CH + pl;
+  const bool valid = cb < NB && p < P;
+  const int64_t pc = p < P ? p : P - 1;
+  const int n0 = grp * NL;
+  const int64_t t0 = k * C;
+  const int64_t t1 = (t0 + C < T) ? t0 + C : T;
+  const int len = static_cast<int>(t1 - t0);
+  if constexpr (FINAL) {
+    const float* __restrict__ srcs[2] = {b, c};
+    stage_rows<2>(rows, srcs, t0, len, NN, C, tid);
+  } else {
+    const float* __restrict__ srcs[1] = {b};
+    stage_rows<1>(rows, srcs, t0, len, NN, C, tid);
+  }
+  float al2[NL], h[NL];
+#pragma unroll
+  for (int j = 0; j < NL; j++) {
+    al2[j] = alpha[pc * NN + n0 + j] * kLog2e;
+    h[j] = FINAL ? h_ckpt[(k * P + pc) * NN + n0 + j] : 0.0f;
+  }
+  const uint32_t ob4 = static_cast<uint32_t>(pc) * 4u;
+  const uint32_t obx = static_cast<uint32_t>(pc) * static_cast<uint32_t>(sizeof(IO));
+  float rs[D], rx[D];
+  auto ld = [&](int slot, int64_t t) {
+    rs[slot] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(sp + t * P) + ob4);
+    rx[slot] = to_f32(*reinterpret_cast<const IO*>(reinterpret_cast<const char*>(x + t * P) + obx));
+  };
+#pragma unroll
+  for (int q = 0; q < D - 1; q++)
+    if (q < len) ld(q, t0 + q);
+  __syncthreads();  // staged rows visible
+  double ss = 0.0;
+  for (int q8 = 0; q8 < len; q8 += D) {
+#pragma unroll
+    for (int r = 0; r < D; r++) {
+      const int tau = q8 + r;
+      if (tau < len) {
+        if (tau + D - 1 < len) ld((r + D - 1) % D, t0 + tau + D - 1);
+        const float ns = -rs[r];
+        const float xv = rx[r];
+        const float* rb = rows + tau * NN + n0;
+        float bt[NL];
+#pragma unroll
+        for (int j = 0; j < NL; j += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(rb + j);
+          bt[j] = v.x; bt[j + 1] = v.y; bt[j + 2] = v.z; bt[j + 3] = v.w;
+        }
+        if constexpr (FINAL) {
+          const float* rc = rows + static_cast<size_t>(C) * NN + tau * NN + n0;
+          float acc = 0.0f;
+#pragma unroll
+          for (int j = 0; j < NL; j += 4) {
+            const float4 cv = *reinterpret_cast<const float4*>(rc + j);
+            const float cq[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+              const float a = fast_exp2(ns * al2[j + jj]);
+              h[j + jj] = fmaf(a, h[j + jj], bt[j + jj] * xv);
+              acc = fmaf(cq[jj], h[j + jj], acc);
+            }
+          }
+          acc = group_sum<G, CH>(acc);
+          if (valid && grp == 0)
+            *reinterpret_cast<float*>(reinterpret_cast<char*>(y + (t0 + tau) * P) + ob4) = acc;
+        } else {
+#pragma unroll
+          for (int j = 0; j < NL; j++) {
+            const float a = fast_exp2(ns * al2[j]);
+            h[j] = fmaf(a, h[j], bt[j] * xv);
+          }
+          ss -= static_cast<double>(ns);
+        }
+      }
+    }
+  }
+  if constexpr (!FINAL) {
+    if (valid) {
+#pragma unroll
+      for (int j = 0; j < NL; j++) hloc[(k * P + p) * NN + n0 + j] = h[j];
+      if (grp == 0) ssum[k * P + p] = ss;
+    }
+  }
+}
+
 // ----------------------------------------------------------------- launchers
 
 template <typename IO, int NL, int G>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   constexpr int CH = 64 / G;
+  constexpr int NN = NL * G;
   const int64_t NB = (a.P + CH - 1) / CH;
   const int64_t K = (a.T + a.C - 1) / a.C;
-  dim3 grid(static_cast<unsigned>(K), static_cast<unsigned>(NB));
-  k_fwd_local<IO, NL, G><<<grid, 64, 0, st>>>(a.T, a.P, a.N, a.C, a.s, static_cast<const IO*>(a.x), a.b,
-                                              a.alpha, a.hloc, a.ssum);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // staged kernels: rows of a chunk (b, c) in LDS, 4 channel blocks per workgroup
+  const size_t rows_local = static_cast<size_t>(a.C) * NN * 4, rows_final = 2 * rows_local;
+  const bool staged = (NN % 4 == 0) && rows_final <= kFwdRowLds;
+  const dim3 grid(static_cast<unsigned>(K), static_cast<unsigned>(NB));
+  const dim3 grid_s(static_cast<unsigned>(K), static_cast<unsigned>((NB + kFwdWpb - 1) / kFwdWpb));
+  hipError_t e;
+  if (staged) {
+    k_fwd_staged<IO, NL, G, false><<<grid_s, 64 * kFwdWpb, rows_local, st>>>(
+        a.T, a.P, a.N, a.C, NB, a.s, static_cast<const IO*>(a.x), a.b, a.c, a.alpha, a.h_ckpt, a.y, a.hloc, a.ssum);
+  } else {
+    k_fwd_local<IO, NL, G><<<grid, 64, 0, st>>>(a.T, a.P, a.N, a.C, a.s, static_cast<const IO*>(a.x), a.b,
+                                                a.alpha, a.hloc, a.ssum);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   a.marks.rec(2, st);
   const int64_t PN = a.P * a.N;
   k_fwd_carry<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, a.alpha, a.ssum, a.hloc,
                                                                       a.h_ckpt);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   a.marks.rec(3, st);
-  k_fwd_final<IO, NL, G><<<grid, 64, 0, st>>>(a.T, a.P, a.N, a.C, a.s, static_cast<const IO*>(a.x), a.b, a.c,
-                                              a.alpha, a.h_ckpt, a.y);
+  if (staged) {
+    k_fwd_staged<IO, NL, G, true><<<grid_s, 64 * kFwdWpb, rows_final, st>>>(
+        a.T, a.P, a.N, a.C, NB, a.s, static_cast<const IO*>(a.x), a.b, a.c, a.alpha, a.h_ckpt, a.y, a.hloc, a.ssum);
+  } else {
+    k_fwd_final<IO, NL, G><<<grid, 64, 0, st>>>(a.T, a.P, a.N, a.C, a.s, static_cast<const IO*>(a.x), a.b, a.c,
+                                                a.alpha, a.h_ckpt, a.y);
+  }
   e = hipGetLastError();
   a.marks.rec(4, st);
   return e;

@@ -38,6 +38,9 @@ template <typename T> __device__ __forceinline__ float load_io(const T* p);
 template <> __device__ __forceinline__ float load_io<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float load_io<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
 
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
+
 template <typename T> __device__ __forceinline__ void store_io(T* p, float v);
 template <> __device__ __forceinline__ void store_io<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void store_io<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16(v); }

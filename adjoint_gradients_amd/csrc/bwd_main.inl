@@ -5,7 +5,8 @@
 //   phase 1  forward walk from the chunk checkpoint h_{t0-1}; the state at
 //            the start of every S-token sub-chunk goes to a per-wavefront
 //            scratch area in global memory (written and read back by the same
-//            lanes, so it mostly stays in L2 / the infinity cache);
+//            lanes).  Where k_bwd_hsub can stage the chunk's rows, it does this
+//            walk beforehand at higher occupancy and this phase is skipped;
 //   phase 2  sub-chunks right to left: recompute the S states into registers,
 //            then walk them in reverse with the adjoint recurrence and the
 //            local VJPs (equations in scan_bwd.hip).
@@ -16,8 +17,6 @@
 // register rings filled two tokens ahead.
 
 namespace {
-
-constexpr int kWpb = 4;  // wavefronts per workgroup of the main kernel
 
 struct Tok {
   float s, x, g, sm, gm;
@@ -235,7 +234,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   if constexpr (WIN) st.H = a.hwin[k * P + pc];
 
   // ---------------- phase 1: forward walk, sub-chunk start states to scratch
-  {
+  // (skipped when the separate sub-chunk pass already wrote them)
+  if (!a.hsub_ready) {
     float h[NL];
 #pragma unroll
     for (int j = 0; j < NL; j++) h[j] = a.h_ckpt[(k * P + pc) * NN + n0 + j];

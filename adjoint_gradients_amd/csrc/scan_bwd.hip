@@ -60,6 +60,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 constexpr int kSub = 8;  // tokens per recomputed sub-chunk (registers hold S x NL states)
+constexpr int kWpb = 4;  // wavefronts per workgroup of the main kernel and of the sub-chunk pass
 
 }  // namespace
 
@@ -153,6 +154,224 @@ __global__ __launch_bounds__(64) void k_bwd_local(BwdArgs a) {
   if (valid) {
 #pragma unroll
     for (int j = 0; j < NL; j++) a.umu[(k * P + p) * NN + n0 + j] = inc[j];
+  }
+}
+
+// Staged variant of k_bwd_local (N >= 4, rows of a chunk fit in LDS): a
+// 4-wavefront workgroup takes 4 channel blocks of one chunk; the chunk's c
+// rows and its window-partner rows c_{t+W} are staged once into LDS, and the
+// per-lane s, g and partner s, g come through an 8-token register ring,
+// walked right to left.
+constexpr int kBwdLocWpb = 4;
+constexpr int kBwdLocRing = 8;
+constexpr size_t kBwdLocRowLds = 32 * 1024;
+
+template <typename IO, int NL, int G, bool WIN>
+__global__ __launch_bounds__(256) void k_bwd_local_staged(BwdArgs a, int64_t NB) {
+  constexpr int CH = 64 / G;
+  constexpr int NN = NL * G;
+  constexpr int D = kBwdLocRing;
+  extern __shared__ float rows[];  // [WIN ? 2 : 1][C][NN]: c rows, then partner c rows
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+  const int grp = lane / CH, pl = lane % CH;
+  const int64_t T = a.T, P = a.P, W = a.W;
+  const int C = a.C;
+  const int64_t K = (T + C - 1) / C;
+  const int64_t k = blockIdx.x;
+  const int64_t cb = static_cast<int64_t>(blockIdx.y) * kBwdLocWpb + w;
+  const int64_t p = cb * CH + pl;
+  const bool valid = cb < NB && p < P;
+  const int64_t pc = p < P ? p : P - 1;
+  const int n0 = grp * NL;
+  const int64_t t0 = k * C;
+  const int64_t t1 = (t0 + C < T) ? t0 + C : T;
+  const int len = static_cast<int>(t1 - t0);
+  // stage rows: c[t0 .. t1) and (window) c[t0 + W .. t1 + W) clipped to T
+  {
+    const int per = len * NN / 4;
+    const float4* s4 = reinterpret_cast<const float4*>(a.c + t0 * NN);
+    float4* d4 = reinterpret_cast<float4*>(rows);
+    for (int e = tid; e < per; e += 64 * kBwdLocWpb) d4[e] = s4[e];
+    if constexpr (WIN) {
+      const int64_t m1 = (t1 + W < T) ? t1 + W : T;
+      const int plen = (t0 + W < m1) ? static_cast<int>(m1 - (t0 + W)) : 0;
+      const int pper = plen * NN / 4;
+      const float4* m4 = reinterpret_cast<const float4*>(a.c + (t0 + W) * NN);
+      float4* e4 = reinterpret_cast<float4*>(rows + static_cast<size_t>(C) * NN);
+      for (int e = tid; e < pper; e += 64 * kBwdLocWpb) e4[e] = m4[e];
+    }
+  }
+  float al2[NL], inc[NL];
+#pragma unroll
+  for (int j = 0; j < NL; j++) {
+    al2[j] = a.alpha[pc * NN + n0 + j] * kLog2e;
+    inc[j] = 0.0f;
+  }
+  double sigma = 0.0, suffix = 0.0;
+  if constexpr (WIN) {
+    // window sum of s after the chunk (see k_bwd_local); sigma starts there
+    const int64_t q = W / C, w0 = W % C;
+    const int64_t kb = (k + q + 1 < K) ? k + q + 1 : K;
+    const int64_t ka = (k + 1 < K) ? k + 1 : K;
+    double H = a.ps64[kb * P + pc] - a.ps64[ka * P + pc];
+    if (k + q + 1 < K) {
+      const int64_t h0 = (k + q + 1) * C;
+      const int64_t h1 = (h0 + w0 < T) ? h0 + w0 : T;
+      for (int64_t t = h0; t < h1; t++) H += static_cast<double>(a.s[t * P + pc]);
+    }
+    if (valid && grp == 0) a.hwin[k * P + p] = H;
+    sigma = H;
+  }
+  const uint32_t ob4 = static_cast<uint32_t>(pc) * 4u;
+  float rs[D], rg[D], rsm[D], rgm[D];
+  // ring slot r holds token t1 - 1 - (index), index = position in the reverse walk
+  auto ld = [&](int slot, int64_t i) {
+    rs[slot] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.s + i * P) + ob4);
+    rg[slot] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.g + i * P) + ob4);
+    if constexpr (WIN) {
+      const int64_t m = i + W;
+      const bool in = m < T;
+      const int64_t mm = in ? m : i;
+      const float sm = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.s + mm * P) + ob4);
+      const float gm = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.g + mm * P) + ob4);
+      rsm[slot] = in ? sm : 0.0f;
+      rgm[slot] = in ? gm : 0.0f;
+    }
+  };
+#pragma unroll
+  for (int q = 0; q < D - 1; q++)
+    if (q < len) ld(q, t1 - 1 - q);
+  __syncthreads();  // staged rows visible
+  for (int q8 = 0; q8 < len; q8 += D) {
+#pragma unroll
+    for (int r = 0; r < D; r++) {
+      const int idx = q8 + r;  // position in the reverse walk
+      if (idx < len) {
+        if (idx + D - 1 < len) ld((r + D - 1) % D, t1 - 1 - (idx + D - 1));
+        const int tau = len - 1 - idx;  // token i = t0 + tau
+        const int64_t i = t0 + tau;
+        const float sv = rs[r], gv = rg[r];
+        float ct[NL];
+        const float* rc = rows + tau * NN + n0;
+#pragma unroll
+        for (int j = 0; j < NL; j += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(rc + j);
+          ct[j] = v.x; ct[j + 1] = v.y; ct[j + 2] = v.z; ct[j + 3] = v.w;
+        }
+        float mu[NL], av[NL];
+#pragma unroll
+        for (int j = 0; j < NL; j++) {
+          av[j] = fast_exp2(-sv * al2[j]);
+          mu[j] = fmaf(gv, ct[j], inc[j]);
+        }
+        if constexpr (WIN) {
+          if (i + W < T) {
+            float cm[NL];
+            const float* rm = rows + static_cast<size_t>(C) * NN + tau * NN + n0;
+#pragma unroll
+            for (int j = 0; j < NL; j += 4) {
+              const float4 v = *reinterpret_cast<const float4*>(rm + j);
+              cm[j] = v.x; cm[j + 1] = v.y; cm[j + 2] = v.z; cm[j + 3] = v.w;
+            }
+            const float E = static_cast<float>(sigma - suffix);
+            const float gm = rgm[r];
+#pragma unroll
+            for (int j = 0; j < NL; j++) {
+              const float Dw = fast_exp2(-E * al2[j]);
+              mu[j] = fmaf(-gm * cm[j], Dw, mu[j]);
+            }
+            suffix += static_cast<double>(rsm[r]);
+          }
+          sigma += static_cast<double>(sv);
+        }
+#pragma unroll
+        for (int j = 0; j < NL; j++) inc[j] = av[j] * mu[j];
+      }
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < NL; j++) a.umu[(k * P + p) * NN + n0 + j] = inc[j];
+  }
+}
+
+// Sub-chunk start states for the main kernel (N >= 4, a chunk's b rows fit in
+// LDS): the forward walk from the chunk checkpoint, as in the main kernel's
+// first phase, with the workgroup layout of the main kernel (4 wavefronts =
+// 4 channel blocks of one chunk, the same per-wavefront scratch layout), the
+// chunk's b rows staged in LDS and s, x through an 8-token register ring.
+template <typename IO, int NL, int G>
+__global__ __launch_bounds__(256) void k_bwd_hsub(BwdArgs a, int64_t NB) {
+  constexpr int CH = 64 / G;
+  constexpr int NN = NL * G;
+  constexpr int D = kBwdLocRing;
+  constexpr int S = kSub;
+  extern __shared__ float rows[];  // [C][NN] b rows
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+  const int grp = lane / CH, pl = lane % CH;
+  const int64_t T = a.T, P = a.P;
+  const int C = a.C;
+  const int64_t k = blockIdx.x;
+  const int64_t cb = static_cast<int64_t>(blockIdx.y) * kWpb + w;
+  const bool wave_live = cb < NB;
+  const int64_t p = cb * CH + pl;
+  const int64_t pc = p < P ? p : P - 1;
+  const int n0 = grp * NL;
+  const int64_t t0 = k * C;
+  const int64_t t1 = (t0 + C < T) ? t0 + C : T;
+  const int len = static_cast<int>(t1 - t0);
+  const int nsub_max = (C + S - 1) / S;
+  float* hsg = a.hsub + ((k * NB + (wave_live ? cb : 0)) * nsub_max) * (NL * 64);
+  {
+    const int per = len * NN / 4;
+    const float4* s4 = reinterpret_cast<const float4*>(a.b + t0 * NN);
+    float4* d4 = reinterpret_cast<float4*>(rows);
+    for (int e = tid; e < per; e += 64 * kWpb) d4[e] = s4[e];
+  }
+  float al2[NL], h[NL];
+#pragma unroll
+  for (int j = 0; j < NL; j++) {
+    al2[j] = a.alpha[pc * NN + n0 + j] * kLog2e;
+    h[j] = a.h_ckpt[(k * P + pc) * NN + n0 + j];
+  }
+  const IO* xp = static_cast<const IO*>(a.x);
+  const uint32_t ob4 = static_cast<uint32_t>(pc) * 4u;
+  const uint32_t obx = static_cast<uint32_t>(pc) * static_cast<uint32_t>(sizeof(IO));
+  float rs[D], rx[D];
+  auto ld = [&](int slot, int64_t t) {
+    rs[slot] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.s + t * P) + ob4);
+    rx[slot] = to_f32(*reinterpret_cast<const IO*>(reinterpret_cast<const char*>(xp + t * P) + obx));
+  };
+#pragma unroll
+  for (int q = 0; q < D - 1; q++)
+    if (q < len) ld(q, t0 + q);
+  __syncthreads();  // staged rows visible
+  static_assert(D % S == 0 || S % D == 0, "ring and sub-chunk sizes");
+  for (int q8 = 0; q8 < len; q8 += D) {
+#pragma unroll
+    for (int r = 0; r < D; r++) {
+      const int tau = q8 + r;
+      if (tau < len) {
+        if (tau % S == 0 && wave_live) {
+#pragma unroll
+          for (int j = 0; j < NL; j++) hsg[((tau / S) * NL + j) * 64 + lane] = h[j];
+        }
+        if (tau + D - 1 < len) ld((r + D - 1) % D, t0 + tau + D - 1);
+        const float ns = -rs[r];
+        const float xv = rx[r];
+        const float* rb = rows + tau * NN + n0;
+#pragma unroll
+        for (int j = 0; j < NL; j += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(rb + j);
+          const float bq[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++)
+            h[j + jj] = fmaf(fast_exp2(ns * al2[j + jj]), h[j + jj], bq[jj] * xv);
+        }
+      }
+    }
   }
 }
 
@@ -281,8 +500,30 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     k_bwd_prefix<<<static_cast<unsigned>((a.P + 255) / 256), 256, 0, st>>>(K, a.P, a.ssum, a.ps64);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  k_bwd_local<IO, NL, G, WIN><<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(NB)), 64, 0, st>>>(a);
+  {
+    constexpr int NNc = NL * G;
+    const size_t rows_b = static_cast<size_t>(WIN ? 2 : 1) * a.C * NNc * 4;
+    if (NNc % 4 == 0 && rows_b <= kBwdLocRowLds) {
+      k_bwd_local_staged<IO, NL, G, WIN>
+          <<<dim3(static_cast<unsigned>(K), static_cast<unsigned>((NB + kBwdLocWpb - 1) / kBwdLocWpb)),
+             64 * kBwdLocWpb, rows_b, st>>>(a, NB);
+    } else {
+      k_bwd_local<IO, NL, G, WIN><<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(NB)), 64, 0, st>>>(a);
+    }
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  BwdArgs am = a;  // arguments of the main kernel
+  am.hsub_ready = 0;
+  {
+    constexpr int NNc = NL * G;
+    const size_t rows_b = static_cast<size_t>(a.C) * NNc * 4;
+    if (NNc % 4 == 0 && rows_b <= kBwdLocRowLds) {
+      k_bwd_hsub<IO, NL, G>
+          <<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(pl.NBW)), 64 * kWpb, rows_b, st>>>(a, NB);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      am.hsub_ready = 1;
+    }
+  }
   a.marks.rec(1, st);
   const int64_t PN = a.P * a.N;
   k_bwd_carry<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, a.alpha, a.ssum, a.umu,
@@ -293,7 +534,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(pl.lds_bytes));
   if (e != hipSuccess) return e;
-  kern<<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(pl.NBW)), pl.wpb * 64, pl.lds_bytes, st>>>(a, pl.NB,
+  kern<<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(pl.NBW)), pl.wpb * 64, pl.lds_bytes, st>>>(am, pl.NB,
                                                                                                     pl.NBW);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.marks.rec(3, st);

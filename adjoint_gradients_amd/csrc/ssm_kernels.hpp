@@ -52,6 +52,7 @@ struct BwdArgs {
   float* dal_part;      // [K][P][N]
   float* dbias_part;    // [K][P]
   float* hsub;          // per-wavefront sub-chunk start states (bwd_hsub_floats)
+  int hsub_ready;       // 1: a separate pass already wrote hsub (the main kernel skips its walk)
   // outputs of the scan
   void* dY;             // [T][ldy] io: columns [0,P) = dDelta, [P,P+N) = db, [P+N,P+2N) = dc
   int64_t ldy;

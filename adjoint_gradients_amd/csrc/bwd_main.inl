@@ -62,10 +62,23 @@ __device__ __forceinline__ void lds_wait() {
 // previous token's code (which would multiply the live registers).
 __device__ __forceinline__ void token_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// NL consecutive floats of a staged row; 16-byte reads when NL % 4 == 0 (the
+// row offsets are then multiples of 4 floats).
 template <int NL>
 __device__ __forceinline__ void lds_row(const float* src, float (&dst)[NL]) {
+  if constexpr (NL % 4 == 0) {
 #pragma unroll
-  for (int j = 0; j < NL; j++) dst[j] = src[j];
+    for (int q = 0; q < NL / 4; q++) {
+      const float4 v = reinterpret_cast<const float4*>(src)[q];
+      dst[4 * q] = v.x;
+      dst[4 * q + 1] = v.y;
+      dst[4 * q + 2] = v.z;
+      dst[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NL; j++) dst[j] = src[j];
+  }
 }
 
 // Per-wavefront running state of the reverse walk.
@@ -109,10 +122,10 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
 #pragma unroll
   for (int j = 0; j < NL; j++) {
     const float tt = mu[j] * hp[j] * av[j];
+    st.inc[j] = av[j] * mu[j];
     ds = fmaf(tt, st.al2[j], ds);
     st.dal[j] = fmaf(tt, tk.s, st.dal[j]);
     dxd = fmaf(mu[j], bt[j], dxd);
-    st.inc[j] = av[j] * mu[j];
   }
   if constexpr (G > 1) {
     ds = group_sum<G, CH>(ds);
@@ -124,42 +137,63 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
     if (a.dxdir) row_ptr(a.dxdir, i, a.P)[off] = dxd;
   }
   st.dbias += dD;
-  // channel sums of db = mu x and dc = g h through an LDS transpose; rows
-  // are padded to CH+1 floats so the row-wise reads spread over the banks
-  constexpr int RS = CH + 1;
+  // channel sums of db = mu x and dc = g h through an LDS transpose (placement
+  // in red_layout.hpp).  Lanes past the last channel contribute zeros; their x
+  // and g are zeroed once per token rather than per product.
+  using RL = redl::Layout<NL, G>;
+  const float xz = valid ? tk.x : 0.0f;
+  const float gz = valid ? tk.g : 0.0f;
   const int n0 = grp * NL;
 #pragma unroll
   for (int j = 0; j < NL; j++) {
-    red[(n0 + j) * RS + pl] = valid ? mu[j] * tk.x : 0.0f;
-    red[(NN + n0 + j) * RS + pl] = valid ? tk.g * hc[j] : 0.0f;
+    red[RL::at(n0 + j, pl)] = mu[j] * xz;
+    red[RL::at(NN + n0 + j, pl)] = gz * hc[j];
   }
-  lds_wait();
-  if constexpr (OUT <= 64) {
-    constexpr int LPO = 64 / OUT;  // lanes per output
-    constexpr int V = CH / LPO;    // values summed per lane
-    const int o = lane / LPO, r = lane % LPO;
-    const float* src = red + o * RS + r * V;
+  if constexpr (RL::kSwz) {
+    // A wavefront's LDS operations execute in issue order, so its reads see
+    // its own writes without a wait; the wave barrier only keeps the compiler
+    // from moving accesses across this point.
+    __builtin_amdgcn_wave_barrier();
+    const int o = lane >> 1, r = lane & 1;
     float sum = 0.0f;
 #pragma unroll
-    for (int v = 0; v < V; v++) sum += src[v];
-    if constexpr (LPO >= 2) sum = xor_sum<1>(sum);
-    if constexpr (LPO >= 4) sum = xor_sum<2>(sum);
-    if constexpr (LPO >= 8) sum = xor_sum<4>(sum);
-    if constexpr (LPO >= 16) sum = xor_sum<8>(sum);
-    if constexpr (LPO >= 32) sum = xor_sum<16>(sum);
+    for (int q = 0; q < 4; q++) {
+      const float4 v = *reinterpret_cast<const float4*>(red + RL::chunk(o, 4 * r + q));
+      sum += (v.x + v.y) + (v.z + v.w);
+    }
+    sum = xor_sum<1>(sum);
     if (r == 0) xw_tau[o] = sum;
+    __builtin_amdgcn_wave_barrier();
   } else {
-#pragma unroll
-    for (int q = 0; q < OUT / 64; q++) {
-      const int o = lane + 64 * q;
-      const float* src = red + o * RS;
+    constexpr int RS = RL::kRS;
+    lds_wait();
+    if constexpr (OUT <= 64) {
+      constexpr int LPO = 64 / OUT;  // lanes per output
+      constexpr int V = CH / LPO;    // values summed per lane
+      const int o = lane / LPO, r = lane % LPO;
+      const float* src = red + o * RS + r * V;
       float sum = 0.0f;
 #pragma unroll
-      for (int v = 0; v < CH; v++) sum += src[v];
-      xw_tau[o] = sum;
+      for (int v = 0; v < V; v++) sum += src[v];
+      if constexpr (LPO >= 2) sum = xor_sum<1>(sum);
+      if constexpr (LPO >= 4) sum = xor_sum<2>(sum);
+      if constexpr (LPO >= 8) sum = xor_sum<4>(sum);
+      if constexpr (LPO >= 16) sum = xor_sum<8>(sum);
+      if constexpr (LPO >= 32) sum = xor_sum<16>(sum);
+      if (r == 0) xw_tau[o] = sum;
+    } else {
+#pragma unroll
+      for (int q = 0; q < OUT / 64; q++) {
+        const int o = lane + 64 * q;
+        const float* src = red + o * RS;
+        float sum = 0.0f;
+#pragma unroll
+        for (int v = 0; v < CH; v++) sum += src[v];
+        xw_tau[o] = sum;
+      }
     }
+    lds_wait();
   }
-  lds_wait();
 }
 
 }  // namespace
@@ -173,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   constexpr int NQ = WIN ? 3 : 2;                    // staged rows per token: b, c (, c_{t+W})
   constexpr int STG = NQ * S * NN;                   // floats per staging buffer
   constexpr int RPT = (STG + 64 * kWpb - 1) / (64 * kWpb);  // staged floats per thread
-  extern __shared__ float lds[];
+  extern __shared__ __align__(16) float lds[];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int grp = lane / CH, pl = lane % CH;
@@ -188,8 +222,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   const uint32_t off = static_cast<uint32_t>(pc);  // lane offset within a token row
   const int n0 = grp * NL;
   const int nsub_max = (C + S - 1) / S;
-  float* red = lds + 2 * STG + w * (OUT * (CH + 1));  // [OUT][CH+1] per wavefront
-  float* xw = lds + 2 * STG + kWpb * OUT * (CH + 1);   // [kWpb][S][OUT]
+  constexpr int RED = redl::Layout<NL, G>::kFloats;  // transpose area per wavefront
+  float* red = lds + 2 * STG + w * RED;
+  float* xw = lds + 2 * STG + kWpb * RED;  // [kWpb][S][OUT]
   float* hsg = a.hsub + ((k * NB + (wave_live ? cb : 0)) * nsub_max) * (NL * 64);
   const IO* xp = static_cast<const IO*>(a.x);
   const int64_t t0 = k * C;

@@ -32,6 +32,7 @@
 // over workgroups in a separate kernel.
 #include "ssm_common.hpp"
 #include "ssm_kernels.hpp"
+#include "red_layout.hpp"
 
 namespace ssm {
 

@@ -10,11 +10,11 @@
 //   phase 2  sub-chunks right to left: recompute the S states into registers,
 //            then walk them in reverse with the adjoint recurrence and the
 //            local VJPs (equations in scan_bwd.hip).
-// Latency hiding: the per-token rows b_t, c_t and c_{t+W} (shared by all
-// channels) of the next sub-chunk are loaded into registers at the start of a
-// sub-chunk and written to a double-buffered LDS area at its end; the
-// per-lane scalars (s, x, g and the partner token's s, g) come through small
-// register rings filled two tokens ahead.
+// Latency hiding: everything a sub-chunk reads from memory is fetched into
+// registers at the start of the previous sub-chunk and written to LDS at its
+// end -- the per-token rows b_t, c_t and c_{t+W} (shared by all channels) to a
+// double-buffered area, the per-lane quantities (s, x, g and the partner
+// token's s, g) to an area of each wavefront's own.
 
 namespace {
 
@@ -28,28 +28,6 @@ struct Tok {
 template <typename T>
 __device__ __forceinline__ T* row_ptr(T* base, int64_t t, int64_t ld) {
   return base + t * ld;
-}
-
-template <typename IO, bool WIN>
-__device__ __forceinline__ Tok load_tok(const BwdArgs& a, const IO* __restrict__ xp, int64_t i, uint32_t off) {
-  Tok o;
-  const int64_t P = a.P;
-  o.s = row_ptr(a.s, i, P)[off];
-  o.x = load_io(row_ptr(xp, i, P) + off);
-  o.g = row_ptr(a.g, i, P)[off];
-  if constexpr (WIN) {
-    const int64_t m = i + a.W;
-    const bool in = m < a.T;        // uniform
-    const int64_t mm = in ? m : i;  // any valid row; the value is replaced by 0
-    const float sm = row_ptr(a.s, mm, P)[off];
-    const float gm = row_ptr(a.g, mm, P)[off];
-    o.sm = in ? sm : 0.0f;
-    o.gm = in ? gm : 0.0f;
-  } else {
-    o.sm = 0.0f;
-    o.gm = 0.0f;
-  }
-  return o;
 }
 
 // Waits for this wavefront's outstanding LDS operations only (vmcnt untouched).
@@ -143,11 +121,11 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
   using RL = redl::Layout<NL, G>;
   const float xz = valid ? tk.x : 0.0f;
   const float gz = valid ? tk.g : 0.0f;
-  const int n0 = grp * NL;
+  float* wr = red + RL::lane_base(grp, pl);
 #pragma unroll
   for (int j = 0; j < NL; j++) {
-    red[RL::at(n0 + j, pl)] = mu[j] * xz;
-    red[RL::at(NN + n0 + j, pl)] = gz * hc[j];
+    wr[RL::row_off(0, j)] = mu[j] * xz;
+    wr[RL::row_off(1, j)] = gz * hc[j];
   }
   if constexpr (RL::kSwz) {
     // A wavefront's LDS operations execute in issue order, so its reads see
@@ -155,10 +133,11 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
     // from moving accesses across this point.
     __builtin_amdgcn_wave_barrier();
     const int o = lane >> 1, r = lane & 1;
+    const float4* rd = reinterpret_cast<const float4*>(red + RL::chunk(o, 4 * r));
     float sum = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      const float4 v = *reinterpret_cast<const float4*>(red + RL::chunk(o, 4 * r + q));
+      const float4 v = rd[q];
       sum += (v.x + v.y) + (v.z + v.w);
     }
     sum = xor_sum<1>(sum);
@@ -253,7 +232,74 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
       if (e < STG) lds[buf * STG + e] = rows[r];
     }
   };
+  // Per-lane quantities of sub-chunk u (s, x, g and, with a window, s and g
+  // of the partner token t + W) -> registers -> this wavefront's own
+  // double-buffered LDS area [2][NQS][S][CH].  Lane (grp, pl) fetches tokens
+  // grp, grp + G, ... of channel pc, so each load instruction covers G token
+  // rows.  Only this wavefront reads the area, so no barrier guards it: its
+  // LDS operations execute in order.
+  constexpr int NQS = WIN ? 5 : 3;
+  constexpr int SPL = S / G;  // tokens fetched per lane
+  float* sc0 = xw + kWpb * S * OUT + w * (2 * NQS * S * CH);
+  static_assert(2 * STG + kWpb * (RED + S * OUT + 2 * NQS * S * CH) <= bwd_main_lds_floats(NL, G),
+                "LDS layout exceeds the planned size");
+  const uint32_t loff = off + static_cast<uint32_t>(grp) * static_cast<uint32_t>(P);  // P <= 2^20
+  float pv[NQS][SPL];
+  auto fetch_scal = [&](int u) {
+    const int64_t ta = t0 + static_cast<int64_t>(u) * S;
+    if (ta + S <= t1 && (!WIN || ta + S - 1 + a.W < T)) {
+      // every token inside the chunk and every partner inside the sequence
+#pragma unroll
+      for (int i = 0; i < SPL; i++) {
+        const int64_t tb = ta + G * i;  // uniform; the lane's token is tb + grp
+        pv[0][i] = row_ptr(a.s, tb, P)[loff];
+        pv[1][i] = load_io(row_ptr(xp, tb, P) + loff);
+        pv[2][i] = row_ptr(a.g, tb, P)[loff];
+        if constexpr (WIN) {
+          pv[3][i] = row_ptr(a.s, tb + a.W, P)[loff];
+          pv[4][i] = row_ptr(a.g, tb + a.W, P)[loff];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < SPL; i++) {
+        int64_t t = ta + G * i + grp;
+        if (t >= t1) t = t1 - 1;  // past the chunk end: staged, never read
+        pv[0][i] = row_ptr(a.s, t, P)[off];
+        pv[1][i] = load_io(row_ptr(xp, t, P) + off);
+        pv[2][i] = row_ptr(a.g, t, P)[off];
+        if constexpr (WIN) {
+          const int64_t m = t + a.W;
+          const bool in = m < T;
+          const int64_t mm = in ? m : t;
+          const float sm = row_ptr(a.s, mm, P)[off];
+          const float gm = row_ptr(a.g, mm, P)[off];
+          pv[3][i] = in ? sm : 0.0f;
+          pv[4][i] = in ? gm : 0.0f;
+        }
+      }
+    }
+  };
+  auto put_scal = [&](int u) {
+    float* sc = sc0 + (u & 1) * (NQS * S * CH);
+#pragma unroll
+    for (int q = 0; q < NQS; q++)
+#pragma unroll
+      for (int i = 0; i < SPL; i++) sc[(q * S + G * i + grp) * CH + pl] = pv[q][i];
+  };
+  const float* sc = sc0;  // area of the current sub-chunk
+  auto scal = [&](int q, int tau) { return sc[(q * S + tau) * CH + pl]; };
+  auto read_tok = [&](int tau) {
+    Tok o;
+    o.s = scal(0, tau);
+    o.x = scal(1, tau);
+    o.g = scal(2, tau);
+    o.sm = WIN ? scal(3, tau) : 0.0f;
+    o.gm = WIN ? scal(4, tau) : 0.0f;
+    return o;
+  };
   fetch_rows(nsub - 1);
+  fetch_scal(nsub - 1);
 
   RevState<NL> st;
 #pragma unroll
@@ -306,49 +352,46 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
     }
   }
   put_rows((nsub - 1) & 1);
+  put_scal(nsub - 1);
   __syncthreads();
 
   // ---------------- phase 2: sub-chunks right to left
-  float fs[4], fx[4];  // recompute ring (s, x)
-  Tok ring[4];         // reverse-walk ring
   float hs[NL];
-  bool pre = false;    // fs/fx slots 0,1 and hs already hold the next sub-chunk's values
+  bool pre = false;  // hs already holds the next sub-chunk's start state
   for (int u = nsub - 1; u >= 0; u--) {
     const int buf = u & 1;
     const float* sb = lds + buf * STG;  // b rows [S][NN], then c rows, then partner c rows
     const int64_t ta = t0 + static_cast<int64_t>(u) * S;
     const int len = static_cast<int>((t1 - ta < S) ? t1 - ta : S);
-    if (u > 0) fetch_rows(u - 1);
+    sc = sc0 + buf * (NQS * S * CH);
+    if (u > 0) {
+      fetch_rows(u - 1);
+      fetch_scal(u - 1);
+    }
     if (!pre) {
 #pragma unroll
       for (int j = 0; j < NL; j++) hs[j] = hsg[(u * NL + j) * 64 + lane];
     }
+    pre = false;
     float hr[S][NL];
     if (len == S) {
       // recompute the sub-chunk's states
-      if (!pre) {
-        fs[0] = row_ptr(a.s, ta, P)[off];
-        fx[0] = load_io(row_ptr(xp, ta, P) + off);
-        fs[1] = row_ptr(a.s, ta + 1, P)[off];
-        fx[1] = load_io(row_ptr(xp, ta + 1, P) + off);
-      }
       {
         float hh[NL];
 #pragma unroll
         for (int j = 0; j < NL; j++) hh[j] = hs[j];
+        float cs = scal(0, 0), cx = scal(1, 0);
 #pragma unroll
         for (int tau = 0; tau < S; tau++) {
           token_fence();
-          if (tau + 2 < S) {
-            fs[(tau + 2) & 3] = row_ptr(a.s, ta + tau + 2, P)[off];
-            fx[(tau + 2) & 3] = load_io(row_ptr(xp, ta + tau + 2, P) + off);
+          const float ns = -cs;
+          const float xv = cx;
+          if (tau + 1 < S) {
+            cs = scal(0, tau + 1);
+            cx = scal(1, tau + 1);
           }
-          if (tau == S - 2) ring[(S - 1) & 3] = load_tok<IO, WIN>(a, xp, ta + S - 1, off);
-          if (tau == S - 1) ring[(S - 2) & 3] = load_tok<IO, WIN>(a, xp, ta + S - 2, off);
           float bt[NL];
           lds_row<NL>(sb + tau * NN + n0, bt);
-          const float ns = -fs[tau & 3];
-          const float xv = fx[tau & 3];
 #pragma unroll
           for (int j = 0; j < NL; j++) {
             hh[j] = fmaf(fast_exp2(ns * st.al2[j]), hh[j], bt[j] * xv);
@@ -356,20 +399,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
           }
         }
       }
+      if (u > 0) put_scal(u - 1);
       // reverse walk
-      pre = false;
+      Tok cur = read_tok(S - 1);
 #pragma unroll
       for (int tau = S - 1; tau >= 0; tau--) {
         token_fence();
-        if (tau >= 2) ring[(tau - 2) & 3] = load_tok<IO, WIN>(a, xp, ta + tau - 2, off);
-        if (tau == 1 && u > 0) {
-          // prefetch the next (left) sub-chunk's first recompute tokens
-          const int64_t tn = ta - S;
-          fs[0] = row_ptr(a.s, tn, P)[off];
-          fx[0] = load_io(row_ptr(xp, tn, P) + off);
-          fs[1] = row_ptr(a.s, tn + 1, P)[off];
-          fx[1] = load_io(row_ptr(xp, tn + 1, P) + off);
-        }
+        Tok nxt = cur;
+        if (tau > 0) nxt = read_tok(tau - 1);
         float bt[NL], ct[NL], cm[NL];
         lds_row<NL>(sb + tau * NN + n0, bt);
         lds_row<NL>(sb + S * NN + tau * NN + n0, ct);
@@ -381,17 +418,18 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         float hp[NL];
 #pragma unroll
         for (int j = 0; j < NL; j++) hp[j] = (tau > 0) ? hr[tau > 0 ? tau - 1 : 0][j] : hs[j];
-        rev_token<IO, NL, G, WIN>(st, a, ring[tau & 3], bt, ct, cm, hp, hr[tau], ta + tau, off, valid, grp, pl, lane,
-                                  red, xw + (w * S + tau) * OUT);
+        rev_token<IO, NL, G, WIN>(st, a, cur, bt, ct, cm, hp, hr[tau], ta + tau, off, valid, grp, pl, lane, red,
+                                  xw + (w * S + tau) * OUT);
         if (tau == 0 && u > 0) {
           // start state of the next sub-chunk (hs is no longer needed here)
 #pragma unroll
           for (int j = 0; j < NL; j++) hs[j] = hsg[((u - 1) * NL + j) * 64 + lane];
           pre = true;
         }
+        cur = nxt;
       }
     } else {
-      // partial sub-chunk (end of a ragged chunk): no register rings
+      // partial sub-chunk (end of a ragged chunk)
       {
         float hh[NL];
 #pragma unroll
@@ -399,9 +437,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
 #pragma unroll
         for (int tau = 0; tau < S; tau++) {
           if (tau < len) {
-            const int64_t t = ta + tau;
-            const float ns = -row_ptr(a.s, t, P)[off];
-            const float xv = load_io(row_ptr(xp, t, P) + off);
+            const float ns = -scal(0, tau);
+            const float xv = scal(1, tau);
             float bt[NL];
             lds_row<NL>(sb + tau * NN + n0, bt);
 #pragma unroll
@@ -412,11 +449,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
           }
         }
       }
-      pre = false;
+      if (u > 0) put_scal(u - 1);
 #pragma unroll
       for (int tau = S - 1; tau >= 0; tau--) {
         if (tau < len) {
-          const Tok tk = load_tok<IO, WIN>(a, xp, ta + tau, off);
+          const Tok tk = read_tok(tau);
           float bt[NL], ct[NL], cm[NL];
           lds_row<NL>(sb + tau * NN + n0, bt);
           lds_row<NL>(sb + S * NN + tau * NN + n0, ct);

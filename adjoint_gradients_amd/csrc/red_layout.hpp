@@ -6,21 +6,31 @@
 // Logical buffer: OUT = 2 NN rows (db of state n, then dc of state n) by CH
 // columns (the wavefront's channels).  Writes: for state j of its group, lane
 // (grp, pl) stores one float at row grp NL + j (and NN + grp NL + j), column
-// pl -- one ds_write_b32 per row pair, all 64 lanes.  Reads: lane l sums row
+// pl -- one ds_write_b32 per row, all 64 lanes.  Reads: lane l sums row
 // l / LPO, columns (l % LPO) V .. + V - 1, LPO = 64 / OUT lanes per row.
 //
+// Every address is a per-lane base plus a per-instruction constant
+// (row_off(part, j) + lane_base(grp, pl) for writes, row_start(o) + 4 c for
+// reads), so the kernel keeps one address register per access kind and the
+// constants become instruction offsets.
+//
 // General shapes pad each row to CH + 1 floats (rows start on every bank).
-// For NL = 8, G = 2 (CH = 32, OUT = 32, V = 16) rows are unpadded and the
-// lane's 16 values are fetched as four 16-byte reads, so the placement must
-// keep both access kinds free of bank conflicts (64 banks of 4 bytes; a
-// 16-byte read is served 16 lanes per pass, a 4-byte write 64 lanes):
-//   * physical row pr = row ^ ((row >> 3) & 1): the two groups' rows j and
-//     8 + j get opposite parity, so one write instruction covers all 64 banks;
-//   * 4-float chunk c of a row sits in slot c ^ ((pr >> 1) & 3): the 8 rows read
-//     in one pass (4 of each parity) put their chunks on 16 distinct bank quads.
+// For NL = 8, G = 2 (CH = 32, OUT = 32, V = 16) the lane's 16 values are read
+// as four 16-byte pieces, and both access kinds are kept free of bank
+// conflicts (64 banks of 4 bytes; a 16-byte read is served 16 lanes per pass,
+// a 4-byte write 64 lanes per pass):
+//   * rows are 32 floats, row j of a group starting at kRowJ[j] floats, whose
+//     bank quads (kRowJ / 4 mod 16 = 0, 9, 1, 10, 2, 11, 3, 8) and the same
+//     plus 4 (the second half of a row) are 16 distinct quads: the 8 rows one
+//     read pass covers (one group, one part) never share a quad;
+//   * the second group's rows sit 352 floats (32 banks mod 64) after the
+//     first's, so a write instruction (rows j and 8 + j) covers all 64 banks.
 #pragma once
 
 namespace redl {
+
+// floats of the buffer for NL states per lane and G lane groups
+constexpr int floats(int NL, int G) { return (NL == 8 && G == 2) ? 4 * 352 : 2 * NL * G * (64 / G + 1); }
 
 template <int NL, int G>
 struct Layout {
@@ -28,18 +38,27 @@ struct Layout {
   static constexpr int NN = NL * G;
   static constexpr int OUT = 2 * NN;
   static constexpr bool kSwz = (NL == 8 && G == 2);
-  static constexpr int kRS = kSwz ? CH : CH + 1;  // floats per row
-  static constexpr int kFloats = OUT * kRS;
+  static constexpr int kRS = CH + 1;  // padded layout: floats per row
+  static constexpr int kGroup = 352;  // unpadded layout: floats per group block
+  static constexpr int kFloats = floats(NL, G);
+  static_assert(kFloats == (kSwz ? 4 * kGroup : OUT * kRS), "buffer size");
 
-  static constexpr int prow(int row) { return kSwz ? (row ^ ((row >> 3) & 1)) : row; }
-  static constexpr int slot(int pr, int c) { return c ^ ((pr >> 1) & 3); }
-
-  // float index of (row, col)
-  static constexpr int at(int row, int col) {
-    return kSwz ? prow(row) * kRS + 4 * slot(prow(row), col >> 2) + (col & 3) : row * kRS + col;
+  static constexpr int row_j(int j) {
+    constexpr int r[8] = {0, 36, 68, 104, 136, 172, 204, 288};
+    return r[j];
   }
-  // float index of 4-float chunk c (columns 4 c .. 4 c + 3) of a row (swizzled layout)
-  static constexpr int chunk(int row, int c) { return prow(row) * kRS + 4 * slot(prow(row), c); }
+  // constant part of a write address: state j of a group, part 0 (db) or 1 (dc)
+  static constexpr int row_off(int part, int j) { return kSwz ? part * 2 * kGroup + row_j(j) : (part * NN + j) * kRS; }
+  // per-lane part of a write address
+  static constexpr int lane_base(int grp, int pl) { return kSwz ? grp * kGroup + pl : grp * NL * kRS + pl; }
+  // start of logical row `row`
+  static constexpr int row_start(int row) {
+    return row_off(row / NN, row % NL) + lane_base((row % NN) / NL, 0);
+  }
+  // float index of (row, col)
+  static constexpr int at(int row, int col) { return row_start(row) + col; }
+  // float index of 4-float chunk c (columns 4 c .. 4 c + 3) of a row
+  static constexpr int chunk(int row, int c) { return row_start(row) + 4 * c; }
 };
 
 }  // namespace redl

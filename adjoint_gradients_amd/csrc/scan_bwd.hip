@@ -63,6 +63,16 @@ __device__ __forceinline__ void wave_lds_sync() {
 constexpr int kSub = 8;  // tokens per recomputed sub-chunk (registers hold S x NL states)
 constexpr int kWpb = 4;  // wavefronts per workgroup of the main kernel and of the sub-chunk pass
 
+// LDS floats of k_bwd_main (NL states per lane, G groups): two staging
+// buffers of 3 row kinds x kSub tokens x NN states, and per wavefront the
+// channel-sum transpose area, the token sums [kSub][2 NN] and two buffers of
+// 5 per-lane quantities [kSub][CH].  The kernel checks its own layout against
+// this at compile time.
+constexpr size_t bwd_main_lds_floats(int NL, int G) {
+  return static_cast<size_t>(2 * 3 * kSub * NL * G) +
+         static_cast<size_t>(kWpb) * (redl::floats(NL, G) + kSub * 2 * NL * G + 2 * 5 * kSub * (64 / G));
+}
+
 }  // namespace
 
 // Exclusive prefix over chunks of the per-chunk sums of s, in fp64.
@@ -466,9 +476,7 @@ bool bwd_plan(int64_t P, int64_t N, int C, BwdPlan* pl) {
   const int CH = 64 / G;
   const int S = kSub;
   const int wpb = kWpb;
-  // LDS: two staging buffers of 3 rows x S tokens x N states, the per-wave
-  // transpose area [2N][CH] and the per-wave token sums [S][2N]
-  const size_t floats = 2 * 3 * static_cast<size_t>(S) * N + static_cast<size_t>(wpb) * (2 * N * (CH + 1) + S * 2 * N);
+  const size_t floats = bwd_main_lds_floats(NL, G);
   if (floats * 4 > 160 * 1024) return false;
   (void)C;
   const int64_t NB = (P + CH - 1) / CH;

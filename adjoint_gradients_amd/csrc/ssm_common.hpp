@@ -26,13 +26,9 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// float -> bfloat16, round to nearest, ties to even (NaN kept quiet).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u) return static_cast<bf16_t>((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
-}
+// float -> bfloat16, round to nearest, ties to even (NaN kept quiet): one
+// v_cvt_pk_bf16_f32 on gfx950, in the default round-to-nearest mode.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f)); }
 
 template <typename T> __device__ __forceinline__ float load_io(const T* p);
 template <> __device__ __forceinline__ float load_io<float>(const float* p) { return *p; }

@@ -244,16 +244,21 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   static_assert(2 * STG + kWpb * (RED + S * OUT + 2 * NQS * S * CH) <= bwd_main_lds_floats(NL, G),
                 "LDS layout exceeds the planned size");
   const uint32_t loff = off + static_cast<uint32_t>(grp) * static_cast<uint32_t>(P);  // P <= 2^20
-  float pv[NQS][SPL];
+  // The loaded values are converted and masked only when they are stored, so
+  // no wait for the loads sits in the code that issues them.
+  float pv[NQS][SPL];          // pv[1] unused: x is kept raw in px
+  typename IoRaw<IO>::type px[SPL];
+  uint32_t pin = 0;            // bit i: the partner of token i lies inside the sequence
   auto fetch_scal = [&](int u) {
     const int64_t ta = t0 + static_cast<int64_t>(u) * S;
     if (ta + S <= t1 && (!WIN || ta + S - 1 + a.W < T)) {
       // every token inside the chunk and every partner inside the sequence
+      pin = ~0u;
 #pragma unroll
       for (int i = 0; i < SPL; i++) {
         const int64_t tb = ta + G * i;  // uniform; the lane's token is tb + grp
         pv[0][i] = row_ptr(a.s, tb, P)[loff];
-        pv[1][i] = load_io(row_ptr(xp, tb, P) + loff);
+        px[i] = load_raw(row_ptr(xp, tb, P) + loff);
         pv[2][i] = row_ptr(a.g, tb, P)[loff];
         if constexpr (WIN) {
           pv[3][i] = row_ptr(a.s, tb + a.W, P)[loff];
@@ -261,21 +266,21 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         }
       }
     } else {
+      pin = 0;
 #pragma unroll
       for (int i = 0; i < SPL; i++) {
         int64_t t = ta + G * i + grp;
         if (t >= t1) t = t1 - 1;  // past the chunk end: staged, never read
         pv[0][i] = row_ptr(a.s, t, P)[off];
-        pv[1][i] = load_io(row_ptr(xp, t, P) + off);
+        px[i] = load_raw(row_ptr(xp, t, P) + off);
         pv[2][i] = row_ptr(a.g, t, P)[off];
         if constexpr (WIN) {
           const int64_t m = t + a.W;
           const bool in = m < T;
           const int64_t mm = in ? m : t;
-          const float sm = row_ptr(a.s, mm, P)[off];
-          const float gm = row_ptr(a.g, mm, P)[off];
-          pv[3][i] = in ? sm : 0.0f;
-          pv[4][i] = in ? gm : 0.0f;
+          pv[3][i] = row_ptr(a.s, mm, P)[off];
+          pv[4][i] = row_ptr(a.g, mm, P)[off];
+          pin |= (in ? 1u : 0u) << i;
         }
       }
     }
@@ -283,9 +288,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   auto put_scal = [&](int u) {
     float* sc = sc0 + (u & 1) * (NQS * S * CH);
 #pragma unroll
-    for (int q = 0; q < NQS; q++)
-#pragma unroll
-      for (int i = 0; i < SPL; i++) sc[(q * S + G * i + grp) * CH + pl] = pv[q][i];
+    for (int i = 0; i < SPL; i++) {
+      float* d = sc + (G * i + grp) * CH + pl;
+      d[0] = pv[0][i];
+      d[S * CH] = raw_to_f32(px[i]);
+      d[2 * S * CH] = pv[2][i];
+      if constexpr (WIN) {
+        const bool in = (pin >> i) & 1u;
+        d[3 * S * CH] = in ? pv[3][i] : 0.0f;
+        d[4 * S * CH] = in ? pv[4][i] : 0.0f;
+      }
+    }
   };
   const float* sc = sc0;  // area of the current sub-chunk
   auto scal = [&](int q, int tau) { return sc[(q * S + tau) * CH + pl]; };
@@ -321,10 +334,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
 #pragma unroll
     for (int j = 0; j < NL; j++) h[j] = a.h_ckpt[(k * P + pc) * NN + n0 + j];
     const int64_t nwalk = static_cast<int64_t>(nsub - 1) * S;  // multiple of S (and of 4)
-    float rs[4], rx[4], rb[4][NL];
+    float rs[4], rb[4][NL];
+    typename IoRaw<IO>::type rx[4];
     auto ld = [&](int slot, int64_t t) {
       rs[slot] = row_ptr(a.s, t, P)[off];
-      rx[slot] = load_io(row_ptr(xp, t, P) + off);
+      rx[slot] = load_raw(row_ptr(xp, t, P) + off);
       load_row<NL>(row_ptr(a.b, t, NN) + n0, rb[slot]);
     };
     if (nwalk > 0) {
@@ -343,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         if (q4 + r + 3 < nwalk) ld((r + 3) & 3, t0 + q4 + r + 3);
         const float ns = -rs[r];
 #pragma unroll
-        for (int j = 0; j < NL; j++) h[j] = fmaf(fast_exp2(ns * st.al2[j]), h[j], rb[r][j] * rx[r]);
+        for (int j = 0; j < NL; j++) h[j] = fmaf(fast_exp2(ns * st.al2[j]), h[j], rb[r][j] * raw_to_f32(rx[r]));
       }
     }
     if (wave_live) {

@@ -241,13 +241,11 @@ __global__ __launch_bounds__(256) void k_bwd_local_staged(BwdArgs a, int64_t NB)
     rs[slot] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.s + i * P) + ob4);
     rg[slot] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.g + i * P) + ob4);
     if constexpr (WIN) {
+      // partner token; the walk reads these only where i + W < T
       const int64_t m = i + W;
-      const bool in = m < T;
-      const int64_t mm = in ? m : i;
-      const float sm = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.s + mm * P) + ob4);
-      const float gm = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.g + mm * P) + ob4);
-      rsm[slot] = in ? sm : 0.0f;
-      rgm[slot] = in ? gm : 0.0f;
+      const int64_t mm = m < T ? m : i;
+      rsm[slot] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.s + mm * P) + ob4);
+      rgm[slot] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.g + mm * P) + ob4);
     }
   };
 #pragma unroll
@@ -350,10 +348,11 @@ __global__ __launch_bounds__(256) void k_bwd_hsub(BwdArgs a, int64_t NB) {
   const IO* xp = static_cast<const IO*>(a.x);
   const uint32_t ob4 = static_cast<uint32_t>(pc) * 4u;
   const uint32_t obx = static_cast<uint32_t>(pc) * static_cast<uint32_t>(sizeof(IO));
-  float rs[D], rx[D];
+  float rs[D];
+  typename IoRaw<IO>::type rx[D];
   auto ld = [&](int slot, int64_t t) {
     rs[slot] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.s + t * P) + ob4);
-    rx[slot] = to_f32(*reinterpret_cast<const IO*>(reinterpret_cast<const char*>(xp + t * P) + obx));
+    rx[slot] = load_raw(reinterpret_cast<const IO*>(reinterpret_cast<const char*>(xp + t * P) + obx));
   };
 #pragma unroll
   for (int q = 0; q < D - 1; q++)
@@ -371,7 +370,7 @@ __global__ __launch_bounds__(256) void k_bwd_hsub(BwdArgs a, int64_t NB) {
         }
         if (tau + D - 1 < len) ld((r + D - 1) % D, t0 + tau + D - 1);
         const float ns = -rs[r];
-        const float xv = rx[r];
+        const float xv = raw_to_f32(rx[r]);
         const float* rb = rows + tau * NN + n0;
 #pragma unroll
         for (int j = 0; j < NL; j += 4) {

@@ -198,10 +198,11 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
   }
   const uint32_t ob4 = static_cast<uint32_t>(pc) * 4u;
   const uint32_t obx = static_cast<uint32_t>(pc) * static_cast<uint32_t>(sizeof(IO));
-  float rs[D], rx[D];
+  float rs[D];
+  typename IoRaw<IO>::type rx[D];
   auto ld = [&](int slot, int64_t t) {
     rs[slot] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(sp + t * P) + ob4);
-    rx[slot] = to_f32(*reinterpret_cast<const IO*>(reinterpret_cast<const char*>(x + t * P) + obx));
+    rx[slot] = load_raw(reinterpret_cast<const IO*>(reinterpret_cast<const char*>(x + t * P) + obx));
   };
 #pragma unroll
   for (int q = 0; q < D - 1; q++)
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
       if (tau < len) {
         if (tau + D - 1 < len) ld((r + D - 1) % D, t0 + tau + D - 1);
         const float ns = -rs[r];
-        const float xv = rx[r];
+        const float xv = raw_to_f32(rx[r]);
         const float* rb = rows + tau * NN + n0;
         float bt[NL];
 #pragma unroll

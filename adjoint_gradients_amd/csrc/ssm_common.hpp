@@ -34,6 +34,17 @@ template <typename T> __device__ __forceinline__ float load_io(const T* p);
 template <> __device__ __forceinline__ float load_io<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float load_io<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
 
+// An io element as held in a register between its load and its use: the
+// bf16 bits (zero-extended) or the float itself.  Converting at the use keeps
+// a wait for the load out of the code that issues it (a conversion right
+// after a prefetching load would wait for that load at once).
+template <typename T> struct IoRaw;
+template <> struct IoRaw<float> { typedef float type; };
+template <> struct IoRaw<bf16_t> { typedef uint32_t type; };
+template <typename T> __device__ __forceinline__ typename IoRaw<T>::type load_raw(const T* p) { return *p; }
+__device__ __forceinline__ float raw_to_f32(float v) { return v; }
+__device__ __forceinline__ float raw_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
+
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
 

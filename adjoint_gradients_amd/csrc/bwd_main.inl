@@ -10,17 +10,69 @@
 //   phase 2  sub-chunks right to left: recompute the S states into registers,
 //            then walk them in reverse with the adjoint recurrence and the
 //            local VJPs (equations in scan_bwd.hip).
-// Latency hiding: everything a sub-chunk reads from memory is fetched into
-// registers at the start of the previous sub-chunk and written to LDS at its
-// end -- the per-token rows b_t, c_t and c_{t+W} (shared by all channels) to a
-// double-buffered area, the per-lane quantities (s, x, g and the partner
-// token's s, g) to an area of each wavefront's own.
+// Latency hiding: everything a sub-chunk reads from memory is brought by LDS
+// DMA during the previous sub-chunk (issued after its recompute, waited for
+// at its end) -- the per-token rows b_t, c_t and c_{t+W} (shared by all
+// channels) into a double-buffered area, the per-lane quantities (s, x, g and
+// the partner token's s, g) into a double-buffered area of each wavefront's
+// own -- so no register holds prefetched data; only the next sub-chunk's
+// start state is loaded into registers ahead of time.
 
 namespace {
 
 struct Tok {
   float s, x, g, sm, gm;
 };
+
+typedef __attribute__((address_space(3))) char lds_byte;
+
+// LDS byte address of a pointer into the kernel's dynamic LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_byte*)(p)));
+}
+
+// LDS DMA (global_load_lds_*): lane l's element goes from global memory
+// straight to LDS byte address lds + 4 l, without a register round trip; a
+// 2-byte element is zero-extended to 4 bytes there.  dma_s takes a
+// wave-uniform base (scalar registers) plus the lane's 32-bit byte offset,
+// dma_v the lane's own 64-bit address (the LDS address is wave-uniform in
+// both).  M0 carries the LDS address; it is saved and restored.  The loads count in vmcnt like any other; their data
+// may be read once this wavefront has waited for them (and, for data read by
+// other wavefronts, after a barrier).
+// A wave-uniform value moved to scalar registers (free when it is there).
+template <typename T>
+__device__ __forceinline__ const T* sgpr_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <typename T>
+__device__ __forceinline__ void dma_s(const T* base_any, uint32_t voff, uint32_t lds_any) {
+  const T* base = sgpr_ptr(base_any);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_any);
+  uint32_t saved;
+  if constexpr (sizeof(T) == 2)
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds), "v"(voff), "s"(base) : "memory");
+  else
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds), "v"(voff), "s"(base) : "memory");
+}
+template <typename T>
+__device__ __forceinline__ void dma_v(const T* addr, uint32_t lds_any) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_any);
+  uint32_t saved;
+  if constexpr (sizeof(T) == 2)
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds), "v"(addr) : "memory");
+  else
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds), "v"(addr) : "memory");
+}
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Row-pointer addressing: `row` is uniform across the wavefront (a scalar
 // register pair), `off` the lane's channel offset -- one VGPR shared by all
@@ -86,14 +138,16 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
     mu[j] = fmaf(tk.g, ct[j], st.inc[j]);
   }
   if constexpr (WIN) {
-    // drop the token leaving the window: - g_{i+W} c_{i+W} prod_{j=i+1}^{i+W} a_j
-    const float E = static_cast<float>(st.sigma + st.H - st.suffix);
+    if (i + a.W < a.T) {  // uniform: the partner token i + W exists
+      // drop the token leaving the window: - g_{i+W} c_{i+W} prod_{j=i+1}^{i+W} a_j
+      const float E = static_cast<float>(st.sigma + st.H - st.suffix);
 #pragma unroll
-    for (int j = 0; j < NL; j++) {
-      const float D = fast_exp2(-E * st.al2[j]);
-      mu[j] = fmaf(-tk.gm * cm[j], D, mu[j]);
+      for (int j = 0; j < NL; j++) {
+        const float D = fast_exp2(-E * st.al2[j]);
+        mu[j] = fmaf(-tk.gm * cm[j], D, mu[j]);
+      }
+      st.suffix += static_cast<double>(tk.sm);
     }
-    st.suffix += static_cast<double>(tk.sm);
     st.sigma += static_cast<double>(tk.s);
   }
   float ds = 0.0f, dxd = 0.0f;
@@ -185,7 +239,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   constexpr int OUT = 2 * NN;
   constexpr int NQ = WIN ? 3 : 2;                    // staged rows per token: b, c (, c_{t+W})
   constexpr int STG = NQ * S * NN;                   // floats per staging buffer
-  constexpr int RPT = (STG + 64 * kWpb - 1) / (64 * kWpb);  // staged floats per thread
   extern __shared__ __align__(16) float lds[];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
@@ -210,109 +263,92 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   const int64_t t1 = (t0 + C < T) ? t0 + C : T;
   const int nsub = static_cast<int>((t1 - t0 + S - 1) / S);
 
-  // rows of sub-chunk u (b, c, c_{t+W}) -> registers -> LDS buffer
-  float rows[RPT];
-  auto fetch_rows = [&](int u) {
+  // Rows of sub-chunk u (b, c, c_{t+W}, shared by all channels) -> LDS
+  // buffer u & 1, by DMA spread over the workgroup's wavefronts: instruction r
+  // moves elements 64 r .. 64 r + 63 of the buffer [3][S][NN].
+  auto dma_rows = [&](int u) {
     const int64_t ta = t0 + static_cast<int64_t>(u) * S;
-#pragma unroll
-    for (int r = 0; r < RPT; r++) {
-      const int e = tid + r * 64 * kWpb;
+    const uint32_t dst = lds_addr(lds + (u & 1) * STG);
+    for (int r = w; r * 64 < STG; r += kWpb) {
+      const int e = r * 64 + lane;
       if (e < STG) {
         const int q = e / (S * NN), tau = (e / NN) % S, n = e % NN;
         int64_t t = ta + tau + (q == 2 ? a.W : 0);
         if (t >= T) t = T - 1;  // such rows only meet zero weights
-        rows[r] = (q == 0 ? a.b : a.c)[t * NN + n];
+        dma_v((q == 0 ? a.b : a.c) + t * NN + n, dst + 256u * r);
       }
     }
   };
-  auto put_rows = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < RPT; r++) {
-      const int e = tid + r * 64 * kWpb;
-      if (e < STG) lds[buf * STG + e] = rows[r];
-    }
-  };
+
   // Per-lane quantities of sub-chunk u (s, x, g and, with a window, s and g
-  // of the partner token t + W) -> registers -> this wavefront's own
-  // double-buffered LDS area [2][NQS][S][CH].  Lane (grp, pl) fetches tokens
-  // grp, grp + G, ... of channel pc, so each load instruction covers G token
-  // rows.  Only this wavefront reads the area, so no barrier guards it: its
-  // LDS operations execute in order.
+  // of the partner token t + W) -> this wavefront's own double-buffered LDS
+  // area [2][NQS][S][CH], by DMA; each quantity's block is padded by 32
+  // floats so that reads or writes of two quantities merged into one
+  // instruction (32 lanes per pass) hit disjoint banks.  Lane (grp, pl) brings
+  // tokens grp, grp + G, ... of channel pc, so each instruction covers G token
+  // rows.  x arrives raw (bf16 zero-extended to 4 bytes, or the float).  Only
+  // this wavefront reads the area.  Partner values of tokens whose partner
+  // lies past the sequence end are whatever the clamped row holds; the walk
+  // does not use them.
   constexpr int NQS = WIN ? 5 : 3;
-  constexpr int SPL = S / G;  // tokens fetched per lane
-  float* sc0 = xw + kWpb * S * OUT + w * (2 * NQS * S * CH);
-  static_assert(2 * STG + kWpb * (RED + S * OUT + 2 * NQS * S * CH) <= bwd_main_lds_floats(NL, G),
+  constexpr int SPL = S / G;       // tokens fetched per lane
+  constexpr int SQ = S * CH + 32;  // floats per quantity block
+  float* sc0 = xw + kWpb * S * OUT + w * (2 * NQS * SQ);
+  static_assert(2 * STG + kWpb * (RED + S * OUT + 2 * NQS * SQ) <= bwd_main_lds_floats(NL, G),
                 "LDS layout exceeds the planned size");
-  const uint32_t loff = off + static_cast<uint32_t>(grp) * static_cast<uint32_t>(P);  // P <= 2^20
-  // The loaded values are converted and masked only when they are stored, so
-  // no wait for the loads sits in the code that issues them.
-  float pv[NQS][SPL];          // pv[1] unused: x is kept raw in px
-  typename IoRaw<IO>::type px[SPL];
-  uint32_t pin = 0;            // bit i: the partner of token i lies inside the sequence
-  auto fetch_scal = [&](int u) {
+  const uint32_t lrow = static_cast<uint32_t>(grp) * static_cast<uint32_t>(P) + off;  // P <= 2^20
+  const uint32_t voff4 = lrow * 4u, voffx = lrow * static_cast<uint32_t>(sizeof(IO));
+  auto dma_scal = [&](int u) {
     const int64_t ta = t0 + static_cast<int64_t>(u) * S;
+    const uint32_t dst = lds_addr(sc0 + (u & 1) * (NQS * SQ));
     if (ta + S <= t1 && (!WIN || ta + S - 1 + a.W < T)) {
       // every token inside the chunk and every partner inside the sequence
-      pin = ~0u;
 #pragma unroll
       for (int i = 0; i < SPL; i++) {
-        const int64_t tb = ta + G * i;  // uniform; the lane's token is tb + grp
-        pv[0][i] = row_ptr(a.s, tb, P)[loff];
-        px[i] = load_raw(row_ptr(xp, tb, P) + loff);
-        pv[2][i] = row_ptr(a.g, tb, P)[loff];
+        const int64_t tb = ta + G * i;  // the lane's token is tb + grp
+        const uint32_t d = dst + 4u * (G * i * CH);
+        dma_s(a.s + tb * P, voff4, d);
+        dma_s(xp + tb * P, voffx, d + 4u * SQ);
+        dma_s(a.g + tb * P, voff4, d + 8u * SQ);
         if constexpr (WIN) {
-          pv[3][i] = row_ptr(a.s, tb + a.W, P)[loff];
-          pv[4][i] = row_ptr(a.g, tb + a.W, P)[loff];
+          dma_s(a.s + (tb + a.W) * P, voff4, d + 12u * SQ);
+          dma_s(a.g + (tb + a.W) * P, voff4, d + 16u * SQ);
         }
       }
     } else {
-      pin = 0;
 #pragma unroll
       for (int i = 0; i < SPL; i++) {
         int64_t t = ta + G * i + grp;
         if (t >= t1) t = t1 - 1;  // past the chunk end: staged, never read
-        pv[0][i] = row_ptr(a.s, t, P)[off];
-        px[i] = load_raw(row_ptr(xp, t, P) + off);
-        pv[2][i] = row_ptr(a.g, t, P)[off];
+        const uint32_t d = dst + 4u * (G * i * CH);
+        dma_v(a.s + t * P + pc, d);
+        dma_v(xp + t * P + pc, d + 4u * SQ);
+        dma_v(a.g + t * P + pc, d + 8u * SQ);
         if constexpr (WIN) {
           const int64_t m = t + a.W;
-          const bool in = m < T;
-          const int64_t mm = in ? m : t;
-          pv[3][i] = row_ptr(a.s, mm, P)[off];
-          pv[4][i] = row_ptr(a.g, mm, P)[off];
-          pin |= (in ? 1u : 0u) << i;
+          const int64_t mm = m < T ? m : t;
+          dma_v(a.s + mm * P + pc, d + 12u * SQ);
+          dma_v(a.g + mm * P + pc, d + 16u * SQ);
         }
       }
     }
   };
-  auto put_scal = [&](int u) {
-    float* sc = sc0 + (u & 1) * (NQS * S * CH);
-#pragma unroll
-    for (int i = 0; i < SPL; i++) {
-      float* d = sc + (G * i + grp) * CH + pl;
-      d[0] = pv[0][i];
-      d[S * CH] = raw_to_f32(px[i]);
-      d[2 * S * CH] = pv[2][i];
-      if constexpr (WIN) {
-        const bool in = (pin >> i) & 1u;
-        d[3 * S * CH] = in ? pv[3][i] : 0.0f;
-        d[4 * S * CH] = in ? pv[4][i] : 0.0f;
-      }
-    }
-  };
   const float* sc = sc0;  // area of the current sub-chunk
-  auto scal = [&](int q, int tau) { return sc[(q * S + tau) * CH + pl]; };
+  auto scal = [&](int q, int tau) { return sc[q * SQ + tau * CH + pl]; };
+  auto scal_x = [&](int tau) {
+    return raw_to_f32(__builtin_bit_cast(typename IoRaw<IO>::type, scal(1, tau)));
+  };
   auto read_tok = [&](int tau) {
     Tok o;
     o.s = scal(0, tau);
-    o.x = scal(1, tau);
+    o.x = scal_x(tau);
     o.g = scal(2, tau);
     o.sm = WIN ? scal(3, tau) : 0.0f;
     o.gm = WIN ? scal(4, tau) : 0.0f;
     return o;
   };
-  fetch_rows(nsub - 1);
-  fetch_scal(nsub - 1);
+  dma_rows(nsub - 1);
+  dma_scal(nsub - 1);
 
   RevState<NL> st;
 #pragma unroll
@@ -365,28 +401,33 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
       for (int j = 0; j < NL; j++) hsg[((nsub - 1) * NL + j) * 64 + lane] = h[j];
     }
   }
-  put_rows((nsub - 1) & 1);
-  put_scal(nsub - 1);
-  __syncthreads();
+  wait_vm_all();
+  __syncthreads();  // staged data of the first sub-chunk visible
 
   // ---------------- phase 2: sub-chunks right to left
-  float hs[NL];
-  bool pre = false;  // hs already holds the next sub-chunk's start state
+  float hs[NL], hn[NL];  // start states of the current and of the next sub-chunk
   for (int u = nsub - 1; u >= 0; u--) {
     const int buf = u & 1;
     const float* sb = lds + buf * STG;  // b rows [S][NN], then c rows, then partner c rows
     const int64_t ta = t0 + static_cast<int64_t>(u) * S;
     const int len = static_cast<int>((t1 - ta < S) ? t1 - ta : S);
-    sc = sc0 + buf * (NQS * S * CH);
-    if (u > 0) {
-      fetch_rows(u - 1);
-      fetch_scal(u - 1);
-    }
-    if (!pre) {
+    sc = sc0 + buf * (NQS * SQ);
+    if (u == nsub - 1) {
 #pragma unroll
       for (int j = 0; j < NL; j++) hs[j] = hsg[(u * NL + j) * 64 + lane];
+    } else {
+#pragma unroll
+      for (int j = 0; j < NL; j++) hs[j] = hn[j];
     }
-    pre = false;
+    // after the recompute: bring sub-chunk u - 1's data and start state
+    auto prefetch = [&]() {
+      if (u > 0) {
+        dma_rows(u - 1);
+        dma_scal(u - 1);
+#pragma unroll
+        for (int j = 0; j < NL; j++) hn[j] = hsg[((u - 1) * NL + j) * 64 + lane];
+      }
+    };
     float hr[S][NL];
     if (len == S) {
       // recompute the sub-chunk's states
@@ -394,7 +435,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         float hh[NL];
 #pragma unroll
         for (int j = 0; j < NL; j++) hh[j] = hs[j];
-        float cs = scal(0, 0), cx = scal(1, 0);
+        float cs = scal(0, 0), cx = scal_x(0);
 #pragma unroll
         for (int tau = 0; tau < S; tau++) {
           token_fence();
@@ -402,7 +443,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
           const float xv = cx;
           if (tau + 1 < S) {
             cs = scal(0, tau + 1);
-            cx = scal(1, tau + 1);
+            cx = scal_x(tau + 1);
           }
           float bt[NL];
           lds_row<NL>(sb + tau * NN + n0, bt);
@@ -413,7 +454,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
           }
         }
       }
-      if (u > 0) put_scal(u - 1);
+      prefetch();
       // reverse walk
       Tok cur = read_tok(S - 1);
 #pragma unroll
@@ -434,12 +475,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         for (int j = 0; j < NL; j++) hp[j] = (tau > 0) ? hr[tau > 0 ? tau - 1 : 0][j] : hs[j];
         rev_token<IO, NL, G, WIN>(st, a, cur, bt, ct, cm, hp, hr[tau], ta + tau, off, valid, grp, pl, lane, red,
                                   xw + (w * S + tau) * OUT);
-        if (tau == 0 && u > 0) {
-          // start state of the next sub-chunk (hs is no longer needed here)
-#pragma unroll
-          for (int j = 0; j < NL; j++) hs[j] = hsg[((u - 1) * NL + j) * 64 + lane];
-          pre = true;
-        }
         cur = nxt;
       }
     } else {
@@ -452,7 +487,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         for (int tau = 0; tau < S; tau++) {
           if (tau < len) {
             const float ns = -scal(0, tau);
-            const float xv = scal(1, tau);
+            const float xv = scal_x(tau);
             float bt[NL];
             lds_row<NL>(sb + tau * NN + n0, bt);
 #pragma unroll
@@ -463,7 +498,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
           }
         }
       }
-      if (u > 0) put_scal(u - 1);
+      prefetch();
 #pragma unroll
       for (int tau = S - 1; tau >= 0; tau--) {
         if (tau < len) {
@@ -484,7 +519,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         }
       }
     }
-    __syncthreads();
+    wait_vm_all();
+    __syncthreads();  // staged data of u - 1 visible; token sums complete
     // sum over the workgroup's wavefronts -> one partial per (token, workgroup)
     const int tot = len * OUT;
     for (int idx = tid; idx < tot; idx += 64 * kWpb) {
@@ -494,8 +530,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
       for (int ww = 0; ww < kWpb; ww++) v += xw[(ww * S + tau) * OUT + o];
       a.part[((ta + tau) * NBW + blockIdx.y) * OUT + o] = v;
     }
-    if (u > 0) put_rows((u - 1) & 1);
-    __syncthreads();  // staged rows of u-1 visible; xw free again
+    __syncthreads();  // xw free again
   }
   if (valid) {
 #pragma unroll

@@ -16,21 +16,25 @@
 //
 // General shapes pad each row to CH + 1 floats (rows start on every bank).
 // For NL = 8, G = 2 (CH = 32, OUT = 32, V = 16) the lane's 16 values are read
-// as four 16-byte pieces, and both access kinds are kept free of bank
-// conflicts (64 banks of 4 bytes; a 16-byte read is served 16 lanes per pass,
-// a 4-byte write 64 lanes per pass):
-//   * rows are 32 floats, row j of a group starting at kRowJ[j] floats, whose
-//     bank quads (kRowJ / 4 mod 16 = 0, 9, 1, 10, 2, 11, 3, 8) and the same
+// as four 16-byte pieces, and all accesses are kept free of bank conflicts
+// (64 banks of 4 bytes; a 16-byte read is served 16 lanes per pass, a 4-byte
+// write 64 lanes per pass, and a two-address ds_write2_b32 -- into which the
+// compiler merges the writes of rows 2i and 2i + 1 -- 32 lanes per pass):
+//   * rows are 32 floats, row j of a group starting at row_j(j) floats, whose
+//     bank quads (row_j / 4 mod 16 = 0, 8, 1, 9, 2, 10, 3, 11) and the same
 //     plus 4 (the second half of a row) are 16 distinct quads: the 8 rows one
 //     read pass covers (one group, one part) never share a quad;
-//   * the second group's rows sit 352 floats (32 banks mod 64) after the
-//     first's, so a write instruction (rows j and 8 + j) covers all 64 banks.
+//   * rows 2i and 2i + 1 start 32 banks apart, so a merged write of both by
+//     one group's 32 lanes covers all 64 banks;
+//   * the second group's rows sit 288 floats (32 banks mod 64) after the
+//     first's, so a single write instruction (rows j and 8 + j) covers all 64
+//     banks.
 #pragma once
 
 namespace redl {
 
 // floats of the buffer for NL states per lane and G lane groups
-constexpr int floats(int NL, int G) { return (NL == 8 && G == 2) ? 4 * 352 : 2 * NL * G * (64 / G + 1); }
+constexpr int floats(int NL, int G) { return (NL == 8 && G == 2) ? 4 * 288 : 2 * NL * G * (64 / G + 1); }
 
 template <int NL, int G>
 struct Layout {
@@ -39,12 +43,12 @@ struct Layout {
   static constexpr int OUT = 2 * NN;
   static constexpr bool kSwz = (NL == 8 && G == 2);
   static constexpr int kRS = CH + 1;  // padded layout: floats per row
-  static constexpr int kGroup = 352;  // unpadded layout: floats per group block
+  static constexpr int kGroup = 288;  // unpadded layout: floats per group block
   static constexpr int kFloats = floats(NL, G);
   static_assert(kFloats == (kSwz ? 4 * kGroup : OUT * kRS), "buffer size");
 
   static constexpr int row_j(int j) {
-    constexpr int r[8] = {0, 36, 68, 104, 136, 172, 204, 288};
+    constexpr int r[8] = {0, 32, 68, 100, 136, 168, 204, 236};
     return r[j];
   }
   // constant part of a write address: state j of a group, part 0 (db) or 1 (dc)

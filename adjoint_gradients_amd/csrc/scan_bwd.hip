@@ -66,11 +66,11 @@ constexpr int kWpb = 4;  // wavefronts per workgroup of the main kernel and of t
 // LDS floats of k_bwd_main (NL states per lane, G groups): two staging
 // buffers of 3 row kinds x kSub tokens x NN states, and per wavefront the
 // channel-sum transpose area, the token sums [kSub][2 NN] and two buffers of
-// 5 per-lane quantities [kSub][CH].  The kernel checks its own layout against
-// this at compile time.
+// 5 per-lane quantities [kSub][CH] (each padded by 32 floats).  The kernel
+// checks its own layout against this at compile time.
 constexpr size_t bwd_main_lds_floats(int NL, int G) {
   return static_cast<size_t>(2 * 3 * kSub * NL * G) +
-         static_cast<size_t>(kWpb) * (redl::floats(NL, G) + kSub * 2 * NL * G + 2 * 5 * kSub * (64 / G));
+         static_cast<size_t>(kWpb) * (redl::floats(NL, G) + kSub * 2 * NL * G + 2 * 5 * (kSub * (64 / G) + 32));
 }
 
 }  // namespace

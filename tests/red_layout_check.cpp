@@ -2,7 +2,8 @@
 // (adjoint_gradients_amd/csrc/red_layout.hpp), for every lane layout the
 // kernels instantiate: the placement is a bijection onto the buffer; every
 // lane's reads return exactly the logical row segment it sums; and, for the
-// unpadded layout, each write instruction (64 lanes, 4 bytes each) and each
+// unpadded layout, each write instruction (64 lanes, 4 bytes each), each
+// merged write of rows 2i and 2i + 1 (32 lanes, 8 bytes each) and each
 // 16-byte read pass (16 lanes) touches distinct banks (64 banks of 4 bytes).
 #include <cstdio>
 #include <set>
@@ -26,6 +27,19 @@ void check() {
       CHECK(owner[i] < 0, "NL %d G %d: (%d,%d) collides", NL, G, row, col);
       owner[i] = row * CH + col;
     }
+  // merged writes of rows 2i and 2i + 1 (ds_write2_b32): 32 lanes of one group per pass
+  if (L::kSwz)
+    for (int part = 0; part < 2; part++)
+      for (int grp = 0; grp < G; grp++)
+        for (int j = 0; j + 1 < NL; j += 2) {
+          std::set<int> banks;
+          for (int pl = 0; pl < CH; pl++) {
+            banks.insert(L::at(part * NN + grp * NL + j, pl) % 64);
+            banks.insert(L::at(part * NN + grp * NL + j + 1, pl) % 64);
+          }
+          CHECK(banks.size() == 64, "NL %d G %d: merged write part %d grp %d rows %d,%d conflict (%zu banks)", NL, G,
+                part, grp, j, j + 1, banks.size());
+        }
   // writes: instruction (part, j), lane (grp, pl)
   for (int part = 0; part < 2; part++)
     for (int j = 0; j < NL; j++) {

@@ -153,8 +153,8 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
   float ds = 0.0f, dxd = 0.0f;
 #pragma unroll
   for (int j = 0; j < NL; j++) {
-    const float tt = mu[j] * hp[j] * av[j];
     st.inc[j] = av[j] * mu[j];
+    const float tt = st.inc[j] * hp[j];  // mu_i a_i h_{i-1}
     ds = fmaf(tt, st.al2[j], ds);
     st.dal[j] = fmaf(tt, tk.s, st.dal[j]);
     dxd = fmaf(mu[j], bt[j], dxd);

@@ -32,7 +32,8 @@
 namespace gdl {
 
 constexpr int NT = 256;
-constexpr int NS = 4;                          // LDS stages
+constexpr int NS = 4;                          // LDS stages (wait_stages covers NS <= 5)
+static_assert(NS >= 3 && NS <= 5, "stage count");
 constexpr int kStageBytes = 2 * kTileBytes;    // A tile, then B tile
 constexpr size_t kLdsBytes = static_cast<size_t>(NS) * kStageBytes;
 constexpr int kLoadsPerWave = 2 * kInstrPerTile / 4;  // both operands, per stage
@@ -75,6 +76,16 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Wait until at most `n` stages' loads of this wave (n = 0 .. 3) are still
+// outstanding.
+template <int L>
+__device__ __forceinline__ void wait_stages(int64_t n) {
+  if (n >= 3) wait_vm<3 * L>();
+  else if (n == 2) wait_vm<2 * L>();
+  else if (n == 1) wait_vm<L>();
+  else wait_vm<0>();
+}
 
 template <bool KC>
 struct Operand {
@@ -184,59 +195,85 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_
   for (int p = 0; p < NS - 1; p++)
     if (p < nsteps) issue(p);
 
-  // One stage: multiply LDS stage s % NS; with REFILL, also load stage
-  // s + NS - 1 (into the stage consumed in step s - 1).  Fragments of both k
-  // sub-steps are held in two register sets.  The volatile load statements
-  // are scheduling boundaries, so the order written here is the issue order:
-  // sub-step 0's operand reads first, the eight loads spread over sub-step
-  // 0's MFMAs, sub-step 1's reads in between.
-  auto stage_step = [&](int64_t s, auto refill_tag) {
-    constexpr bool REFILL = decltype(refill_tag)::value;
+  // Operand fragments of one k sub-step: A blocks 0..3, B blocks 0..3.
+  struct Frags {
+    bf16x8_t a[4], b[4];
+  };
+  auto read_frags = [&](Frags& f, int64_t s, int q) {
     const lds_char* st = lds + (s % NS) * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < 4; i++) f.a[i] = oa.read(st, i, q);
+#pragma unroll
+    for (int j = 0; j < 4; j++) f.b[j] = ob.read(st + kTileBytes, j, q);
+  };
+
+  // Stage s: multiply sub-step 0 (read one sub-step earlier) with the reads
+  // of sub-step 1's fragments spread between the MFMAs; then -- mid-stage --
+  // wait for stage s + 1's loads and
+  // pass the barrier: every wave's loads of stage s + 1 are then in LDS and
+  // every wave has finished reading stage s - 1, whose LDS the loads of stage
+  // s + NS - 1 refill.  Sub-step 1's MFMAs follow, with those loads (REFILL)
+  // and the reads of stage s + 1's sub-step 0 fragments spread between them,
+  // where the wave has issue slots to spare.  Every MFMA's operands were read
+  // 16 MFMAs earlier.  At the mid-stage wait the loads issued after stage
+  // s + 1's are those of stages s + 2 .. s + NS - 2 that exist.
+  // Scheduling barriers keep this issue order (left alone, the scheduler
+  // sinks the fragment reads next to their MFMAs and waits on each).
+  Frags f0, f1;
+  auto stage = [&](int64_t s, auto refill_tag, auto next_tag) {
+    constexpr bool REFILL = decltype(refill_tag)::value;  // load stage s + NS - 1
+    constexpr bool NEXT = decltype(next_tag)::value;      // stage s + 1 exists
+    const lds_char* st0 = lds + (s % NS) * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.a[i], f0.b[j], acc[i][j], 0, 0, 0);
+      f1.a[i] = oa.read(st0, i, 1);
+      f1.b[i] = ob.read(st0 + kTileBytes, i, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NEXT) {
+      // stages issued after s + 1: up to s + NS - 2 (this stage's refill comes later)
+      const int64_t last = (s + NS - 2 < nsteps - 1) ? s + NS - 2 : nsteps - 1;
+      wait_stages<kLoadsPerWave>(last - (s + 1));
+      barrier();
+    }
     const int64_t kn = kbeg + (s + NS - 1) * kBK;
     const uint32_t stn = lds_base + static_cast<uint32_t>(((s + NS - 1) % NS) * kStageBytes);
-    bf16x8_t af[2][4], bfr[2][4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) af[0][i] = oa.read(st, i, 0);
-#pragma unroll
-    for (int j = 0; j < 4; j++) bfr[0][j] = ob.read(st + kTileBytes, j, 0);
+    const lds_char* st1 = lds + ((s + 1) % NS) * kStageBytes;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[0][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.a[i], f1.b[j], acc[i][j], 0, 0, 0);
         if constexpr (REFILL) {
-          if (j == 1) oa.issue_one(stn, kn, wave, i);
-          if (j == 3) ob.issue_one(stn + kTileBytes, kn, wave, i);
+          if (j == 0) oa.issue_one(stn, kn, wave, i);
+          if (j == 2) ob.issue_one(stn + kTileBytes, kn, wave, i);
         }
       }
-      af[1][i] = oa.read(st, i, 1);
-      bfr[1][i] = ob.read(st + kTileBytes, i, 1);
+      if constexpr (NEXT) {
+        f0.a[i] = oa.read(st1, i, 0);
+        f0.b[i] = ob.read(st1 + kTileBytes, i, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[1][j], acc[i][j], 0, 0, 0);
   };
 
-  // Steady state: step s needs its own loads done while the loads of the
-  // NS - 2 later stages already issued may still be in flight.
-  int64_t s = 0;
-  for (; s + NS - 1 < nsteps; s++) {
-    wait_vm<(NS - 2) * kLoadsPerWave>();
-    barrier();  // every wave's loads of step s are in LDS; step s - 1 is consumed
-    stage_step(s, std::true_type{});
-  }
-  // Drain: no more loads to issue; fewer later stages outstanding.
-  for (; s < nsteps; s++) {
-    const int64_t later = nsteps - 1 - s;
-    if (later >= 2) wait_vm<2 * kLoadsPerWave>();
-    else if (later == 1) wait_vm<kLoadsPerWave>();
-    else wait_vm<0>();
+  if (nsteps > 0) {
+    // stages 0 .. min(NS - 1, nsteps) - 1 were issued; stage 0 must be in
+    const int64_t issued = (nsteps < NS - 1) ? nsteps : NS - 1;
+    wait_stages<kLoadsPerWave>(issued - 1);
     barrier();
-    stage_step(s, std::false_type{});
+    read_frags(f0, 0, 0);
+    // Nothing pending in LGKM at the loop entry (scalar argument loads
+    // included), so the loop's waits count only its own in-order LDS reads.
+    __builtin_amdgcn_s_waitcnt(0xC07F);
   }
+  int64_t s = 0;
+  for (; s + NS - 1 < nsteps; s++) stage(s, std::true_type{}, std::true_type{});
+  for (; s + 1 < nsteps; s++) stage(s, std::false_type{}, std::true_type{});
+  if (s < nsteps) stage(s, std::false_type{}, std::false_type{});
 
   // Epilogue.  Lane l holds, in acc[i][j][r], row m0 + 128 wm + 32 i +
   // 8 (r / 4) + 4 (l / 32) + r % 4 of column n0 + 128 wn + 32 j + l % 32.  The

@@ -92,6 +92,16 @@ def test_bf16_small(orc):
     _run_case(orc, inp, 200, 256, "bf16 W=200")
 
 
+@pytest.mark.parametrize("T,P", [(64, 32), (96, 64), (160, 96), (128, 160), (32, 128)])
+def test_bf16_short_k(orc, T, P):
+    # bf16 GEMMs with 1 to 5 k-steps of 32 (projection K = P, weight gradient
+    # K = T split over blocks): pipeline fill and drain with fewer steps than
+    # LDS stages
+    c = small_case(T, P, 16, 11, io="bf16")
+    inp = make_layer(c)
+    _run_case(orc, inp, T, 32, f"bf16 short-k T={T} P={P}")
+
+
 def test_determinism_and_linearity():
     import adjoint_gradients_amd as agm  # noqa: F401
 

@@ -28,6 +28,7 @@ EXPORTED = (
     "ssm_version",
     "ssm_status_str",
     "ssm_saved_bytes",
+    "ssm_sub_state_bytes",
     "ssm_workspace_bytes",
     "ssm_forward",
     "ssm_adjoint_grad",
@@ -55,7 +56,7 @@ class Layer(ctypes.Structure):
 
 class Saved(ctypes.Structure):
     _fields_ = [("s", ctypes.c_void_p), ("b", ctypes.c_void_p), ("c", ctypes.c_void_p),
-                ("h_ckpt", ctypes.c_void_p), ("s_sum", ctypes.c_void_p)]
+                ("h_ckpt", ctypes.c_void_p), ("s_sum", ctypes.c_void_p), ("h_sub", ctypes.c_void_p)]
 
 
 class Grads(ctypes.Structure):
@@ -75,6 +76,8 @@ def _load():
     lib.ssm_status_str.restype = ctypes.c_char_p
     lib.ssm_saved_bytes.argtypes = [P(Dims)]
     lib.ssm_saved_bytes.restype = ctypes.c_size_t
+    lib.ssm_sub_state_bytes.argtypes = [P(Dims)]
+    lib.ssm_sub_state_bytes.restype = ctypes.c_size_t
     lib.ssm_workspace_bytes.argtypes = [P(Dims), ctypes.c_int64, ctypes.c_int32]
     lib.ssm_workspace_bytes.restype = ctypes.c_size_t
     lib.ssm_forward.argtypes = [P(Dims), P(Layer), ctypes.c_void_p, ctypes.c_void_p, P(Saved),
@@ -113,6 +116,10 @@ def ssm_saved_bytes(dims: Dims) -> int:
     return int(lib.ssm_saved_bytes(ctypes.byref(dims)))
 
 
+def ssm_sub_state_bytes(dims: Dims) -> int:
+    return int(lib.ssm_sub_state_bytes(ctypes.byref(dims)))
+
+
 def ssm_workspace_bytes(dims: Dims, window: int = 0, K: int = 0) -> int:
     return int(lib.ssm_workspace_bytes(ctypes.byref(dims), int(window), int(K)))
 
@@ -144,7 +151,7 @@ def layer_struct(W_delta, W_B, W_C, alpha, delta_bias=None) -> Layer:
 
 def saved_struct(saved: dict) -> Saved:
     return Saved(_ptr(saved["s"]), _ptr(saved["b"]), _ptr(saved["c"]), _ptr(saved["h_ckpt"]),
-                 _ptr(saved["s_sum"]))
+                 _ptr(saved["s_sum"]), _ptr(saved.get("h_sub")))
 
 
 def grads_struct(grads: dict) -> Grads:
@@ -219,18 +226,26 @@ def io_dtype(io: str):
     return torch.bfloat16 if io == "bf16" else torch.float32
 
 
-def alloc_saved(dims: Dims, device="cuda") -> dict:
+def alloc_saved(dims: Dims, device="cuda", sub_states=False) -> dict:
+    """Saved-state buffers; with sub_states, also the optional h_sub buffer
+    (the forward then keeps the state of every 8th token for the gradient)."""
     import torch
 
     K = (dims.T + dims.chunk - 1) // dims.chunk
     f = dict(device=device, dtype=torch.float32)
-    return {
+    out = {
         "s": torch.empty(dims.T, dims.P, **f),
         "b": torch.empty(dims.T, dims.N, **f),
         "c": torch.empty(dims.T, dims.N, **f),
         "h_ckpt": torch.empty(K, dims.P, dims.N, **f),
         "s_sum": torch.empty(K, dims.P, device=device, dtype=torch.float64),
     }
+    if sub_states:
+        nbytes = ssm_sub_state_bytes(dims)
+        if nbytes == 0:
+            raise SsmError(4, "ssm_sub_state_bytes")
+        out["h_sub"] = torch.empty(nbytes // 4, **f)
+    return out
 
 
 def alloc_workspace(nbytes: int, device="cuda"):
@@ -239,15 +254,16 @@ def alloc_workspace(nbytes: int, device="cuda"):
     return torch.empty(max(int(nbytes), 1), device=device, dtype=torch.uint8)
 
 
-def forward(dims: Dims, layer: LayerTensors, x, ws=None, saved=None, y=None, stream=None):
-    """Runs ssm_forward; returns (y, saved dict)."""
+def forward(dims: Dims, layer: LayerTensors, x, ws=None, saved=None, y=None, stream=None, sub_states=False):
+    """Runs ssm_forward; returns (y, saved dict).  sub_states: keep h_sub (when
+    saved is not given)."""
     import torch
 
     nbytes = ssm_workspace_bytes(dims, 0, 0)
     if nbytes == 0:
         raise SsmError(4, "ssm_workspace_bytes")
     ws = alloc_workspace(nbytes, x.device) if ws is None else ws
-    saved = alloc_saved(dims, x.device) if saved is None else saved
+    saved = alloc_saved(dims, x.device, sub_states) if saved is None else saved
     y = torch.empty(dims.T, dims.P, device=x.device, dtype=torch.float32) if y is None else y
     ssm_forward(dims, layer.struct(), x, y, saved_struct(saved), ws, ws.numel(), stream)
     return y, saved

@@ -73,6 +73,7 @@ ssm_status check_saved(const ssm_saved* s) {
   if (!s || !s->s || !s->b || !s->c || !s->h_ckpt || !s->s_sum) return SSM_ERR_ARG;
   if (!aligned16(s->s) || !aligned16(s->b) || !aligned16(s->c) || !aligned16(s->h_ckpt) || !aligned16(s->s_sum))
     return SSM_ERR_ARG;
+  if (s->h_sub && !aligned16(s->h_sub)) return SSM_ERR_ARG;
   return SSM_OK;
 }
 
@@ -183,6 +184,7 @@ ssm_saved carve_saved(Carver& cv, const ssm_dims* d) {
   s.c = cv.take<float>(static_cast<size_t>(T * N));
   s.h_ckpt = cv.take<float>(static_cast<size_t>(K * P * N));
   s.s_sum = cv.take<double>(static_cast<size_t>(K * P));
+  s.h_sub = nullptr;  // the stack keeps only the chunk checkpoints
   return s;
 }
 
@@ -234,6 +236,7 @@ hipError_t run_forward(const ssm_dims* d, const ssm_layer* L, const void* x, flo
   if (e != hipSuccess) return e;
   mk.rec(1, st);
   FwdArgs fa{d->T, d->P, d->N, d->chunk, sv->s, x, sv->b, sv->c, L->alpha, w.hloc, sv->s_sum, sv->h_ckpt, y};
+  fa.hsub = sv->h_sub;
   fa.marks = mk;
   return ssm::launch_forward_scan(fa, bf, st);
 }
@@ -253,7 +256,9 @@ hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, co
   a.s = sv->s; a.x = x; a.b = sv->b; a.c = sv->c; a.alpha = L->alpha; a.h_ckpt = sv->h_ckpt;
   a.ssum = sv->s_sum; a.g = g;
   a.ps64 = w.ps64; a.hwin = w.hwin; a.umu = w.umu; a.carry = w.carry; a.part = w.part;
-  a.dal_part = w.dal_part; a.dbias_part = w.dbias_part; a.hsub = w.hsub;
+  a.dal_part = w.dal_part; a.dbias_part = w.dbias_part;
+  a.hsub = sv->h_sub ? sv->h_sub : w.hsub;
+  a.hsub_given = sv->h_sub ? 1 : 0;
   a.dY = w.dY; a.ldy = M;
   a.dxdir = need_dx ? w.dxdir : nullptr;
   a.dalpha = gr->dalpha; a.dbias = gr->dbias;
@@ -283,7 +288,7 @@ hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, co
 
 extern "C" {
 
-int32_t ssm_version(void) { return 100; }
+int32_t ssm_version(void) { return 200; }
 
 const char* ssm_status_str(ssm_status s) {
   switch (s) {
@@ -301,6 +306,11 @@ size_t ssm_saved_bytes(const ssm_dims* d) {
   Carver cv(nullptr);
   carve_saved(cv, d);
   return cv.off;
+}
+
+size_t ssm_sub_state_bytes(const ssm_dims* d) {
+  if (check_dims(d) != SSM_OK) return 0;
+  return ssm::bwd_hsub_floats(d->T, d->P, d->N, d->chunk) * sizeof(float);
 }
 
 size_t ssm_workspace_bytes(const ssm_dims* d, int64_t window, int32_t K) {

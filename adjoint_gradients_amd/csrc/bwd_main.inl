@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   constexpr int RED = redl::Layout<NL, G>::kFloats;  // transpose area per wavefront
   float* red = lds + 2 * STG + w * RED;
   float* xw = lds + 2 * STG + kWpb * RED;  // [kWpb][S][OUT]
-  float* hsg = a.hsub + ((k * NB + (wave_live ? cb : 0)) * nsub_max) * (NL * 64);
+  float* hsg = a.hsub + hsub_offset(k, wave_live ? cb : 0, 0, NB, nsub_max, NL);
   const IO* xp = static_cast<const IO*>(a.x);
   const int64_t t0 = k * C;
   const int64_t t1 = (t0 + C < T) ? t0 + C : T;
@@ -412,9 +412,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
     const int64_t ta = t0 + static_cast<int64_t>(u) * S;
     const int len = static_cast<int>((t1 - ta < S) ? t1 - ta : S);
     sc = sc0 + buf * (NQS * SQ);
+    // A wavefront past the last channel block has no states of its own; it
+    // starts from zero (it must not read another wavefront's, which a
+    // different workgroup may still be writing) and contributes zeros.
     if (u == nsub - 1) {
 #pragma unroll
-      for (int j = 0; j < NL; j++) hs[j] = hsg[(u * NL + j) * 64 + lane];
+      for (int j = 0; j < NL; j++) hs[j] = wave_live ? hsg[(u * NL + j) * 64 + lane] : 0.0f;
     } else {
 #pragma unroll
       for (int j = 0; j < NL; j++) hs[j] = hn[j];
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         dma_rows(u - 1);
         dma_scal(u - 1);
 #pragma unroll
-        for (int j = 0; j < NL; j++) hn[j] = hsg[((u - 1) * NL + j) * 64 + lane];
+        for (int j = 0; j < NL; j++) hn[j] = wave_live ? hsg[((u - 1) * NL + j) * 64 + lane] : 0.0f;
       }
     };
     float hr[S][NL];

@@ -60,7 +60,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-constexpr int kSub = 8;  // tokens per recomputed sub-chunk (registers hold S x NL states)
 constexpr int kWpb = 4;  // wavefronts per workgroup of the main kernel and of the sub-chunk pass
 
 // LDS floats of k_bwd_main (NL states per lane, G groups): two staging
@@ -332,7 +331,7 @@ __global__ __launch_bounds__(256) void k_bwd_hsub(BwdArgs a, int64_t NB) {
   const int64_t t1 = (t0 + C < T) ? t0 + C : T;
   const int len = static_cast<int>(t1 - t0);
   const int nsub_max = (C + S - 1) / S;
-  float* hsg = a.hsub + ((k * NB + (wave_live ? cb : 0)) * nsub_max) * (NL * 64);
+  float* hsg = a.hsub + hsub_offset(k, wave_live ? cb : 0, 0, NB, nsub_max, NL);
   {
     const int per = len * NN / 4;
     const float4* s4 = reinterpret_cast<const float4*>(a.b + t0 * NN);
@@ -521,8 +520,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   BwdArgs am = a;  // arguments of the main kernel
-  am.hsub_ready = 0;
-  {
+  am.hsub_ready = a.hsub_given ? 1 : 0;
+  if (!a.hsub_given) {
     constexpr int NNc = NL * G;
     const size_t rows_b = static_cast<size_t>(a.C) * NNc * 4;
     if (NNc % 4 == 0 && rows_b <= kBwdLocRowLds) {

@@ -102,7 +102,8 @@ __global__ __launch_bounds__(64) void k_fwd_final(int64_t T, int64_t P, int64_t 
                                                   const float* __restrict__ sp, const IO* __restrict__ x,
                                                   const float* __restrict__ b, const float* __restrict__ c,
                                                   const float* __restrict__ alpha,
-                                                  const float* __restrict__ h_ckpt, float* __restrict__ y) {
+                                                  const float* __restrict__ h_ckpt, float* __restrict__ y,
+                                                  float* __restrict__ hsub) {
   constexpr int CH = 64 / G;
   const int lane = threadIdx.x;
   const int grp = lane / CH, pl = lane % CH;
@@ -119,7 +120,14 @@ __global__ __launch_bounds__(64) void k_fwd_final(int64_t T, int64_t P, int64_t 
   }
   const int64_t t0 = k * C;
   const int64_t t1 = (t0 + C < T) ? t0 + C : T;
+  // sub-chunk start states for the gradient, when kept
+  const int64_t NB = (P + CH - 1) / CH, nsub_max = (C + kSub - 1) / kSub;
+  float* hsg = hsub ? hsub + hsub_offset(k, blockIdx.y, 0, NB, nsub_max, NL) + lane : nullptr;
   for (int64_t t = t0; t < t1; t++) {
+    if (hsg && (t - t0) % kSub == 0) {
+#pragma unroll
+      for (int j = 0; j < NL; j++) hsg[((t - t0) / kSub * NL + j) * 64] = h[j];
+    }
     const float ns = -sp[t * P + pc];
     const float xv = load_io(x + t * P + pc);
     float bt[NL], ct[NL];
@@ -166,7 +174,8 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
                                                     const float* __restrict__ b, const float* __restrict__ c,
                                                     const float* __restrict__ alpha,
                                                     const float* __restrict__ h_ckpt, float* __restrict__ y,
-                                                    float* __restrict__ hloc, double* __restrict__ ssum) {
+                                                    float* __restrict__ hloc, double* __restrict__ ssum,
+                                                    float* __restrict__ hsub) {
   constexpr int CH = 64 / G;
   constexpr int NN = NL * G;
   constexpr int D = kFwdRing;
@@ -208,12 +217,20 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
   for (int q = 0; q < D - 1; q++)
     if (q < len) ld(q, t0 + q);
   __syncthreads();  // staged rows visible
+  // sub-chunk start states for the gradient, when kept (final pass only)
+  const int64_t nsub_max = (C + kSub - 1) / kSub;
+  float* hsg = (FINAL && hsub && cb < NB) ? hsub + hsub_offset(k, cb, 0, NB, nsub_max, NL) + lane : nullptr;
+  static_assert(D % kSub == 0, "ring length a multiple of the sub-chunk");
   double ss = 0.0;
   for (int q8 = 0; q8 < len; q8 += D) {
 #pragma unroll
     for (int r = 0; r < D; r++) {
       const int tau = q8 + r;
       if (tau < len) {
+        if (FINAL && r % kSub == 0 && hsg) {
+#pragma unroll
+          for (int j = 0; j < NL; j++) hsg[(tau / kSub * NL + j) * 64] = h[j];
+        }
         if (tau + D - 1 < len) ld((r + D - 1) % D, t0 + tau + D - 1);
         const float ns = -rs[r];
         const float xv = raw_to_f32(rx[r]);
@@ -277,7 +294,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   hipError_t e;
   if (staged) {
     k_fwd_staged<IO, NL, G, false><<<grid_s, 64 * kFwdWpb, rows_local, st>>>(
-        a.T, a.P, a.N, a.C, NB, a.s, static_cast<const IO*>(a.x), a.b, a.c, a.alpha, a.h_ckpt, a.y, a.hloc, a.ssum);
+        a.T, a.P, a.N, a.C, NB, a.s, static_cast<const IO*>(a.x), a.b, a.c, a.alpha, a.h_ckpt, a.y, a.hloc, a.ssum,
+        nullptr);
   } else {
     k_fwd_local<IO, NL, G><<<grid, 64, 0, st>>>(a.T, a.P, a.N, a.C, a.s, static_cast<const IO*>(a.x), a.b,
                                                 a.alpha, a.hloc, a.ssum);
@@ -291,10 +309,11 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   a.marks.rec(3, st);
   if (staged) {
     k_fwd_staged<IO, NL, G, true><<<grid_s, 64 * kFwdWpb, rows_final, st>>>(
-        a.T, a.P, a.N, a.C, NB, a.s, static_cast<const IO*>(a.x), a.b, a.c, a.alpha, a.h_ckpt, a.y, a.hloc, a.ssum);
+        a.T, a.P, a.N, a.C, NB, a.s, static_cast<const IO*>(a.x), a.b, a.c, a.alpha, a.h_ckpt, a.y, a.hloc, a.ssum,
+        a.hsub);
   } else {
     k_fwd_final<IO, NL, G><<<grid, 64, 0, st>>>(a.T, a.P, a.N, a.C, a.s, static_cast<const IO*>(a.x), a.b, a.c,
-                                                a.alpha, a.h_ckpt, a.y);
+                                                a.alpha, a.h_ckpt, a.y, a.hsub);
   }
   e = hipGetLastError();
   a.marks.rec(4, st);

@@ -17,6 +17,18 @@ struct Marks {
   }
 };
 
+// Sub-chunk start states of the gradient kernel: the state entering token
+// kC + kSub u of chunk k, for channel block cb (CH = 64 / G channels) and lane
+// l = grp CH + pl of the scan layout, state n = grp NL + j, stored at float
+// offset hsub_offset(k, cb, u, NB, nsub_max, NL) + j 64 + l, nsub_max =
+// ceil(C / kSub).  Written either by the final forward scan (when the caller
+// keeps them) or by a pass of the gradient.
+constexpr int kSub = 8;  // tokens per recomputed sub-chunk
+__host__ __device__ constexpr int64_t hsub_offset(int64_t k, int64_t cb, int64_t u, int64_t NB, int64_t nsub_max,
+                                                  int NL) {
+  return ((k * NB + cb) * nsub_max + u) * (static_cast<int64_t>(NL) * 64);
+}
+
 struct FwdArgs {
   int64_t T, P, N;
   int C;
@@ -29,6 +41,7 @@ struct FwdArgs {
   double* ssum;         // [K][P]   per-chunk sum of s (saved)
   float* h_ckpt;        // [K][P][N] saved
   float* y;             // [T][P]
+  float* hsub = nullptr;  // optional: sub-chunk start states (bwd_hsub_floats floats)
   Marks marks{};        // phases 2..4: after local scan, carry, final scan
 };
 
@@ -53,6 +66,7 @@ struct BwdArgs {
   float* dbias_part;    // [K][P]
   float* hsub;          // per-wavefront sub-chunk start states (bwd_hsub_floats)
   int hsub_ready;       // 1: a separate pass already wrote hsub (the main kernel skips its walk)
+  int hsub_given;       // 1: hsub was written by the forward (no pass needed)
   // outputs of the scan
   void* dY;             // [T][ldy] io: columns [0,P) = dDelta, [P,P+N) = db, [P+N,P+2N) = dc
   int64_t ldy;

@@ -202,6 +202,9 @@ def main():
     ap.add_argument("--source-hash", metavar="PHASE", default=None,
                     help="print the hash of the sources a phase's kernels are built from and exit")
     ap.add_argument("--phases", action="store_true", help="print the per-phase breakdown to stderr")
+    ap.add_argument("--no-sub-states", action="store_true",
+                    help="the forward keeps only the chunk checkpoints (the gradient rebuilds the "
+                         "sub-chunk states in a pass of its own)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB three times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -247,7 +250,7 @@ def main():
     dims = agm.make_dims(T, P, N, chunk, io)
     ws_f = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, 0, 0), dev)
     ws_b = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, window, 0), dev)
-    saved = agm.alloc_saved(dims, dev)
+    saved = agm.alloc_saved(dims, dev, sub_states=not args.no_sub_states)
     grads = agm.alloc_grads(dims, device=dev)
     y = torch.empty(T, P, device=dev, dtype=torch.float32)
     L = lay.struct()
@@ -338,7 +341,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{case.name}: one selective SSM layer, T={T}, P={P}, N={N}, io={io}, "
                                f"fp32 state, window={window}, checkpoint every {chunk} tokens",
-                   "T": T, "P": P, "N": N, "window": window, "chunk": chunk},
+                   "T": T, "P": P, "N": N, "window": window, "chunk": chunk,
+                   "sub_states_saved": not args.no_sub_states},
         "roofline": roof,
         "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
     }

@@ -97,13 +97,25 @@ typedef struct {
 
 /* State saved by ssm_forward for ssm_adjoint_grad (caller-owned buffers).
  * Instead of the whole state sequence h (T*P*N) only the checkpoints are
- * kept; the gradient call recomputes h inside each chunk. */
+ * kept; the gradient call recomputes h inside each chunk (the segment
+ * recomputation of "Training Deep Nets with Sublinear Memory Cost").
+ *
+ * h_sub is optional (NULL: not kept).  When set, ssm_forward also stores the
+ * state entering every 8th token of each chunk there, in a layout private to
+ * this library (ssm_sub_state_bytes(dims) bytes, 16-byte aligned), and
+ * ssm_adjoint_grad reads it instead of re-walking each chunk to rebuild it:
+ * more saved memory (T*P*N/8 floats, 16 GiB at T = 2^20, P = 2048, N = 16,
+ * against 0.5 GiB of chunk checkpoints) for one pass less in the gradient.
+ * h_sub must be NULL in both calls or, in the gradient call, hold what
+ * ssm_forward wrote for the same dims, x and layer.  The gradient's
+ * workspace size does not depend on it. */
 typedef struct {
   float *s;        /* [T][P]  softplus(Delta) */
   float *b;        /* [T][N] */
   float *c;        /* [T][N] */
   float *h_ckpt;   /* [ceil(T/C)][P][N]  h_{kC-1}; entry 0 is the zero state */
   double *s_sum;   /* [ceil(T/C)][P]  sum of s over each chunk, in fp64 */
+  float *h_sub;    /* optional sub-chunk states (see above), or NULL */
 } ssm_saved;
 
 /* Gradient outputs of one layer.  The three weight gradients are required;
@@ -123,9 +135,13 @@ int32_t ssm_version(void);
 /* Human-readable name of a status code (static string, never NULL). */
 const char *ssm_status_str(ssm_status status);
 
-/* Bytes of the five ssm_saved buffers together (informational; the caller
- * may allocate them separately).  0 if dims are invalid. */
+/* Bytes of the five required ssm_saved buffers together (informational; the
+ * caller may allocate them separately; h_sub not included).  0 if dims are
+ * invalid. */
 size_t ssm_saved_bytes(const ssm_dims *dims);
+
+/* Bytes of the optional ssm_saved.h_sub buffer.  0 if dims are invalid. */
+size_t ssm_sub_state_bytes(const ssm_dims *dims);
 
 /* Workspace bytes needed by ssm_forward (window = 0, K = 0), by
  * ssm_adjoint_grad (window >= 1, K = 0) or by ssm_stack_grad (K >= 1).
@@ -136,7 +152,7 @@ size_t ssm_workspace_bytes(const ssm_dims *dims, int64_t window, int32_t K);
  * Forward pass of one layer: the projections, the chunked scan of the
  * recurrence (Section 3.1) with checkpoints every C tokens, and y.
  *   x   [T][P] io (input), y [T][P] float32 (output)
- *   saved: all five buffers written.
+ *   saved: the five required buffers written, and h_sub when it is set.
  *   ws: at least ssm_workspace_bytes(dims, 0, 0) bytes (256-byte aligned).
  */
 ssm_status ssm_forward(const ssm_dims *dims, const ssm_layer *layer, const void *x, float *y,

@@ -38,8 +38,9 @@ def layer_tensors(inp, io):
                             to_dev(inp["alpha"]), to_dev(inp["delta_bias"]))
 
 
-def gpu_layer(inp, window, chunk, want_dx=True, io=None, g=None):
-    """Forward + adjoint gradient of one layer on the GPU; returns numpy float64 dict."""
+def gpu_layer(inp, window, chunk, want_dx=True, io=None, g=None, sub_states=False):
+    """Forward + adjoint gradient of one layer on the GPU; returns numpy float64 dict.
+    sub_states: the forward keeps the sub-chunk states (saved h_sub) for the gradient."""
     import torch
 
     import adjoint_gradients_amd as agm
@@ -51,13 +52,14 @@ def gpu_layer(inp, window, chunk, want_dx=True, io=None, g=None):
     lay = layer_tensors(inp, io)
     x = to_dev(inp["x"], io)
     gg = to_dev(inp["g"] if g is None else g)
-    y, saved = agm.forward(dims, lay, x)
+    y, saved = agm.forward(dims, lay, x, sub_states=sub_states)
     grads = agm.adjoint_grad(dims, lay, x, saved, gg, window, want_dx=want_dx)
     torch.cuda.synchronize()
     out = {k: v.double().cpu().numpy() for k, v in grads.items()}
     out["y"] = y.double().cpu().numpy()
     for k, v in saved.items():
-        out["saved_" + k] = v.double().cpu().numpy()
+        if k != "h_sub":  # private layout
+            out["saved_" + k] = v.double().cpu().numpy()
     return out
 
 

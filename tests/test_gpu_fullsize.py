@@ -51,7 +51,7 @@ def test_cfg2_full_oracle(orc, window, want_dx):
     case = CONFIGS[2]
     inp = make_layer(case)
     say(f"case {case.name} full: T={case.T} P={case.P} N={case.N} W={window} C={CHUNK} dx={want_dx}")
-    got = gpu_layer(inp, window, CHUNK, want_dx=want_dx)
+    got = gpu_layer(inp, window, CHUNK, want_dx=want_dx, sub_states=True)
     o = oracle_inputs(inp)
     ref = orc.layer_grad(o, window=window, want_dx=want_dx)
     keys = [k for k in GRAD_KEYS if want_dx or k[0] != "dx"]
@@ -81,7 +81,7 @@ def _device_layer(case, window, chans):
                            w(inp["delta_bias"]))
     dims = agm.make_dims(T, P, N, CHUNK, case.io)
     x, g = inp["x_dev"], inp["g_dev"]
-    y, saved = agm.forward(dims, lay, x)
+    y, saved = agm.forward(dims, lay, x, sub_states=True)  # as the benchmark runs it
     grads = agm.adjoint_grad(dims, lay, x, saved, g, window, want_dx=False)
     torch.cuda.synchronize()
     ci = torch.as_tensor(chans, device=dev, dtype=torch.long)

@@ -30,11 +30,11 @@ def orc():
     return oracle
 
 
-def _run_case(orc, inp, window, chunk, label, tol=None):
+def _run_case(orc, inp, window, chunk, label, tol=None, sub_states=False):
     say(f"case {label}: T={inp['x'].shape[0]} P={inp['x'].shape[1]} N={inp['W_B'].shape[0]} "
-        f"io={inp['io']} W={window} C={chunk}")
+        f"io={inp['io']} W={window} C={chunk} sub_states={sub_states}")
     tol = tol if tol is not None else TOL[inp["io"]]
-    got = gpu_layer(inp, window, chunk)
+    got = gpu_layer(inp, window, chunk, sub_states=sub_states)
     o = oracle_inputs(inp)
     T = inp["x"].shape[0]
     ref = orc.layer_grad(o, window=None if window >= T else window)
@@ -100,6 +100,61 @@ def test_bf16_short_k(orc, T, P):
     c = small_case(T, P, 16, 11, io="bf16")
     inp = make_layer(c)
     _run_case(orc, inp, T, 32, f"bf16 short-k T={T} P={P}")
+
+
+@pytest.mark.parametrize("label,T,P,N,io,window,chunk", [
+    ("exact", 256, 64, 16, "f32", 256, 256),
+    ("ragged C", 300, 40, 8, "f32", 300, 100),
+    ("C < sub-chunk", 300, 40, 8, "f32", 300, 3),
+    ("window", 1024, 96, 16, "f32", 255, 256),
+    ("window C not dividing", 700, 70, 16, "f32", 200, 7),
+    ("N=1", 300, 40, 1, "f32", 120, 64),
+    ("N=64", 512, 48, 64, "f32", 200, 256),
+    ("bf16", 1024, 96, 16, "bf16", 200, 256),
+])
+def test_sub_states(orc, label, T, P, N, io, window, chunk):
+    # the forward keeps the sub-chunk states and the gradient skips its own
+    # pass: same oracle tolerance, and the same result as without them
+    inp = make_layer(small_case(T, P, N, 21, io=io))
+    got, _ = _run_case(orc, inp, window, chunk, f"sub-states {label}", sub_states=True)
+    ref = gpu_layer(inp, window, chunk, sub_states=False)
+    for gk, _ in GRAD_KEYS:
+        assert rel_err(got[gk], ref[gk]) <= 1e-5, gk
+
+
+@pytest.mark.parametrize("sub_states", [False, True])
+@pytest.mark.parametrize("T,P,N,io,window,chunk", [
+    (512, 48, 64, "f32", 200, 256),    # 6 channel blocks: idle wavefronts in the last workgroup
+    (300, 40, 8, "f32", 120, 100),
+    (1024, 96, 16, "bf16", 200, 256),
+    (700, 70, 32, "f32", 700, 64),
+])
+def test_poisoned_buffers(orc, T, P, N, io, window, chunk, sub_states):
+    # workspaces and saved buffers filled with NaN bytes beforehand: a read of
+    # anything the library did not write shows up in the outputs
+    import torch
+
+    import adjoint_gradients_amd as agm
+    from gpu_util import layer_tensors, to_dev
+
+    inp = make_layer(small_case(T, P, N, 31, io=io))
+    say(f"case poisoned T={T} P={P} N={N} io={io} W={window} C={chunk} sub_states={sub_states}")
+    dims = agm.make_dims(T, P, N, chunk, io)
+    lay = layer_tensors(inp, io)
+    x = to_dev(inp["x"], io)
+    g = to_dev(inp["g"])
+    ws_f = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, 0, 0), x.device).fill_(255)
+    ws_b = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, window, 0), x.device).fill_(255)
+    saved = agm.alloc_saved(dims, x.device, sub_states=sub_states)
+    for v in saved.values():
+        v.view(torch.uint8).fill_(255)
+    y, saved = agm.forward(dims, lay, x, ws=ws_f, saved=saved)
+    grads = agm.adjoint_grad(dims, lay, x, saved, g, window, want_dx=True, ws=ws_b)
+    torch.cuda.synchronize()
+    got = {k: v.double().cpu().numpy() for k, v in grads.items()}
+    got["y"] = y.double().cpu().numpy()
+    ref = orc.layer_grad(oracle_inputs(inp), window=None if window >= T else window)
+    compare(got, ref, GRAD_KEYS, TOL[io], f"poisoned N={N} P={P} sub_states={sub_states}")
 
 
 def test_determinism_and_linearity():

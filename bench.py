@@ -38,10 +38,12 @@ FWD_PHASES = ["proj_gemm", "fwd_local", "fwd_carry", "fwd_final"]
 BWD_PHASES = ["bwd_local", "bwd_carry", "bwd_main", "bwd_reduce", "wgrad_gemm", "dx_gemm"]
 
 
-def algorithmic(name, T, P, N, C, W, s_io):
+def algorithmic(name, T, P, N, C, W, s_io, sub_states=False):
     """Per-launch algorithmic work of a phase: (bytes, flops, valu_ops).
 
-    Bytes count each compulsory HBM stream once.  valu_ops counts the VALU
+    Bytes count each compulsory HBM stream once.  With sub_states the forward
+    keeps the state entering every 8th token (T/8 x P x N fp32): the final
+    forward scan writes it and the fused gradient kernel reads it.  valu_ops counts the VALU
     issue slots of the method's own arithmetic per (t, p, n) element, a
     hardware exp2 counting 2 (it issues at half rate on gfx950):
       a_t = exp(-alpha s_t)                          mul + exp        3
@@ -64,15 +66,16 @@ def algorithmic(name, T, P, N, C, W, s_io):
         return (T * (P * s_io + 4 * P + 4 * N) + K * P * N * 12, 0, 5 * E)
     if name == "fwd_carry":
         return (K * P * N * 8 + K * P * 8, 0, 4 * K * P * N)
+    sub = (T + 7) // 8 * P * N * 4 if sub_states else 0
     if name == "fwd_final":
-        return (T * (P * s_io + 8 * P + 8 * N) + K * P * N * 4, 0, 6 * E)
+        return (T * (P * s_io + 8 * P + 8 * N) + K * P * N * 4 + sub, 0, 6 * E)
     if name == "bwd_local":
         return (T * (8 * P + 4 * N) + K * P * N * 4, 0, (10 if win else 5) * E)
     if name == "bwd_carry":
         return (K * P * N * 8 + K * P * 8, 0, 4 * K * P * N)
     if name == "bwd_main":
         # per token: x, s, g, b, c, dDelta (io) and db/dc, plus h_ckpt once per chunk
-        return (T * (P * s_io + 4 * P + 4 * P + 8 * N + P * s_io + 8 * N) + K * P * N * 4, 0,
+        return (T * (P * s_io + 4 * P + 4 * P + 8 * N + P * s_io + 8 * N) + K * P * N * 4 + sub, 0,
                 (21 if win else 16) * E)
     if name == "bwd_reduce":
         return (T * 2 * N * 4 * 2, 0, 0)
@@ -87,12 +90,12 @@ def algorithmic(name, T, P, N, C, W, s_io):
 # only used while these files are byte-identical to when it was taken.
 CSRC = os.path.join(ROOT, "adjoint_gradients_amd", "csrc")
 PHASE_SOURCES = {
-    "bwd_main": ["scan_bwd.hip", "bwd_main.inl", "ssm_common.hpp", "ssm_kernels.hpp"],
-    "bwd_local": ["scan_bwd.hip", "bwd_main.inl", "ssm_common.hpp", "ssm_kernels.hpp"],
+    "bwd_main": ["scan_bwd.hip", "bwd_main.inl", "red_layout.hpp", "ssm_common.hpp", "ssm_kernels.hpp"],
+    "bwd_local": ["scan_bwd.hip", "bwd_main.inl", "red_layout.hpp", "ssm_common.hpp", "ssm_kernels.hpp"],
     "fwd_final": ["scan_fwd.hip", "ssm_common.hpp", "ssm_kernels.hpp"],
     "fwd_local": ["scan_fwd.hip", "ssm_common.hpp", "ssm_kernels.hpp"],
-    "proj_gemm": ["gemm.hip", "gemm_bf16.inl", "ssm_kernels.hpp"],
-    "wgrad_gemm": ["gemm.hip", "gemm_bf16.inl", "ssm_kernels.hpp"],
+    "proj_gemm": ["gemm.hip", "gemm_dl.inl", "gemm_dl_index.hpp", "gemm_bf16.inl", "ssm_kernels.hpp"],
+    "wgrad_gemm": ["gemm.hip", "gemm_dl.inl", "gemm_dl_index.hpp", "gemm_bf16.inl", "ssm_kernels.hpp"],
 }
 
 
@@ -299,7 +302,7 @@ def main():
 
     rows = []
     for k, ms in phase_ms.items():
-        by, fl, ops = algorithmic(k, T, P, N, chunk, window, s_io)
+        by, fl, ops = algorithmic(k, T, P, N, chunk, window, s_io, not args.no_sub_states)
         rows.append((k, ms, by / (ms * 1e-3) / 1e9 if ms > 0 else 0.0, fl / (ms * 1e-3) / 1e12 if ms > 0 else 0.0,
                      ops / (ms * 1e-3) / 1e9 if ms > 0 else 0.0))
     if args.phases:
@@ -310,7 +313,7 @@ def main():
 
     dom = max(rows, key=lambda r: r[1])
     name, ms = dom[0], dom[1]
-    by, fl, ops = algorithmic(name, T, P, N, chunk, window, s_io)
+    by, fl, ops = algorithmic(name, T, P, N, chunk, window, s_io, not args.no_sub_states)
     if fl > 0:
         peak = MFMA_BF16_PEAK_TFS if io == "bf16" else MFMA_F32_PEAK_TFS
         ach = fl / (ms * 1e-3) / 1e12

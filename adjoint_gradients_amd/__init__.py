@@ -29,6 +29,7 @@ EXPORTED = (
     "ssm_status_str",
     "ssm_saved_bytes",
     "ssm_sub_state_bytes",
+    "ssm_grad_workspace_bytes_sub",
     "ssm_workspace_bytes",
     "ssm_forward",
     "ssm_adjoint_grad",
@@ -78,6 +79,8 @@ def _load():
     lib.ssm_saved_bytes.restype = ctypes.c_size_t
     lib.ssm_sub_state_bytes.argtypes = [P(Dims)]
     lib.ssm_sub_state_bytes.restype = ctypes.c_size_t
+    lib.ssm_grad_workspace_bytes_sub.argtypes = [P(Dims), ctypes.c_int64]
+    lib.ssm_grad_workspace_bytes_sub.restype = ctypes.c_size_t
     lib.ssm_workspace_bytes.argtypes = [P(Dims), ctypes.c_int64, ctypes.c_int32]
     lib.ssm_workspace_bytes.restype = ctypes.c_size_t
     lib.ssm_forward.argtypes = [P(Dims), P(Layer), ctypes.c_void_p, ctypes.c_void_p, P(Saved),
@@ -118,6 +121,10 @@ def ssm_saved_bytes(dims: Dims) -> int:
 
 def ssm_sub_state_bytes(dims: Dims) -> int:
     return int(lib.ssm_sub_state_bytes(ctypes.byref(dims)))
+
+
+def ssm_grad_workspace_bytes_sub(dims: Dims, window: int) -> int:
+    return int(lib.ssm_grad_workspace_bytes_sub(ctypes.byref(dims), int(window)))
 
 
 def ssm_workspace_bytes(dims: Dims, window: int = 0, K: int = 0) -> int:
@@ -287,7 +294,10 @@ def alloc_grads(dims: Dims, want_dx=False, want_dalpha=True, want_dbias=True, de
 def adjoint_grad(dims: Dims, layer: LayerTensors, x, saved: dict, g, window: int, want_dx=False, ws=None,
                  grads=None, stream=None) -> dict:
     """Runs ssm_adjoint_grad; returns the gradient dict."""
-    nbytes = ssm_workspace_bytes(dims, window, 0)
+    if saved.get("h_sub") is not None:
+        nbytes = ssm_grad_workspace_bytes_sub(dims, window)
+    else:
+        nbytes = ssm_workspace_bytes(dims, window, 0)
     if nbytes == 0:
         raise SsmError(4, "ssm_workspace_bytes")
     ws = alloc_workspace(nbytes, x.device) if ws is None else ws

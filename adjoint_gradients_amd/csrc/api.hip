@@ -153,7 +153,8 @@ struct BwdWs {
   int splits;
 };
 
-BwdWs carve_bwd(Carver& cv, const ssm_dims* d, int64_t W, bool need_dx) {
+// own_hsub: the workspace holds the sub-chunk states (the caller did not keep them)
+BwdWs carve_bwd(Carver& cv, const ssm_dims* d, int64_t W, bool need_dx, bool own_hsub = true) {
   BwdWs w;
   BwdPlan pl;
   ssm::bwd_plan(d->P, d->N, d->chunk, &pl);
@@ -170,7 +171,7 @@ BwdWs carve_bwd(Carver& cv, const ssm_dims* d, int64_t W, bool need_dx) {
   w.hwin = win ? cv.take<double>(static_cast<size_t>(K * P)) : nullptr;
   w.dal_part = cv.take<float>(static_cast<size_t>(K * P * N));
   w.dbias_part = cv.take<float>(static_cast<size_t>(K * P));
-  w.hsub = cv.take<float>(ssm::bwd_hsub_floats(T, P, N, d->chunk));
+  w.hsub = own_hsub ? cv.take<float>(ssm::bwd_hsub_floats(T, P, N, d->chunk)) : nullptr;
   w.splits = splitk_for(d);
   w.wpart = cv.take<float>(static_cast<size_t>(w.splits) * M * P);
   return w;
@@ -194,9 +195,9 @@ size_t fwd_ws_bytes(const ssm_dims* d) {
   return cv.off;
 }
 
-size_t bwd_ws_bytes(const ssm_dims* d, int64_t W, bool need_dx) {
+size_t bwd_ws_bytes(const ssm_dims* d, int64_t W, bool need_dx, bool own_hsub = true) {
   Carver cv(nullptr);
-  carve_bwd(cv, d, W, need_dx);
+  carve_bwd(cv, d, W, need_dx, own_hsub);
   return cv.off;
 }
 
@@ -313,6 +314,11 @@ size_t ssm_sub_state_bytes(const ssm_dims* d) {
   return ssm::bwd_hsub_floats(d->T, d->P, d->N, d->chunk) * sizeof(float);
 }
 
+size_t ssm_grad_workspace_bytes_sub(const ssm_dims* d, int64_t window) {
+  if (check_dims(d) != SSM_OK || window < 1) return 0;
+  return bwd_ws_bytes(d, window < d->T ? window : d->T, true, false);
+}
+
 size_t ssm_workspace_bytes(const ssm_dims* d, int64_t window, int32_t K) {
   if (check_dims(d) != SSM_OK) return 0;
   if (K < 0 || window < 0) return 0;
@@ -352,9 +358,10 @@ static ssm_status adjoint_impl(const ssm_dims* d, const ssm_layer* L, const void
   if (mk.n < 0 || (mk.n > 0 && !mk.ev)) return SSM_ERR_ARG;
   const int64_t W = window < d->T ? window : d->T;
   const bool need_dx = gr->dx != nullptr;
-  if ((s = check_ws(ws, ws_bytes, bwd_ws_bytes(d, W, need_dx))) != SSM_OK) return s;
+  const bool own_hsub = sv->h_sub == nullptr;
+  if ((s = check_ws(ws, ws_bytes, bwd_ws_bytes(d, W, need_dx, own_hsub))) != SSM_OK) return s;
   Carver cv(ws);
-  BwdWs w = carve_bwd(cv, d, W, need_dx);
+  BwdWs w = carve_bwd(cv, d, W, need_dx, own_hsub);
   hipError_t e = run_backward(d, L, x, sv, g, W, gr, nullptr, w, static_cast<hipStream_t>(stream), mk);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

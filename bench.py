@@ -193,6 +193,97 @@ def cpu_baseline(case, window, chunk, tokens):
                       f"{case.name} workload (P={case.P}, N={case.N}, window={window}); wall {wall:.2f} s"}
 
 
+def study_truncation():
+    """Truncation quality: relative gradient error of the W-token adjoint window
+    against the exact adjoint (W = T), for layers whose decay rate is set
+    exactly: W_delta = 0, so softplus(Delta) = u in every channel and the decay
+    rate of state n is u (n + 1).  The slowest state's tail beyond W weighs
+    about exp(-u W).  fp32 throughout (the kernels' own rounding is ~1e-6)."""
+    import math
+
+    import torch
+
+    import adjoint_gradients_amd as agm
+    from ssm_inputs import LayerCase, make_layer
+
+    T, P, N, C = 32768, 256, 16, 256
+    keys = ("dW_delta", "dW_B", "dW_C", "dalpha", "dbias", "dx")
+    rows = []
+    for u in (1e-4, 1e-3, 1e-2, 1e-1):
+        case = LayerCase(f"trunc_u{u:g}", T, P, N, "f32", (), bias="softplus_values", bias_u=(u,),
+                         wdelta="zero", seed=7)
+        inp = make_layer(case)
+        dev = "cuda:0"
+        t = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+        lay = agm.LayerTensors(t(inp["W_delta"]), t(inp["W_B"]), t(inp["W_C"]), t(inp["alpha"]),
+                               t(inp["delta_bias"]))
+        x, g = t(inp["x"]), t(inp["g"])
+        dims = agm.make_dims(T, P, N, C, "f32")
+        _, saved = agm.forward(dims, lay, x)
+        ref = agm.adjoint_grad(dims, lay, x, saved, g, T, want_dx=True)
+        for W in (16, 64, 256, 1024, 4096):
+            gr = agm.adjoint_grad(dims, lay, x, saved, g, W, want_dx=True)
+            err = {k: float((gr[k].double() - ref[k].double()).norm() / ref[k].double().norm()) for k in keys}
+            row = {"study": "truncation", "T": T, "P": P, "N": N, "u": u, "W": W,
+                   "tail_exp_minus_uW": math.exp(-u * W), "rel_err": err}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+    print(f"{'u':>8s} {'W':>6s} {'exp(-uW)':>10s} " + " ".join(f"{k:>9s}" for k in keys), file=sys.stderr)
+    for r in rows:
+        print(f"{r['u']:8.0e} {r['W']:6d} {r['tail_exp_minus_uW']:10.2e} "
+              + " ".join(f"{r['rel_err'][k]:9.2e}" for k in keys), file=sys.stderr)
+
+
+def study_memory():
+    """Device memory of one layer's forward + gradient at the 128K and 1M-token
+    workloads: the buffers the caller allocates (the library allocates
+    nothing), measured as torch's peak of allocated bytes, beside two
+    references -- the per-token storage of the reviewed paper's memory
+    analysis ({A_t, C_t, h_t, y_t} for every token) applied to this layer in
+    fp16, T (2 P N + N + P) x 2 bytes, and a store-everything backpropagation
+    through time that keeps at least every h_t, T P N x 4 bytes."""
+    import torch
+
+    import adjoint_gradients_amd as agm
+    from ssm_inputs import CONFIGS, make_layer_device
+
+    gib = float(1 << 30)
+    for cfg_idx, window in ((2, 1024), (3, 4096)):
+        case = CONFIGS[cfg_idx]
+        T, P, N, io = case.T, case.P, case.N, case.io
+        dims = agm.make_dims(T, P, N, 256, io)
+        for sub in (False, True):
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats()
+            inp = make_layer_device(case, "cuda:0")
+            dt = agm.io_dtype(io)
+            dv = lambda a, d=torch.float32: torch.from_numpy(a).to("cuda:0").to(d)  # noqa: E731
+            lay = agm.LayerTensors(dv(inp["W_delta"], dt), dv(inp["W_B"], dt), dv(inp["W_C"], dt),
+                                   dv(inp["alpha"]), dv(inp["delta_bias"]))
+            x, g = inp["x_dev"], inp["g_dev"]
+            base = torch.cuda.memory_allocated()
+            y, saved = agm.forward(dims, lay, x, sub_states=sub)
+            grads = agm.adjoint_grad(dims, lay, x, saved, g, window)
+            torch.cuda.synchronize()
+            peak = torch.cuda.max_memory_allocated()
+            row = {
+                "study": "memory", "workload": case.name, "T": T, "P": P, "N": N, "window": window,
+                "sub_states_saved": sub,
+                "inputs_gib": round(base / gib, 3),
+                "saved_gib": round((agm.ssm_saved_bytes(dims) + (agm.ssm_sub_state_bytes(dims) if sub else 0))
+                                   / gib, 3),
+                "workspace_fwd_gib": round(agm.ssm_workspace_bytes(dims, 0, 0) / gib, 3),
+                "workspace_grad_gib": round((agm.ssm_grad_workspace_bytes_sub(dims, window) if sub
+                                             else agm.ssm_workspace_bytes(dims, window, 0)) / gib, 3),
+                "peak_allocated_gib": round(peak / gib, 3),
+                "paper_sec45_per_token_fp16_gib": round(T * (2 * P * N + N + P) * 2 / gib, 3),
+                "bptt_all_h_fp32_gib": round(T * P * N * 4 / gib, 3),
+            }
+            print(json.dumps(row), flush=True)
+            del y, saved, grads, inp, x, g, lay
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +299,8 @@ def main():
     ap.add_argument("--no-sub-states", action="store_true",
                     help="the forward keeps only the chunk checkpoints (the gradient rebuilds the "
                          "sub-chunk states in a pass of its own)")
+    ap.add_argument("--study", choices=("truncation", "memory"), default=None,
+                    help="run a measurement study instead of the benchmark (JSON lines on stdout)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB three times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -222,6 +315,12 @@ def main():
 
     import torch
 
+    if args.study == "truncation":
+        study_truncation()
+        return
+    if args.study == "memory":
+        study_memory()
+        return
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20) // 4
         src = torch.ones(n, device="cuda:0", dtype=torch.float32)
@@ -252,8 +351,9 @@ def main():
     x, g = inp["x_dev"], inp["g_dev"]
     dims = agm.make_dims(T, P, N, chunk, io)
     ws_f = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, 0, 0), dev)
-    ws_b = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, window, 0), dev)
     saved = agm.alloc_saved(dims, dev, sub_states=not args.no_sub_states)
+    ws_b = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, window, 0) if args.no_sub_states
+                               else agm.ssm_grad_workspace_bytes_sub(dims, window), dev)
     grads = agm.alloc_grads(dims, device=dev)
     y = torch.empty(T, P, device=dev, dtype=torch.float32)
     L = lay.struct()

@@ -105,10 +105,10 @@ typedef struct {
  * this library (ssm_sub_state_bytes(dims) bytes, 16-byte aligned), and
  * ssm_adjoint_grad reads it instead of re-walking each chunk to rebuild it:
  * more saved memory (T*P*N/8 floats, 16 GiB at T = 2^20, P = 2048, N = 16,
- * against 0.5 GiB of chunk checkpoints) for one pass less in the gradient.
+ * against 0.5 GiB of chunk checkpoints) for one pass less in the gradient,
+ * whose workspace then shrinks by as much (ssm_grad_workspace_bytes_sub).
  * h_sub must be NULL in both calls or, in the gradient call, hold what
- * ssm_forward wrote for the same dims, x and layer.  The gradient's
- * workspace size does not depend on it. */
+ * ssm_forward wrote for the same dims, x and layer. */
 typedef struct {
   float *s;        /* [T][P]  softplus(Delta) */
   float *b;        /* [T][N] */
@@ -148,6 +148,11 @@ size_t ssm_sub_state_bytes(const ssm_dims *dims);
  * 0 if the arguments are invalid or unsupported. */
 size_t ssm_workspace_bytes(const ssm_dims *dims, int64_t window, int32_t K);
 
+/* Workspace bytes of ssm_adjoint_grad (window >= 1) when saved->h_sub is set:
+ * smaller than ssm_workspace_bytes(dims, window, 0) by the region that would
+ * otherwise hold the sub-chunk states.  0 if the arguments are invalid. */
+size_t ssm_grad_workspace_bytes_sub(const ssm_dims *dims, int64_t window);
+
 /*
  * Forward pass of one layer: the projections, the chunked scan of the
  * recurrence (Section 3.1) with checkpoints every C tokens, and y.
@@ -165,7 +170,8 @@ ssm_status ssm_forward(const ssm_dims *dims, const ssm_layer *layer, const void 
  * ssm_forward for the same x and layer.
  *   g [T][P] float32 cotangent of y; window >= 1 (>= T means exact).
  *   grads: outputs (see ssm_grads).
- *   ws: at least ssm_workspace_bytes(dims, window, 0) bytes.
+ *   ws: at least ssm_workspace_bytes(dims, window, 0) bytes, or, when
+ *       saved->h_sub is set, ssm_grad_workspace_bytes_sub(dims, window).
  */
 ssm_status ssm_adjoint_grad(const ssm_dims *dims, const ssm_layer *layer, const void *x,
                             const ssm_saved *saved, const float *g, int64_t window,

@@ -144,7 +144,8 @@ def test_poisoned_buffers(orc, T, P, N, io, window, chunk, sub_states):
     x = to_dev(inp["x"], io)
     g = to_dev(inp["g"])
     ws_f = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, 0, 0), x.device).fill_(255)
-    ws_b = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, window, 0), x.device).fill_(255)
+    nb = agm.ssm_grad_workspace_bytes_sub(dims, window) if sub_states else agm.ssm_workspace_bytes(dims, window, 0)
+    ws_b = agm.alloc_workspace(nb, x.device).fill_(255)
     saved = agm.alloc_saved(dims, x.device, sub_states=sub_states)
     for v in saved.values():
         v.view(torch.uint8).fill_(255)

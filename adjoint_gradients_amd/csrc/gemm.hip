@@ -113,6 +113,26 @@ struct EpiAdd {
     if (e.add1) r += e.add1[idx];
     e.out[idx] = r;
   }
+  // NV outputs at element offsets off[]: every addend is loaded before any
+  // result is stored.  out may be add1 (an in-place update), so the compiler
+  // cannot move a later element's loads above an earlier element's store by
+  // itself; element by element, each would wait a full memory round trip.
+  template <int NV>
+  __device__ __forceinline__ void at_batch(const Prep& q, const int64_t (&off)[NV], const float (&v)[NV]) const {
+    // same rounding as at(): (v + add0) + add1
+    float r[NV];
+#pragma unroll
+    for (int k = 0; k < NV; k++) r[k] = v[k] + e.add0[off[k] + q.col];
+    if (e.add1) {
+      float a1[NV];
+#pragma unroll
+      for (int k = 0; k < NV; k++) a1[k] = e.add1[off[k] + q.col];
+#pragma unroll
+      for (int k = 0; k < NV; k++) r[k] += a1[k];
+    }
+#pragma unroll
+    for (int k = 0; k < NV; k++) e.out[off[k] + q.col] = r[k];
+  }
 };
 
 // Stage a BR x BK tile of operand X (rows r0.., k0..) into LDS as [BR][BK+PAD].

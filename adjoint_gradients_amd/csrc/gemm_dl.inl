@@ -147,6 +147,14 @@ struct Operand {
   }
 };
 
+// Epilogues whose outputs read memory provide at_batch (loads before stores).
+template <class E, class = void>
+constexpr bool kHasBatchImpl = false;
+template <class E>
+constexpr bool kHasBatchImpl<E, decltype(&E::template at_batch<16>, void())> = true;
+template <class E>
+constexpr bool kHasBatch = kHasBatchImpl<E>;
+
 template <class Epi, bool a_kc, bool b_kc>
 __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_t K, const bf16_t* __restrict__ A,
                                                    int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
@@ -291,12 +299,28 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_
     if (full_rows) {
 #pragma unroll
       for (int i = 0; i < 4; i++, oi += 32 * ld) {
-        int64_t orr = oi;
+        if constexpr (kHasBatch<Epi>) {
+          int64_t offs[16];
+          float vals[16];
+          int64_t orr = oi;
 #pragma unroll
-        for (int rr = 0; rr < 4; rr++, orr += 8 * ld) {
-          int64_t o = orr;
+          for (int rr = 0; rr < 4; rr++, orr += 8 * ld) {
+            int64_t o = orr;
 #pragma unroll
-          for (int r3 = 0; r3 < 4; r3++, o += ld) epi.at(q, o, acc[i][j][rr * 4 + r3]);
+            for (int r3 = 0; r3 < 4; r3++, o += ld) {
+              offs[rr * 4 + r3] = o;
+              vals[rr * 4 + r3] = acc[i][j][rr * 4 + r3];
+            }
+          }
+          epi.at_batch(q, offs, vals);
+        } else {
+          int64_t orr = oi;
+#pragma unroll
+          for (int rr = 0; rr < 4; rr++, orr += 8 * ld) {
+            int64_t o = orr;
+#pragma unroll
+            for (int r3 = 0; r3 < 4; r3++, o += ld) epi.at(q, o, acc[i][j][rr * 4 + r3]);
+          }
         }
       }
     } else {

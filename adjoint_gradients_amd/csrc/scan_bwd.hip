@@ -175,6 +175,9 @@ __global__ __launch_bounds__(64) void k_bwd_local(BwdArgs a) {
 constexpr int kBwdLocWpb = 4;
 constexpr int kBwdLocRing = 8;
 constexpr size_t kBwdLocRowLds = 32 * 1024;
+// The sub-chunk pass stages only b rows; up to 64 KB of them (C = 256 at
+// N = 64) still leaves room for two workgroups per CU.
+constexpr size_t kHsubRowLds = 64 * 1024;
 
 template <typename IO, int NL, int G, bool WIN>
 __global__ __launch_bounds__(256) void k_bwd_local_staged(BwdArgs a, int64_t NB) {
@@ -524,7 +527,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   if (!a.hsub_given) {
     constexpr int NNc = NL * G;
     const size_t rows_b = static_cast<size_t>(a.C) * NNc * 4;
-    if (NNc % 4 == 0 && rows_b <= kBwdLocRowLds) {
+    if (NNc % 4 == 0 && rows_b <= kHsubRowLds) {
+      auto hk = k_bwd_hsub<IO, NL, G>;
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(hk), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(rows_b));
+      if (e != hipSuccess) return e;
       k_bwd_hsub<IO, NL, G>
           <<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(pl.NBW)), 64 * kWpb, rows_b, st>>>(a, NB);
       if ((e = hipGetLastError()) != hipSuccess) return e;

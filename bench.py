@@ -26,6 +26,7 @@ WORKLOADS = {
     "cfg2w1k": (2, 1024, 256),
     "cfg1": (1, 2048, 256),
     "cfg1exact": (1, 16384, 256),
+    "cfg4": (4, 4096, 256),  # the 4-layer residual stack (ssm_stack_grad), timed whole
 }
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -284,6 +285,66 @@ def study_memory():
             del y, saved, grads, inp, x, g, lay
 
 
+def bench_stack(args, cfg_idx, window, chunk):
+    """One step of the K-layer residual stack: ssm_stack_grad (K forwards, then
+    the K gradients in reverse with the cotangent passed down), timed whole
+    with events on the library's stream.  Inputs as in the stack tests."""
+    import numpy as np
+    import torch
+
+    import adjoint_gradients_amd as agm
+    from ssm_inputs import CONFIGS, _alpha, _weights
+
+    case = CONFIGS[cfg_idx]
+    T, P, N, K = case.T, case.P, case.N, case.K
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    rng = np.random.Generator(np.random.PCG64(case.seed))
+    lays = []
+    for _ in range(K):
+        wts = _weights(rng, case)
+        lays.append(agm.LayerTensors(*(torch.from_numpy(wts[k]).to(dev).to(torch.bfloat16)
+                                       for k in ("W_delta", "W_B", "W_C")),
+                                     torch.from_numpy(_alpha(case)).to(dev), torch.zeros(P, device=dev)))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1_000_003 * (case.seed + 1))
+    x0 = (torch.randn(T, P, generator=gen, device=dev) * case.x_scale).to(torch.bfloat16)
+    g = torch.randn(T, P, generator=gen, device=dev)
+    dims = agm.make_dims(T, P, N, chunk, "bf16")
+    ws = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, window, K), dev)
+    grads = [agm.alloc_grads(dims, device=dev) for _ in range(K)]
+    dx0 = torch.empty(T, P, device=dev, dtype=torch.float32)
+    xK = torch.empty(T, P, device=dev, dtype=torch.float32)
+    L = [lay.struct() for lay in lays]
+    G = [agm.grads_struct(gr) for gr in grads]
+
+    def step():
+        agm.ssm_stack_grad(K, dims, L, x0, g, window, G, dx0, xK, ws, ws.numel())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    line = {
+        "metric": "SSM adjoint-gradient tokens/s through a K-layer residual stack (fwd+adjoint+VJP)",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{case.name}: {K}-layer residual stack, T={T}, P={P}, N={N}, io=bf16, "
+                               f"fp32 state and residual, window={window}, checkpoint every {chunk} tokens",
+                   "T": T, "P": P, "N": N, "K": K, "window": window, "chunk": chunk},
+        "roofline": None,
+        "note": "stack call timed whole (no per-kernel events); the single-layer workloads carry the roofline",
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,6 +396,9 @@ def main():
     from ssm_inputs import CONFIGS, make_layer_device
 
     cfg_idx, window, chunk = WORKLOADS[args.workload]
+    if CONFIGS[cfg_idx].K > 1:
+        bench_stack(args, cfg_idx, window, chunk)
+        return
     case = CONFIGS[cfg_idx]
     dev = "cuda:0"
     torch.cuda.set_device(0)

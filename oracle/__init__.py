@@ -19,7 +19,9 @@ module builds it with gcc, loads it with ctypes and composes the steps:
   stack        residual layers r^{k+1} = r^k + y^k(cast(r^k)), loss on r^K,
                each layer driven by the total cotangent of its output
                (Proposition 3, "Core claim"; the cotangent reading is recorded
-               in the design notes)
+               in the design notes); optionally the layer input is the
+               normalised stream cast(RMSNorm_gamma(r^k)) (the review's
+               Algorithm 1 normalised input; the norm is a reading)
 """
 from __future__ import annotations
 
@@ -71,6 +73,10 @@ def _load():
     lib.orc_input_grad.restype = None
     lib.orc_cast_input.argtypes = [_i64, _d, ctypes.c_int, _d]
     lib.orc_cast_input.restype = None
+    lib.orc_rmsnorm.argtypes = [_i64, _i64, _d, _d, ctypes.c_double, _d, _d]
+    lib.orc_rmsnorm.restype = None
+    lib.orc_rmsnorm_vjp.argtypes = [_i64, _i64, _d, _d, ctypes.c_double, _d, _d, _d]
+    lib.orc_rmsnorm_vjp.restype = None
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -265,18 +271,45 @@ def cast_input(r: np.ndarray, io: str) -> np.ndarray:
     return out
 
 
+NORM_EPS = 1e-5  # epsilon of the RMS normalisation (part of its definition)
+
+
+def rmsnorm(r: np.ndarray, gamma: np.ndarray, eps: float = NORM_EPS):
+    """RMS normalisation of every row: (gamma * r / sqrt(mean(r^2) + eps), 1/rms)."""
+    r = _f64(r)
+    T, P = r.shape
+    out = np.empty_like(r)
+    rinv = np.empty(T, dtype=np.float64)
+    g = _f64(gamma)
+    _load().orc_rmsnorm(T, P, _pd(r), _pd(g), float(eps), _pd(out), _pd(rinv))
+    return out, rinv
+
+
+def rmsnorm_vjp(r: np.ndarray, gamma: np.ndarray, dout: np.ndarray, eps: float = NORM_EPS):
+    """(dr, dgamma): the vector-Jacobian product of rmsnorm for cotangent dout."""
+    r, g, d = _f64(r), _f64(gamma), _f64(dout)
+    T, P = r.shape
+    dr = np.empty_like(r)
+    dg = np.empty(P, dtype=np.float64)
+    _load().orc_rmsnorm_vjp(T, P, _pd(r), _pd(g), float(eps), _pd(d), _pd(dr), _pd(dg))
+    return dr, dg
+
+
 def stack_forward(st: dict) -> dict:
-    """Residual stack: r^0 = x^0, x^k = cast(r^k), r^{k+1} = r^k + y^k."""
+    """Residual stack: r^0 = x^0, x^k = cast(r^k) -- or cast(rmsnorm(r^k)) when
+    the layer has a "norm_scale" -- and r^{k+1} = r^k + y^k."""
     r = _f64(st["x"])
-    xs, ys = [], []
+    xs, ys, rs = [], [], []
     for lay in st["layers"]:
-        xk = cast_input(r, st["io"])
+        rs.append(r)
+        src = rmsnorm(r, lay["norm_scale"])[0] if lay.get("norm_scale") is not None else r
+        xk = cast_input(src, st["io"])
         inp = dict(lay, x=xk, g=st["g"])
         yk = forward(inp, x=xk)["y"]
         xs.append(xk)
         ys.append(yk)
         r = r + yk
-    return {"x_layers": xs, "y_layers": ys, "r_final": r}
+    return {"x_layers": xs, "y_layers": ys, "r_layers": rs, "r_final": r}
 
 
 def stack_grad(st: dict, window: int | None = None) -> dict:
@@ -284,7 +317,8 @@ def stack_grad(st: dict, window: int | None = None) -> dict:
 
     Backward: delta = g; for k = K-1..0 run the layer gradient with cotangent
     delta on y^k (the layer's parameters see the total derivative of the loss
-    with respect to their output), then delta += dx^k (the cast is treated as
+    with respect to their output), then delta += dx^k, or the normalisation's
+    VJP of dx^k when the layer normalises its input (the cast is treated as
     the identity).  Returns per-layer gradient dicts, dx0 and the forward.
     """
     fw = stack_forward(st)
@@ -296,7 +330,12 @@ def stack_grad(st: dict, window: int | None = None) -> dict:
         inp = dict(lay, x=fw["x_layers"][k], g=delta)
         gk = layer_grad(inp, window=window, x=fw["x_layers"][k], g=delta, want_dx=True)
         grads[k] = gk
-        delta = delta + gk["dx"]
+        if lay.get("norm_scale") is not None:
+            dr, dg = rmsnorm_vjp(fw["r_layers"][k], lay["norm_scale"], gk["dx"])
+            gk["dnorm_scale"] = dg
+            delta = delta + dr
+        else:
+            delta = delta + gk["dx"]
     return {"layers": grads, "dx0": delta, "forward": fw}
 
 

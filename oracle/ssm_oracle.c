@@ -344,3 +344,48 @@ void orc_cast_input(int64_t n, const double *r, int to_bf16, double *out) {
         out[e] = (double)f;
     }
 }
+
+/*
+ * Normalised layer input of the residual stack.  The pages name a normalised
+ * input (x-hat, y-hat^{k-1} in the review's Algorithm 1) without defining the
+ * norm; the reading taken is RMS normalisation with a per-channel scale:
+ *   rinv_t = 1 / sqrt(mean_p r[t][p]^2 + eps),  out[t][p] = gamma[p] r[t][p] rinv_t.
+ * Plain loops over rows in double precision.
+ */
+void orc_rmsnorm(int64_t T, int64_t P, const double *r, const double *gamma, double eps, double *out,
+                 double *rinv) {
+    for (int64_t t = 0; t < T; t++) {
+        const double *row = r + t * P;
+        double ss = 0.0;
+        for (int64_t p = 0; p < P; p++) ss += row[p] * row[p];
+        const double ri = 1.0 / sqrt(ss / (double)P + eps);
+        rinv[t] = ri;
+        for (int64_t p = 0; p < P; p++) out[t * P + p] = gamma[p] * row[p] * ri;
+    }
+}
+
+/*
+ * Vector-Jacobian product of orc_rmsnorm for the cotangent dout of its
+ * output: with xh = r rinv and u = gamma * dout,
+ *   dr[t][p] = rinv_t (u[p] - xh[p] mean_q(u[q] xh[q])),   dgamma[p] = sum_t dout[t][p] xh[t][p].
+ * (The derivative of rinv_t with respect to r[t][p] is -rinv_t^3 r[t][p] / P.)
+ */
+void orc_rmsnorm_vjp(int64_t T, int64_t P, const double *r, const double *gamma, double eps,
+                     const double *dout, double *dr, double *dgamma) {
+    for (int64_t p = 0; p < P; p++) dgamma[p] = 0.0;
+    for (int64_t t = 0; t < T; t++) {
+        const double *row = r + t * P;
+        const double *d = dout + t * P;
+        double ss = 0.0;
+        for (int64_t p = 0; p < P; p++) ss += row[p] * row[p];
+        const double ri = 1.0 / sqrt(ss / (double)P + eps);
+        double dot = 0.0;
+        for (int64_t p = 0; p < P; p++) dot += gamma[p] * d[p] * row[p] * ri;
+        const double m = dot / (double)P;
+        for (int64_t p = 0; p < P; p++) {
+            const double xh = row[p] * ri;
+            dr[t * P + p] = ri * (gamma[p] * d[p] - xh * m);
+            dgamma[p] += d[p] * xh;
+        }
+    }
+}

@@ -337,3 +337,73 @@ def test_stack_fd_and_g_only_reading_rejected(orc):
     # Reading "every layer is driven by g alone" gives a different answer.
     g_only = orc.layer_grad(dict(lay0, x=ours["forward"]["x_layers"][0], g=st["g"]), window=None)
     assert rel_err(g_only["dW_B"], fd) > 1e-2
+
+
+# ---------------------------------------------------------------- normalised layer input
+
+def test_rmsnorm_closed_form(orc):
+    rng = np.random.default_rng(91)
+    r = rng.standard_normal((6, 40)) * rng.uniform(0.01, 100.0, (6, 1))
+    ones = np.ones(40)
+    out, rinv = orc.rmsnorm(r, ones, eps=0.0)
+    # every row has unit mean square, and scaling a row changes nothing
+    assert np.allclose((out ** 2).mean(axis=1), 1.0, rtol=1e-13, atol=0)
+    assert np.allclose(orc.rmsnorm(3.7 * r, ones, eps=0.0)[0], out, rtol=1e-13, atol=1e-14)
+    assert np.allclose(rinv, 1.0 / np.sqrt((r ** 2).mean(axis=1)), rtol=1e-13)
+    # a per-channel scale multiplies the columns; eps damps small rows
+    gam = rng.uniform(-2, 2, 40)
+    assert np.allclose(orc.rmsnorm(r, gam, eps=0.0)[0], out * gam, rtol=1e-13, atol=1e-14)
+    small = np.full((1, 40), 1e-4)
+    o, _ = orc.rmsnorm(small, ones, eps=1e-5)
+    assert np.allclose(o, 1e-4 / np.sqrt(1e-8 + 1e-5), rtol=1e-13)
+
+
+def test_rmsnorm_vjp_finite_differences(orc):
+    rng = np.random.default_rng(92)
+    T, P = 4, 9
+    r = rng.standard_normal((T, P))
+    gam = rng.uniform(0.5, 1.5, P)
+    d = rng.standard_normal((T, P))
+    dr, dg = orc.rmsnorm_vjp(r, gam, d)
+    f_r = lambda: float(np.sum(d * orc.rmsnorm(r, gam)[0]))
+    f_g = lambda: float(np.sum(d * orc.rmsnorm(r, gam)[0]))
+    assert rel_err(dr, _fd_grad(f_r, r)) < 1e-8
+    assert rel_err(dg, _fd_grad(f_g, gam)) < 1e-8
+
+
+def test_rmsnorm_vjp_orthogonal_to_input_without_eps(orc):
+    # without eps the normalisation is invariant to scaling each row, so the
+    # input cotangent of every row is orthogonal to that row
+    rng = np.random.default_rng(93)
+    r = rng.standard_normal((5, 33))
+    dr, _ = orc.rmsnorm_vjp(r, rng.uniform(-1, 1, 33), rng.standard_normal((5, 33)), eps=0.0)
+    dots = np.einsum("tp,tp->t", dr, r) / (np.linalg.norm(dr, axis=1) * np.linalg.norm(r, axis=1))
+    assert np.abs(dots).max() < 1e-13
+
+
+@pytest.mark.parametrize("K", [2, 3])
+def test_normalised_stack_matches_monolithic_autograd(orc, K):
+    """Stack with normalised layer inputs: the oracle's per-layer backward
+    (layer VJPs, then the normalisation's VJP) equals end-to-end reverse mode
+    through an RMS normalisation written independently in torch."""
+    torch = pytest.importorskip("torch")
+    T, P, N = 24, 6, 3
+    st = _stack64(K, T=T, P=P, N=N, seed=90 + K)
+    rng = np.random.default_rng(94 + K)
+    for lay in st["layers"]:
+        lay["norm_scale"] = rng.uniform(0.5, 1.5, P)
+    ours = orc.stack_grad(st, window=None)
+    ths = [{k: torch.tensor(v, requires_grad=True) for k, v in lay.items()} for lay in st["layers"]]
+    x0 = torch.tensor(st["x"], requires_grad=True)
+    r = x0
+    for th in ths:
+        xin = th["norm_scale"] * r / torch.sqrt((r * r).mean(dim=1, keepdim=True) + orc.NORM_EPS)
+        th2 = dict(th, x=xin)
+        r = r + _torch_forward(th2, T, N)
+    L = (torch.tensor(st["g"]) * r).sum()
+    L.backward()
+    for k in range(K):
+        for pname, gname in (("W_delta", "dW_delta"), ("W_B", "dW_B"), ("W_C", "dW_C"),
+                             ("alpha", "dalpha"), ("delta_bias", "dbias"), ("norm_scale", "dnorm_scale")):
+            assert rel_err(ours["layers"][k][gname], ths[k][pname].grad.numpy()) < 1e-10, (k, pname)
+    assert rel_err(ours["dx0"], x0.grad.numpy()) < 1e-10

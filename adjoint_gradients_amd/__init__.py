@@ -52,7 +52,7 @@ class Dims(ctypes.Structure):
 
 class Layer(ctypes.Structure):
     _fields_ = [("W_delta", ctypes.c_void_p), ("W_B", ctypes.c_void_p), ("W_C", ctypes.c_void_p),
-                ("alpha", ctypes.c_void_p), ("delta_bias", ctypes.c_void_p)]
+                ("alpha", ctypes.c_void_p), ("delta_bias", ctypes.c_void_p), ("norm_scale", ctypes.c_void_p)]
 
 
 class Saved(ctypes.Structure):
@@ -62,7 +62,8 @@ class Saved(ctypes.Structure):
 
 class Grads(ctypes.Structure):
     _fields_ = [("dW_delta", ctypes.c_void_p), ("dW_B", ctypes.c_void_p), ("dW_C", ctypes.c_void_p),
-                ("dalpha", ctypes.c_void_p), ("dbias", ctypes.c_void_p), ("dx", ctypes.c_void_p)]
+                ("dalpha", ctypes.c_void_p), ("dbias", ctypes.c_void_p), ("dx", ctypes.c_void_p),
+                ("dnorm_scale", ctypes.c_void_p)]
 
 
 def _load():
@@ -152,8 +153,8 @@ def make_dims(T: int, P: int, N: int, chunk: int = 256, io: str = "f32") -> Dims
     return Dims(T, P, N, chunk, SSM_BF16 if io == "bf16" else SSM_F32)
 
 
-def layer_struct(W_delta, W_B, W_C, alpha, delta_bias=None) -> Layer:
-    return Layer(_ptr(W_delta), _ptr(W_B), _ptr(W_C), _ptr(alpha), _ptr(delta_bias))
+def layer_struct(W_delta, W_B, W_C, alpha, delta_bias=None, norm_scale=None) -> Layer:
+    return Layer(_ptr(W_delta), _ptr(W_B), _ptr(W_C), _ptr(alpha), _ptr(delta_bias), _ptr(norm_scale))
 
 
 def saved_struct(saved: dict) -> Saved:
@@ -163,7 +164,8 @@ def saved_struct(saved: dict) -> Saved:
 
 def grads_struct(grads: dict) -> Grads:
     return Grads(_ptr(grads.get("dW_delta")), _ptr(grads.get("dW_B")), _ptr(grads.get("dW_C")),
-                 _ptr(grads.get("dalpha")), _ptr(grads.get("dbias")), _ptr(grads.get("dx")))
+                 _ptr(grads.get("dalpha")), _ptr(grads.get("dbias")), _ptr(grads.get("dx")),
+                 _ptr(grads.get("dnorm_scale")))
 
 
 def ssm_forward(dims: Dims, layer: Layer, x, y, saved: Saved, ws, ws_bytes: int, stream=None):
@@ -222,9 +224,10 @@ class LayerTensors:
     W_C: object
     alpha: object
     delta_bias: object = None
+    norm_scale: object = None  # [P] float32: stack layers that read the RMS-normalised stream
 
     def struct(self) -> Layer:
-        return layer_struct(self.W_delta, self.W_B, self.W_C, self.alpha, self.delta_bias)
+        return layer_struct(self.W_delta, self.W_B, self.W_C, self.alpha, self.delta_bias, self.norm_scale)
 
 
 def io_dtype(io: str):
@@ -318,6 +321,9 @@ def stack_grad(dims: Dims, layers: list, x0, g, window: int, ws=None, want_dx0=T
         raise SsmError(4, "ssm_workspace_bytes")
     ws = alloc_workspace(nbytes, x0.device) if ws is None else ws
     grads = [alloc_grads(dims, device=x0.device) for _ in range(K)]
+    for gr, lay in zip(grads, layers):
+        if lay.norm_scale is not None:
+            gr["dnorm_scale"] = torch.empty(dims.P, device=x0.device, dtype=torch.float32)
     f = dict(device=x0.device, dtype=torch.float32)
     dx0 = torch.empty(dims.T, dims.P, **f) if want_dx0 else None
     xK = torch.empty(dims.T, dims.P, **f) if want_xK else None

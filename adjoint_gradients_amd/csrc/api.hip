@@ -66,6 +66,7 @@ ssm_status check_layer(const ssm_layer* L) {
   if (!aligned16(L->W_delta) || !aligned16(L->W_B) || !aligned16(L->W_C) || !aligned16(L->alpha))
     return SSM_ERR_ARG;
   if (L->delta_bias && !aligned16(L->delta_bias)) return SSM_ERR_ARG;
+  if (L->norm_scale && !aligned16(L->norm_scale)) return SSM_ERR_ARG;
   return SSM_OK;
 }
 
@@ -79,7 +80,7 @@ ssm_status check_saved(const ssm_saved* s) {
 
 ssm_status check_grads(const ssm_grads* g) {
   if (!g || !g->dW_delta || !g->dW_B || !g->dW_C) return SSM_ERR_ARG;
-  const void* ps[] = {g->dW_delta, g->dW_B, g->dW_C, g->dalpha, g->dbias, g->dx};
+  const void* ps[] = {g->dW_delta, g->dW_B, g->dW_C, g->dalpha, g->dbias, g->dx, g->dnorm_scale};
   for (const void* p : ps)
     if (p && !aligned16(p)) return SSM_ERR_ARG;
   return SSM_OK;
@@ -201,6 +202,27 @@ size_t bwd_ws_bytes(const ssm_dims* d, int64_t W, bool need_dx, bool own_hsub = 
   return cv.off;
 }
 
+// Normalisation buffers of the stack: per layer the residual r^k and 1/rms per
+// token (kept for the VJP), the layer's dx, and the VJP's row scratch.
+struct NormWs {
+  float* rk;      // [K][T][P]
+  float* rinv;    // [K][T]
+  float* dx;      // [T][P]
+  float* m;       // [T]
+  float* part;    // [row blocks][P]
+};
+
+NormWs carve_norm(Carver& cv, const ssm_dims* d, int32_t K) {
+  NormWs n;
+  const int64_t T = d->T, P = d->P;
+  n.rk = cv.take<float>(static_cast<size_t>(K) * T * P);
+  n.rinv = cv.take<float>(static_cast<size_t>(K) * T);
+  n.dx = cv.take<float>(static_cast<size_t>(T * P));
+  n.m = cv.take<float>(static_cast<size_t>(T));
+  n.part = cv.take<float>(static_cast<size_t>(ssm::norm_row_blocks(T) * P));
+  return n;
+}
+
 size_t stack_ws_bytes(const ssm_dims* d, int64_t W, int32_t K) {
   Carver cv(nullptr);
   for (int32_t k = 0; k < K; k++) carve_saved(cv, d);
@@ -208,6 +230,7 @@ size_t stack_ws_bytes(const ssm_dims* d, int64_t W, int32_t K) {
   cv.take<float>(static_cast<size_t>(d->T * d->P));
   cv.take<float>(static_cast<size_t>(d->T * d->P));
   cv.take<float>(static_cast<size_t>(d->T * d->P));
+  carve_norm(cv, d, K);
   const size_t f = fwd_ws_bytes(d), b = bwd_ws_bytes(d, W, true);
   return cv.off + (f > b ? f : b);
 }
@@ -289,7 +312,7 @@ hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, co
 
 extern "C" {
 
-int32_t ssm_version(void) { return 200; }
+int32_t ssm_version(void) { return 300; }
 
 const char* ssm_status_str(ssm_status s) {
   switch (s) {
@@ -335,6 +358,7 @@ static ssm_status forward_impl(const ssm_dims* d, const ssm_layer* L, const void
   ssm_status s = check_dims(d);
   if (s != SSM_OK) return s;
   if ((s = check_layer(L)) != SSM_OK) return s;
+  if (L->norm_scale) return SSM_ERR_ARG;  // normalisation belongs to the stack
   if ((s = check_saved(sv)) != SSM_OK) return s;
   if (!x || !y || !aligned16(x) || !aligned16(y)) return SSM_ERR_ARG;
   if (mk.n < 0 || (mk.n > 0 && !mk.ev)) return SSM_ERR_ARG;
@@ -351,6 +375,7 @@ static ssm_status adjoint_impl(const ssm_dims* d, const ssm_layer* L, const void
   ssm_status s = check_dims(d);
   if (s != SSM_OK) return s;
   if ((s = check_layer(L)) != SSM_OK) return s;
+  if (L->norm_scale) return SSM_ERR_ARG;  // normalisation belongs to the stack
   if ((s = check_saved(sv)) != SSM_OK) return s;
   if ((s = check_grads(gr)) != SSM_OK) return s;
   if (!x || !g || !aligned16(x) || !aligned16(g)) return SSM_ERR_ARG;
@@ -424,20 +449,32 @@ ssm_status ssm_stack_grad(int32_t K, const ssm_dims* d, const ssm_layer* layers,
   float* r = cv.take<float>(static_cast<size_t>(TP));
   float* y = cv.take<float>(static_cast<size_t>(TP));
   float* delta = cv.take<float>(static_cast<size_t>(TP));
+  NormWs nw = carve_norm(cv, d, K);
   const size_t shared_off = cv.off;
+  const int64_t T = d->T, P = d->P;
+  // x^k = io(r^k), or the normalised stream for a layer with norm_scale
+  // (which also keeps r^k and 1/rms for its VJP)
+  auto make_input = [&](int32_t k) -> hipError_t {
+    void* xk = xs + static_cast<size_t>(k) * xbytes;
+    if (layers[k].norm_scale)
+      return ssm::rmsnorm_forward(T, P, r, layers[k].norm_scale, ssm::kNormEps, xk, bf, nw.rinv + k * T,
+                                  nw.rk + static_cast<size_t>(k) * TP, st);
+    return ssm::residual_update(TP, r, nullptr, xk, bf, st);
+  };
 
   hipError_t e = ssm::residual_init(TP, x0, bf, r, st);
   if (e != hipSuccess) return SSM_ERR_HIP;
-  // x^0 = io(r^0)
-  if ((e = ssm::residual_update(TP, r, nullptr, xs, bf, st)) != hipSuccess) return SSM_ERR_HIP;
+  if ((e = make_input(0)) != hipSuccess) return SSM_ERR_HIP;
   for (int32_t k = 0; k < K; k++) {
     void* xk = xs + static_cast<size_t>(k) * xbytes;
     Carver fc(static_cast<char*>(ws) + shared_off);
     FwdWs fw = carve_fwd(fc, d);
     if ((e = run_forward(d, &layers[k], xk, y, &sv[k], fw, st)) != hipSuccess) return SSM_ERR_HIP;
-    // r^{k+1} = r^k + y^k and x^{k+1} = io(r^{k+1})
-    void* xnext = (k + 1 < K) ? xs + static_cast<size_t>(k + 1) * xbytes : nullptr;
+    // r^{k+1} = r^k + y^k, then x^{k+1} (fused into the update when it is a plain cast)
+    const bool plain_next = k + 1 < K && !layers[k + 1].norm_scale;
+    void* xnext = plain_next ? xs + static_cast<size_t>(k + 1) * xbytes : nullptr;
     if ((e = ssm::residual_update(TP, r, y, xnext, bf, st)) != hipSuccess) return SSM_ERR_HIP;
+    if (k + 1 < K && !plain_next && (e = make_input(k + 1)) != hipSuccess) return SSM_ERR_HIP;
   }
   if (xK) {
     if ((e = hipMemcpyAsync(xK, r, static_cast<size_t>(TP) * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess)
@@ -449,9 +486,20 @@ ssm_status ssm_stack_grad(int32_t K, const ssm_dims* d, const ssm_layer* layers,
     void* xk = xs + static_cast<size_t>(k) * xbytes;
     Carver bc(static_cast<char*>(ws) + shared_off);
     BwdWs bw = carve_bwd(bc, d, W, true);
-    // layer k is driven by delta^{k+1}; then delta^k = delta^{k+1} + dx^k
-    if ((e = run_backward(d, &layers[k], xk, &sv[k], delta, W, &grads[k], delta, bw, st)) != hipSuccess)
-      return SSM_ERR_HIP;
+    // layer k is driven by delta^{k+1}; then delta^k = delta^{k+1} + dx^k, or
+    // + the normalisation's VJP of dx^k
+    if (layers[k].norm_scale) {
+      ssm_grads gl = grads[k];
+      gl.dx = nw.dx;
+      if ((e = run_backward(d, &layers[k], xk, &sv[k], delta, W, &gl, nullptr, bw, st)) != hipSuccess)
+        return SSM_ERR_HIP;
+      if ((e = ssm::rmsnorm_vjp(T, P, nw.rk + static_cast<size_t>(k) * TP, nw.rinv + k * T, layers[k].norm_scale,
+                                nw.dx, nw.m, delta, nw.part, grads[k].dnorm_scale, st)) != hipSuccess)
+        return SSM_ERR_HIP;
+    } else {
+      if ((e = run_backward(d, &layers[k], xk, &sv[k], delta, W, &grads[k], delta, bw, st)) != hipSuccess)
+        return SSM_ERR_HIP;
+    }
   }
   if (dx0) {
     if ((e = hipMemcpyAsync(dx0, delta, static_cast<size_t>(TP) * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess)

@@ -88,6 +88,17 @@ bool bwd_plan(int64_t P, int64_t N, int C, BwdPlan* plan);
 size_t bwd_hsub_floats(int64_t T, int64_t P, int64_t N, int C);
 
 hipError_t launch_forward_scan(const FwdArgs& a, bool bf16, hipStream_t st);
+
+// RMS normalisation of the residual stream (norm.hip).  Forward: xio =
+// io(gamma r rinv), rinv per row, rcopy = r.  VJP for the cotangent d of xio:
+// delta += dr, dgamma (may be null) = sum over rows; m [T] and part
+// [norm_row_blocks(T)][P] are scratch.
+constexpr float kNormEps = 1e-5f;
+int64_t norm_row_blocks(int64_t T);
+hipError_t rmsnorm_forward(int64_t T, int64_t P, const float* r, const float* gamma, float eps, void* xio,
+                           bool bf16, float* rinv, float* rcopy, hipStream_t st);
+hipError_t rmsnorm_vjp(int64_t T, int64_t P, const float* r, const float* rinv, const float* gamma, const float* d,
+                       float* m, float* delta, float* part, float* dgamma, hipStream_t st);
 hipError_t launch_backward_scan(const BwdArgs& a, bool bf16, hipStream_t st);
 
 // ---------------------------------------------------------------- GEMMs

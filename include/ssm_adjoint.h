@@ -93,6 +93,9 @@ typedef struct {
   const void *W_C;          /* [N][P] io */
   const float *alpha;       /* [P][N]  decay rates, a = exp(-softplus(Delta) alpha) */
   const float *delta_bias;  /* [P] or NULL (zero bias) */
+  const float *norm_scale;  /* [P] or NULL.  Stack only: the layer reads the RMS-normalised
+                             * residual stream (see ssm_stack_grad).  The single-layer calls
+                             * take x as given and reject a non-NULL norm_scale. */
 } ssm_layer;
 
 /* State saved by ssm_forward for ssm_adjoint_grad (caller-owned buffers).
@@ -127,6 +130,7 @@ typedef struct {
   float *dalpha;    /* [P][N] or NULL */
   float *dbias;     /* [P] or NULL */
   float *dx;        /* [T][P] or NULL: cotangent of the layer input x */
+  float *dnorm_scale; /* [P] or NULL: gradient of norm_scale (stack layers that normalise) */
 } ssm_grads;
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -185,6 +189,11 @@ ssm_status ssm_adjoint_grad(const ssm_dims *dims, const ssm_layer *layer, const 
  * is driven by the total cotangent delta^{k+1} = dL/dr^{k+1}, and
  * delta^k = delta^{k+1} + dx^k (the io cast is treated as the identity).
  * Every layer uses the same window.
+ * A layer with norm_scale = gamma reads the normalised stream instead (the
+ * review's Algorithm 1 "normalised input"; the norm is RMS normalisation):
+ *   x^k = io(gamma r^k / sqrt(mean_p (r^k)^2 + 1e-5))  per token,
+ * and delta^k = delta^{k+1} + (the normalisation's VJP of dx^k); its
+ * gradient goes to grads[k].dnorm_scale when that is non-NULL.
  *   layers [K], grads [K] (host arrays of structs with device pointers)
  *   x0 [T][P] io; g [T][P] float32
  *   dx0 [T][P] float32 or NULL: dL/dx0

@@ -34,8 +34,10 @@ def to_dev(arr, io="f32"):
 def layer_tensors(inp, io):
     import adjoint_gradients_amd as agm
 
+    ns = inp.get("norm_scale")
     return agm.LayerTensors(to_dev(inp["W_delta"], io), to_dev(inp["W_B"], io), to_dev(inp["W_C"], io),
-                            to_dev(inp["alpha"]), to_dev(inp["delta_bias"]))
+                            to_dev(inp["alpha"]), to_dev(inp["delta_bias"]),
+                            None if ns is None else to_dev(np.asarray(ns, dtype=np.float32)))
 
 
 def gpu_layer(inp, window, chunk, want_dx=True, io=None, g=None, sub_states=False):

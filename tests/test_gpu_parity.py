@@ -158,6 +158,41 @@ def test_poisoned_buffers(orc, T, P, N, io, window, chunk, sub_states):
     compare(got, ref, GRAD_KEYS, TOL[io], f"poisoned N={N} P={P} sub_states={sub_states}")
 
 
+@pytest.mark.parametrize("io,window,mask", [("f32", 256, (1, 1, 1)), ("f32", 50, (1, 0, 1)),
+                                            ("bf16", 256, (1, 1, 1)), ("bf16", 50, (0, 1, 1))])
+def test_stack_normalised(orc, io, window, mask):
+    # layers reading the RMS-normalised residual stream (mask: which layers
+    # normalise); every gradient, dgamma, dx0 and r^K against the oracle
+    c = LayerCase("stack_norm", 256, 48, 16, io, (), K=3, seed=41)
+    st = make_stack(c)
+    rng = np.random.default_rng(42)
+    for lay, m in zip(st["layers"], mask):
+        if m:
+            lay["norm_scale"] = rng.uniform(0.5, 1.5, 48).astype(np.float32)
+    say(f"case normalised stack K=3 io={io} W={window} mask={mask}")
+    grads, dx0, xK = _gpu_stack(st, window, 64)
+    st64 = dict(st, x=np.asarray(st["x"], np.float64), g=np.asarray(st["g"], np.float64),
+                layers=[{k: np.asarray(v, np.float64) for k, v in lay.items()} for lay in st["layers"]])
+    ref = orc.stack_grad(st64, window=None if window >= 256 else window)
+    tol = TOL[io]
+    for k in range(3):
+        names = ["dW_delta", "dW_B", "dW_C", "dalpha", "dbias"] + (["dnorm_scale"] if mask[k] else [])
+        compare(grads[k], ref["layers"][k], [(n, n) for n in names], tol, f"normalised stack layer {k}")
+    assert rel_err(dx0, ref["dx0"]) <= tol
+    assert rel_err(xK, ref["forward"]["r_final"]) <= tol
+
+
+def test_single_layer_rejects_norm_scale():
+    import adjoint_gradients_amd as agm
+    from gpu_util import layer_tensors, to_dev
+
+    inp = make_layer(small_case(64, 16, 4, 43))
+    inp["norm_scale"] = np.ones(16, dtype=np.float32)
+    dims = agm.make_dims(64, 16, 4, 64, "f32")
+    with pytest.raises(agm.SsmError):
+        agm.forward(dims, layer_tensors(inp, "f32"), to_dev(inp["x"]))
+
+
 def test_determinism_and_linearity():
     import adjoint_gradients_amd as agm  # noqa: F401
 

@@ -27,6 +27,7 @@ WORKLOADS = {
     "cfg1": (1, 2048, 256),
     "cfg1exact": (1, 16384, 256),
     "cfg4": (4, 4096, 256),  # the 4-layer residual stack (ssm_stack_grad), timed whole
+    "cfg4norm": (4, 4096, 256),  # the same stack, every layer reading the RMS-normalised stream
 }
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -285,7 +286,7 @@ def study_memory():
             del y, saved, grads, inp, x, g, lay
 
 
-def bench_stack(args, cfg_idx, window, chunk):
+def bench_stack(args, cfg_idx, window, chunk, norm=False):
     """One step of the K-layer residual stack: ssm_stack_grad (K forwards, then
     the K gradients in reverse with the cotangent passed down), timed whole
     with events on the library's stream.  Inputs as in the stack tests."""
@@ -300,12 +301,16 @@ def bench_stack(args, cfg_idx, window, chunk):
     dev = "cuda:0"
     torch.cuda.set_device(0)
     rng = np.random.Generator(np.random.PCG64(case.seed))
+    nrng = np.random.default_rng(44)
     lays = []
     for _ in range(K):
         wts = _weights(rng, case)
+        gam = None
+        if norm:  # gamma ~ U(0.5, 1.5) at the stack's input scale 1 / sqrt(N)
+            gam = torch.from_numpy((nrng.uniform(0.5, 1.5, P) / np.sqrt(N)).astype(np.float32)).to(dev)
         lays.append(agm.LayerTensors(*(torch.from_numpy(wts[k]).to(dev).to(torch.bfloat16)
                                        for k in ("W_delta", "W_B", "W_C")),
-                                     torch.from_numpy(_alpha(case)).to(dev), torch.zeros(P, device=dev)))
+                                     torch.from_numpy(_alpha(case)).to(dev), torch.zeros(P, device=dev), gam))
     gen = torch.Generator(device=dev)
     gen.manual_seed(1_000_003 * (case.seed + 1))
     x0 = (torch.randn(T, P, generator=gen, device=dev) * case.x_scale).to(torch.bfloat16)
@@ -313,6 +318,9 @@ def bench_stack(args, cfg_idx, window, chunk):
     dims = agm.make_dims(T, P, N, chunk, "bf16")
     ws = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, window, K), dev)
     grads = [agm.alloc_grads(dims, device=dev) for _ in range(K)]
+    if norm:
+        for gr in grads:
+            gr["dnorm_scale"] = torch.empty(P, device=dev, dtype=torch.float32)
     dx0 = torch.empty(T, P, device=dev, dtype=torch.float32)
     xK = torch.empty(T, P, device=dev, dtype=torch.float32)
     L = [lay.struct() for lay in lays]
@@ -337,8 +345,9 @@ def bench_stack(args, cfg_idx, window, chunk):
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{case.name}: {K}-layer residual stack, T={T}, P={P}, N={N}, io=bf16, "
-                               f"fp32 state and residual, window={window}, checkpoint every {chunk} tokens",
-                   "T": T, "P": P, "N": N, "K": K, "window": window, "chunk": chunk},
+                               f"fp32 state and residual, window={window}, checkpoint every {chunk} tokens"
+                               + (", RMS-normalised layer inputs" if norm else ""),
+                   "T": T, "P": P, "N": N, "K": K, "window": window, "chunk": chunk, "normalised": norm},
         "roofline": None,
         "note": "stack call timed whole (no per-kernel events); the single-layer workloads carry the roofline",
     }
@@ -397,7 +406,7 @@ def main():
 
     cfg_idx, window, chunk = WORKLOADS[args.workload]
     if CONFIGS[cfg_idx].K > 1:
-        bench_stack(args, cfg_idx, window, chunk)
+        bench_stack(args, cfg_idx, window, chunk, norm=args.workload.endswith("norm"))
         return
     case = CONFIGS[cfg_idx]
     dev = "cuda:0"

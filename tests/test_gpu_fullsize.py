@@ -212,10 +212,12 @@ def test_cfg4_stack_equals_layer_composition():
     assert e <= 1e-5
 
 
-@pytest.mark.parametrize("window", [4096, 1024])
-def test_cfg4_stack_prefix_oracle(orc, window):
+@pytest.mark.parametrize("window,norm", [(4096, False), (1024, False), (4096, True)])
+def test_cfg4_stack_prefix_oracle(orc, window, norm):
     """The 4-layer, P=1536, N=64 bf16 stack on its first 4096 tokens against
-    the oracle's stack (cotangent passing, bf16 layer inputs)."""
+    the oracle's stack (cotangent passing, bf16 layer inputs); with norm, every
+    layer reads the RMS-normalised stream (scale gamma ~ U(0.5, 1.5) / sqrt(N),
+    the input scale of this stack)."""
     from gpu_util import to_dev
     from ssm_inputs import make_stack
 
@@ -226,7 +228,11 @@ def test_cfg4_stack_prefix_oracle(orc, window):
     T = 4096
     st = make_stack(case, T=T)
     K, P, N = st["K"], st["P"], st["N"]
-    say(f"case {case.name} prefix stack: K={K} T={T} P={P} N={N} W={window} C={CHUNK}")
+    if norm:
+        rng = np.random.default_rng(44)
+        for lay in st["layers"]:
+            lay["norm_scale"] = (rng.uniform(0.5, 1.5, P) / np.sqrt(N)).astype(np.float32)
+    say(f"case {case.name} prefix stack: K={K} T={T} P={P} N={N} W={window} C={CHUNK} norm={norm}")
     dims = agm.make_dims(T, P, N, CHUNK, "bf16")
     from gpu_util import layer_tensors
 
@@ -240,7 +246,8 @@ def test_cfg4_stack_prefix_oracle(orc, window):
     worst = 0.0
     for k in range(K):
         got = {n: v.double().cpu().numpy() for n, v in grads[k].items() if v is not None}
-        errs = {n: rel_err(got[n], ref["layers"][k][n]) for n in ("dW_delta", "dW_B", "dW_C", "dalpha", "dbias")}
+        names = ("dW_delta", "dW_B", "dW_C", "dalpha", "dbias") + (("dnorm_scale",) if norm else ())
+        errs = {n: rel_err(got[n], ref["layers"][k][n]) for n in names}
         say(f"  layer {k}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
         worst = max(worst, max(errs.values()))
     e_dx0 = rel_err(dx0.double().cpu().numpy(), ref["dx0"])

@@ -69,7 +69,7 @@ class Grads(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                          "(python -m adjoint_gradients_amd._build)")
+                          "(python adjoint_gradients_amd/_build.py)")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     lib.ssm_version.argtypes = []

@@ -389,12 +389,14 @@ __global__ __launch_bounds__(256) void k_bwd_hsub(BwdArgs a, int64_t NB) {
 
 // Carry of the adjoint sums between chunks, right to left:
 //   carry[K-1] = 0,  carry[k-1] = A_k carry[k] + umu[k],  A_k = exp(-alpha sum_{t in k} s_t).
-// carry[k] is a_{e+1} mu_{e+1} for the last token e of chunk k.
+// carry[k] is a_{e+1} mu_{e+1} for the last token e of chunk k.  umu may be
+// carry itself (windowed aggregates composed in place): each element is read
+// before it is overwritten, by the same thread.
 __global__ __launch_bounds__(256) void k_bwd_carry(int64_t K, int64_t P, int64_t N,
                                                    const float* __restrict__ alpha,
                                                    const double* __restrict__ ssum,
-                                                   const float* __restrict__ umu,
-                                                   float* __restrict__ carry) {
+                                                   const float* umu,
+                                                   float* carry) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t PN = P * N;
   if (e >= PN) return;
@@ -403,9 +405,47 @@ __global__ __launch_bounds__(256) void k_bwd_carry(int64_t K, int64_t P, int64_t
   float cin = 0.0f;
 #pragma unroll 8
   for (int64_t k = K - 1; k >= 0; k--) {
+    const float u = umu[k * PN + e];
     carry[k * PN + e] = cin;
     const float A = fast_exp2(-static_cast<float>(ssum[k * P + p]) * al2);
-    cin = fmaf(A, cin, umu[k * PN + e]);
+    cin = fmaf(A, cin, u);
+  }
+}
+
+// Windows of a whole number q = W / C of chunks.  The window term of chunk
+// k's aggregate is then the exact aggregate of chunk k + q scaled by the
+// decay across the W tokens in between:
+//   sum_{i in k} g_{i+W} c_{i+W} prod_{j=t0}^{i+W} a_j
+//     = exp(-alpha sum_{t=t0}^{t0+W-1} s_t) * umu_exact[k+q],
+// because the tokens i + W of a full chunk k are exactly chunk k + q (a
+// partial chunk is the last one, and has no partner inside the sequence).
+// The local pass therefore runs without window terms (one exp per state
+// element instead of two, no partner reads), and this fully parallel pass
+// writes each windowed aggregate into `out` (the carry array, which
+// k_bwd_carry then turns into carries in place).  Lanes of state 0 also write
+// the fp64 sum of s over the W tokens that follow each chunk, for the main
+// kernel.
+__global__ __launch_bounds__(256) void k_bwd_window_compose(int64_t K, int64_t P, int64_t N, int64_t q,
+                                                            const float* __restrict__ alpha,
+                                                            const double* __restrict__ ps64,
+                                                            const float* __restrict__ umu,
+                                                            float* __restrict__ out,
+                                                            double* __restrict__ hwin) {
+  const int64_t PN = P * N;
+  const int64_t e = static_cast<int64_t>(blockIdx.y) * blockDim.x + threadIdx.x;
+  const int64_t k = blockIdx.x;
+  if (e >= PN) return;
+  const int64_t p = e / N;
+  float u = umu[k * PN + e];
+  if (k + q < K) {
+    const float Ew = static_cast<float>(ps64[(k + q) * P + p] - ps64[k * P + p]);
+    u = fmaf(-fast_exp2(-Ew * (alpha[e] * kLog2e)), umu[(k + q) * PN + e], u);
+  }
+  out[k * PN + e] = u;
+  if (e - p * N == 0) {
+    const int64_t kb = (k + q + 1 < K) ? k + q + 1 : K;
+    const int64_t ka = (k + 1 < K) ? k + 1 : K;
+    hwin[k * P + p] = ps64[kb * P + p] - ps64[ka * P + p];
   }
 }
 
@@ -510,15 +550,26 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     k_bwd_prefix<<<static_cast<unsigned>((a.P + 255) / 256), 256, 0, st>>>(K, a.P, a.ssum, a.ps64);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // A window of whole chunks is composed from exact chunk aggregates in the
+  // carry pass (k_bwd_carry_win); otherwise the local pass walks the window
+  // term itself.
+  const bool compose = WIN && (a.W % a.C) == 0;
   {
     constexpr int NNc = NL * G;
-    const size_t rows_b = static_cast<size_t>(WIN ? 2 : 1) * a.C * NNc * 4;
-    if (NNc % 4 == 0 && rows_b <= kBwdLocRowLds) {
-      k_bwd_local_staged<IO, NL, G, WIN>
-          <<<dim3(static_cast<unsigned>(K), static_cast<unsigned>((NB + kBwdLocWpb - 1) / kBwdLocWpb)),
-             64 * kBwdLocWpb, rows_b, st>>>(a, NB);
-    } else {
-      k_bwd_local<IO, NL, G, WIN><<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(NB)), 64, 0, st>>>(a);
+    const bool wl = WIN && !compose;
+    const size_t rows_b = static_cast<size_t>(wl ? 2 : 1) * a.C * NNc * 4;
+    const dim3 gs(static_cast<unsigned>(K), static_cast<unsigned>((NB + kBwdLocWpb - 1) / kBwdLocWpb));
+    const dim3 g1(static_cast<unsigned>(K), static_cast<unsigned>(NB));
+    const bool staged = NNc % 4 == 0 && rows_b <= kBwdLocRowLds;
+    if constexpr (WIN) {
+      if (wl) {
+        if (staged) k_bwd_local_staged<IO, NL, G, true><<<gs, 64 * kBwdLocWpb, rows_b, st>>>(a, NB);
+        else k_bwd_local<IO, NL, G, true><<<g1, 64, 0, st>>>(a);
+      }
+    }
+    if (!wl) {
+      if (staged) k_bwd_local_staged<IO, NL, G, false><<<gs, 64 * kBwdLocWpb, rows_b, st>>>(a, NB);
+      else k_bwd_local<IO, NL, G, false><<<g1, 64, 0, st>>>(a);
     }
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -540,8 +591,13 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   }
   a.marks.rec(1, st);
   const int64_t PN = a.P * a.N;
-  k_bwd_carry<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, a.alpha, a.ssum, a.umu,
-                                                                      a.carry);
+  if (compose) {
+    k_bwd_window_compose<<<dim3(static_cast<unsigned>(K), static_cast<unsigned>((PN + 255) / 256)), 256, 0, st>>>(
+        K, a.P, a.N, a.W / a.C, a.alpha, a.ps64, a.umu, a.carry, a.hwin);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  k_bwd_carry<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, a.alpha, a.ssum,
+                                                                      compose ? a.carry : a.umu, a.carry);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.marks.rec(2, st);
   auto kern = k_bwd_main<IO, NL, G, WIN>;

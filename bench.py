@@ -71,10 +71,13 @@ def algorithmic(name, T, P, N, C, W, s_io, sub_states=False):
     sub = (T + 7) // 8 * P * N * 4 if sub_states else 0
     if name == "fwd_final":
         return (T * (P * s_io + 8 * P + 8 * N) + K * P * N * 4 + sub, 0, 6 * E)
+    # a window of whole chunks is composed from exact chunk aggregates in the
+    # carry pass, so the local pass then walks no window term
+    compose = win and W % C == 0
     if name == "bwd_local":
-        return (T * (8 * P + 4 * N) + K * P * N * 4, 0, (10 if win else 5) * E)
+        return (T * (8 * P + 4 * N) + K * P * N * 4, 0, (10 if win and not compose else 5) * E)
     if name == "bwd_carry":
-        return (K * P * N * 8 + K * P * 8, 0, 4 * K * P * N)
+        return (K * P * N * 8 + K * P * 8, 0, (9 if compose else 4) * K * P * N)
     if name == "bwd_main":
         # per token: x, s, g, b, c, dDelta (io) and db/dc, plus h_ckpt once per chunk
         return (T * (P * s_io + 4 * P + 4 * P + 8 * N + P * s_io + 8 * N) + K * P * N * 4 + sub, 0,

@@ -85,6 +85,23 @@ def test_window_chunk_not_dividing(orc, chunk):
         _run_case(orc, inp, W, chunk, f"winpin C={chunk} W={W}")
 
 
+@pytest.mark.parametrize("chunk,W", [(32, 32), (32, 96), (64, 320), (100, 300), (128, 640)])
+def test_window_whole_chunks(orc, chunk, W):
+    """Windows of whole chunks: the window terms of a chunk's aggregate come
+    from the exact aggregate W tokens later.  T = 700 leaves a ragged last
+    chunk, and the slow decay keeps every dropped term visible."""
+    inp = make_layer(window_pin_case(seed=102, T=700, P=8, N=4))
+    got, ref = _run_case(orc, inp, W, chunk, f"winpin whole chunks C={chunk} W={W}")
+    exact = orc.layer_grad(oracle_inputs(inp), window=None)
+    say(f"  window-vs-exact gap (dx) = {rel_err(ref['dx'], exact['dx']):.2e}")
+
+
+def test_window_whole_chunks_bf16_n16(orc):
+    inp = make_layer(small_case(1000, 96, 16, 21, io="bf16"))
+    for W in (128, 384):
+        _run_case(orc, inp, W, 128, f"bf16 N=16 whole-chunk window W={W}")
+
+
 def test_bf16_small(orc):
     c = small_case(1024, 96, 16, 9, io="bf16")
     inp = make_layer(c)

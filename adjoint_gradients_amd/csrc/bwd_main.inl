@@ -118,7 +118,7 @@ struct RevState {
   float inc[NL];   // a_{i+1} mu_{i+1}
   float dal[NL];   // sum_i da_i s_i a_i  (dalpha = -dal)
   float dbias;
-  double H, sigma, suffix;  // window sums of s (fp64)
+  double E64;  // sum of s over tokens i+1 .. i+W for the next token i (fp64)
 };
 
 // One token of the reverse walk: adjoint recurrence + local VJPs + channel
@@ -127,7 +127,7 @@ template <typename IO, int NL, int G, bool WIN>
 __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, const Tok& tk, const float (&bt)[NL],
                                           const float (&ct)[NL], const float (&cm)[NL], const float (&hp)[NL],
                                           const float (&hc)[NL], int64_t i, uint32_t off, bool valid, int grp,
-                                          int pl, int lane, float* red, float* xw_tau) {
+                                          int pl, int lane, float* red, int rd_off, float* xw_tau) {
   constexpr int CH = 64 / G;
   constexpr int NN = NL * G;
   constexpr int OUT = 2 * NN;
@@ -140,15 +140,15 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
   if constexpr (WIN) {
     if (i + a.W < a.T) {  // uniform: the partner token i + W exists
       // drop the token leaving the window: - g_{i+W} c_{i+W} prod_{j=i+1}^{i+W} a_j
-      const float E = static_cast<float>(st.sigma + st.H - st.suffix);
+      const float E = static_cast<float>(st.E64);
 #pragma unroll
       for (int j = 0; j < NL; j++) {
         const float D = fast_exp2(-E * st.al2[j]);
         mu[j] = fmaf(-tk.gm * cm[j], D, mu[j]);
       }
-      st.suffix += static_cast<double>(tk.sm);
+      st.E64 -= static_cast<double>(tk.sm);  // token i + W leaves the window of token i - 1
     }
-    st.sigma += static_cast<double>(tk.s);
+    st.E64 += static_cast<double>(tk.s);  // token i enters it
   }
   float ds = 0.0f, dxd = 0.0f;
 #pragma unroll
@@ -159,14 +159,20 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
     st.dal[j] = fmaf(tt, tk.s, st.dal[j]);
     dxd = fmaf(mu[j], bt[j], dxd);
   }
-  if constexpr (G > 1) {
+  // Sums over the lane groups of a channel.  With two groups one exchange
+  // serves both: group 0 then holds the sum of ds, group 1 that of dxd, and
+  // each group stores its own (dD and dbias are only kept from group 0).
+  if constexpr (G == 2) {
+    ds = half_sums_pair(ds, dxd);
+    dxd = ds;
+  } else if constexpr (G > 1) {
     ds = group_sum<G, CH>(ds);
     dxd = group_sum<G, CH>(dxd);
   }
   const float dD = -(ds * (1.0f / kLog2e)) * one_minus_exp_neg(tk.s);
-  if (valid && grp == 0) {
-    store_io(row_ptr(static_cast<IO*>(a.dY), i, a.ldy) + off, dD);
-    if (a.dxdir) row_ptr(a.dxdir, i, a.P)[off] = dxd;
+  if (valid) {
+    if (grp == 0) store_io(row_ptr(static_cast<IO*>(a.dY), i, a.ldy) + off, dD);
+    if (a.dxdir && grp == (G == 2 ? 1 : 0)) row_ptr(a.dxdir, i, a.P)[off] = dxd;
   }
   st.dbias += dD;
   // channel sums of db = mu x and dc = g h through an LDS transpose (placement
@@ -187,12 +193,13 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
     // from moving accesses across this point.
     __builtin_amdgcn_wave_barrier();
     const int o = lane >> 1, r = lane & 1;
-    const float4* rd = reinterpret_cast<const float4*>(red + RL::chunk(o, 4 * r));
-    float sum = 0.0f;
+    const float4* rd = reinterpret_cast<const float4*>(red + rd_off);
+    float sum;
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const float4 v = rd[q];
-      sum += (v.x + v.y) + (v.z + v.w);
+      const float pq = (v.x + v.y) + (v.z + v.w);
+      sum = q == 0 ? pq : sum + pq;
     }
     sum = xor_sum<1>(sum);
     if (r == 0) xw_tau[o] = sum;
@@ -256,6 +263,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   const int nsub_max = (C + S - 1) / S;
   constexpr int RED = redl::Layout<NL, G>::kFloats;  // transpose area per wavefront
   float* red = lds + 2 * STG + w * RED;
+  // this lane's read position in the transpose buffer (swizzled layout),
+  // fixed for the whole kernel
+  const int rd_off = redl::Layout<NL, G>::kSwz ? redl::Layout<NL, G>::chunk(lane >> 1, 4 * (lane & 1)) : 0;
   float* xw = lds + 2 * STG + kWpb * RED;  // [kWpb][S][OUT]
   float* hsg = a.hsub + hsub_offset(k, wave_live ? cb : 0, 0, NB, nsub_max, NL);
   const IO* xp = static_cast<const IO*>(a.x);
@@ -358,10 +368,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
     st.dal[j] = 0.0f;
   }
   st.dbias = 0.0f;
-  st.sigma = 0.0;
-  st.suffix = 0.0;
-  st.H = 0.0;
-  if constexpr (WIN) st.H = a.hwin[k * P + pc];
+  st.E64 = 0.0;
+  if constexpr (WIN) st.E64 = a.hwin[k * P + pc];  // sum of s over the W tokens after the chunk
 
   // ---------------- phase 1: forward walk, sub-chunk start states to scratch
   // (skipped when the separate sub-chunk pass already wrote them)
@@ -477,7 +485,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
 #pragma unroll
         for (int j = 0; j < NL; j++) hp[j] = (tau > 0) ? hr[tau > 0 ? tau - 1 : 0][j] : hs[j];
         rev_token<IO, NL, G, WIN>(st, a, cur, bt, ct, cm, hp, hr[tau], ta + tau, off, valid, grp, pl, lane, red,
-                                  xw + (w * S + tau) * OUT);
+                                  rd_off, xw + (w * S + tau) * OUT);
         cur = nxt;
       }
     } else {
@@ -518,7 +526,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
 #pragma unroll
           for (int j = 0; j < NL; j++) hp[j] = (tau > 0) ? hr[tau > 0 ? tau - 1 : 0][j] : hs[j];
           rev_token<IO, NL, G, WIN>(st, a, tk, bt, ct, cm, hp, hr[tau], ta + tau, off, valid, grp, pl, lane, red,
-                                    xw + (w * S + tau) * OUT);
+                                    rd_off, xw + (w * S + tau) * OUT);
         }
       }
     }

@@ -47,10 +47,10 @@ struct Layout {
   static constexpr int kFloats = floats(NL, G);
   static_assert(kFloats == (kSwz ? 4 * kGroup : OUT * kRS), "buffer size");
 
-  static constexpr int row_j(int j) {
-    constexpr int r[8] = {0, 32, 68, 100, 136, 168, 204, 236};
-    return r[j];
-  }
+  // row j of a group starts at 0, 32, 68, 100, 136, 168, 204, 236 floats
+  // (written as arithmetic: a table indexed by a lane-dependent row would be
+  // placed in global memory and read back with a load)
+  static constexpr int row_j(int j) { return 68 * (j >> 1) + 32 * (j & 1); }
   // constant part of a write address: state j of a group, part 0 (db) or 1 (dc)
   static constexpr int row_off(int part, int j) { return kSwz ? part * 2 * kGroup + row_j(j) : (part * NN + j) * kRS; }
   // per-lane part of a write address

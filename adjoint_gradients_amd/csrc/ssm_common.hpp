@@ -67,22 +67,32 @@ __device__ __forceinline__ float softplus_f(float d) {
 }
 
 // 1 - e^{-s} for s >= 0, i.e. the logistic sigmoid of Delta when s = softplus(Delta).
-// Below 0.5 a Taylor series (truncation < s^10/10! < 3e-10 relative) avoids
-// the cancellation of 1 - e^{-s}; both branches are evaluated and selected
-// (no divergence, no divisions).
+// Below 0.25 the series s sum_k (-s)^k / (k+1)!, cut after k = 6 (remainder
+// < s^7/8! < 2e-9 relative), avoids the cancellation of 1 - e^{-s}; above
+// it, 1 - e^{-s} >= 0.22 loses under 5e-7 relative to the rounding of
+// e^{-s}.  Both branches are evaluated and selected (no divergence, no
+// divisions); the series is one Horner fma per term.
 __device__ __forceinline__ float one_minus_exp_neg(float s) {
   const float big = 1.0f - fast_exp2(-s * kLog2e);
-  // s (1 - s/2 (1 - s/3 (1 - s/4 (... (1 - s/9)))))
-  float t = 1.0f - s * (1.0f / 9.0f);
-  t = 1.0f - s * (1.0f / 8.0f) * t;
-  t = 1.0f - s * (1.0f / 7.0f) * t;
-  t = 1.0f - s * (1.0f / 6.0f) * t;
-  t = 1.0f - s * (1.0f / 5.0f) * t;
-  t = 1.0f - s * (1.0f / 4.0f) * t;
-  t = 1.0f - s * (1.0f / 3.0f) * t;
-  t = 1.0f - s * 0.5f * t;
+  const float z = -s;
+  float t = 1.0f / 5040.0f;
+  t = fmaf(t, z, 1.0f / 720.0f);
+  t = fmaf(t, z, 1.0f / 120.0f);
+  t = fmaf(t, z, 1.0f / 24.0f);
+  t = fmaf(t, z, 1.0f / 6.0f);
+  t = fmaf(t, z, 0.5f);
+  t = fmaf(t, z, 1.0f);
   const float small = s * t;
-  return s > 0.5f ? big : small;
+  return s > 0.25f ? big : small;
+}
+
+// Sums over the two 32-lane halves of two values with one lane exchange:
+// lanes 0..31 get u(l) + u(l + 32), lanes 32..63 get v(l - 32) + v(l).
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second, leaving [u_lo | v_lo] and [u_hi | v_hi].
+__device__ __forceinline__ float half_sums_pair(float u, float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(u), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // v + v(lane ^ D) for a compile-time lane distance D: DPP for 1 and 2,

@@ -39,6 +39,9 @@ template <> struct Tr<float> {
 // large-tile kernel (the column-dependent choice is made once per column, so
 // the unrolled per-element code has no branches).
 struct EpiProj {
+  // its last tile column holds the 2N projection columns past the P of Delta:
+  // the direct-to-LDS kernel skips the blocks past them
+  static constexpr bool kSkipTail = true;
   EpiProjArgs e;
   __device__ __forceinline__ void operator()(int64_t row, int64_t col, float v, int) const {
     if (col < e.P) {

@@ -155,6 +155,12 @@ constexpr bool kHasBatchImpl<E, decltype(&E::template at_batch<16>, void())> = t
 template <class E>
 constexpr bool kHasBatch = kHasBatchImpl<E>;
 
+// Epilogues that opt into per-wave tail variants of the K loop (kSkipTail).
+template <class E, class = void>
+constexpr bool kSkipTailImpl = false;
+template <class E>
+constexpr bool kSkipTailImpl<E, std::void_t<decltype(E::kSkipTail)>> = E::kSkipTail;
+
 template <class Epi, bool a_kc, bool b_kc>
 __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_t K, const bf16_t* __restrict__ A,
                                                    int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
@@ -203,85 +209,195 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_
   for (int p = 0; p < NS - 1; p++)
     if (p < nsteps) issue(p);
 
-  // Operand fragments of one k sub-step: A blocks 0..3, B blocks 0..3.
-  struct Frags {
-    bf16x8_t a[4], b[4];
-  };
-  auto read_frags = [&](Frags& f, int64_t s, int q) {
-    const lds_char* st = lds + (s % NS) * kStageBytes;
+  if constexpr (!kSkipTailImpl<Epi>) {
+    // every wave runs the whole loop (the tail variants below cost the
+    // weight-gradient split-K kernel more in its schedule than they save)
+    // Operand fragments of one k sub-step: A blocks 0..3, B blocks 0..3.
+    struct Frags {
+      bf16x8_t a[4], b[4];
+    };
+    auto read_frags = [&](Frags& f, int64_t s, int q) {
+      const lds_char* st = lds + (s % NS) * kStageBytes;
 #pragma unroll
-    for (int i = 0; i < 4; i++) f.a[i] = oa.read(st, i, q);
+      for (int i = 0; i < 4; i++) f.a[i] = oa.read(st, i, q);
 #pragma unroll
-    for (int j = 0; j < 4; j++) f.b[j] = ob.read(st + kTileBytes, j, q);
-  };
+      for (int j = 0; j < 4; j++) f.b[j] = ob.read(st + kTileBytes, j, q);
+    };
 
-  // Stage s: multiply sub-step 0 (read one sub-step earlier) with the reads
-  // of sub-step 1's fragments spread between the MFMAs; then -- mid-stage --
-  // wait for stage s + 1's loads and
-  // pass the barrier: every wave's loads of stage s + 1 are then in LDS and
-  // every wave has finished reading stage s - 1, whose LDS the loads of stage
-  // s + NS - 1 refill.  Sub-step 1's MFMAs follow, with those loads (REFILL)
-  // and the reads of stage s + 1's sub-step 0 fragments spread between them,
-  // where the wave has issue slots to spare.  Every MFMA's operands were read
-  // 16 MFMAs earlier.  At the mid-stage wait the loads issued after stage
-  // s + 1's are those of stages s + 2 .. s + NS - 2 that exist.
-  // Scheduling barriers keep this issue order (left alone, the scheduler
-  // sinks the fragment reads next to their MFMAs and waits on each).
-  Frags f0, f1;
-  auto stage = [&](int64_t s, auto refill_tag, auto next_tag) {
-    constexpr bool REFILL = decltype(refill_tag)::value;  // load stage s + NS - 1
-    constexpr bool NEXT = decltype(next_tag)::value;      // stage s + 1 exists
-    const lds_char* st0 = lds + (s % NS) * kStageBytes;
+    // Stage s: multiply sub-step 0 (read one sub-step earlier) with the reads
+    // of sub-step 1's fragments spread between the MFMAs; then -- mid-stage --
+    // wait for stage s + 1's loads and
+    // pass the barrier: every wave's loads of stage s + 1 are then in LDS and
+    // every wave has finished reading stage s - 1, whose LDS the loads of stage
+    // s + NS - 1 refill.  Sub-step 1's MFMAs follow, with those loads (REFILL)
+    // and the reads of stage s + 1's sub-step 0 fragments spread between them,
+    // where the wave has issue slots to spare.  Every MFMA's operands were read
+    // 16 MFMAs earlier.  At the mid-stage wait the loads issued after stage
+    // s + 1's are those of stages s + 2 .. s + NS - 2 that exist.
+    // Scheduling barriers keep this issue order (left alone, the scheduler
+    // sinks the fragment reads next to their MFMAs and waits on each).
+    Frags f0, f1;
+    auto stage = [&](int64_t s, auto refill_tag, auto next_tag) {
+      constexpr bool REFILL = decltype(refill_tag)::value;  // load stage s + NS - 1
+      constexpr bool NEXT = decltype(next_tag)::value;      // stage s + 1 exists
+      const lds_char* st0 = lds + (s % NS) * kStageBytes;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+      for (int i = 0; i < 4; i++) {
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.a[i], f0.b[j], acc[i][j], 0, 0, 0);
-      f1.a[i] = oa.read(st0, i, 1);
-      f1.b[i] = ob.read(st0 + kTileBytes, i, 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (NEXT) {
-      // stages issued after s + 1: up to s + NS - 2 (this stage's refill comes later)
-      const int64_t last = (s + NS - 2 < nsteps - 1) ? s + NS - 2 : nsteps - 1;
-      wait_stages<kLoadsPerWave>(last - (s + 1));
-      barrier();
-    }
-    const int64_t kn = kbeg + (s + NS - 1) * kBK;
-    const uint32_t stn = lds_base + static_cast<uint32_t>(((s + NS - 1) % NS) * kStageBytes);
-    const lds_char* st1 = lds + ((s + 1) % NS) * kStageBytes;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.a[i], f1.b[j], acc[i][j], 0, 0, 0);
-        if constexpr (REFILL) {
-          if (j == 0) oa.issue_one(stn, kn, wave, i);
-          if (j == 2) ob.issue_one(stn + kTileBytes, kn, wave, i);
-        }
+        for (int j = 0; j < 4; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.a[i], f0.b[j], acc[i][j], 0, 0, 0);
+        f1.a[i] = oa.read(st0, i, 1);
+        f1.b[i] = ob.read(st0 + kTileBytes, i, 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (NEXT) {
-        f0.a[i] = oa.read(st1, i, 0);
-        f0.b[i] = ob.read(st1 + kTileBytes, i, 0);
+        // stages issued after s + 1: up to s + NS - 2 (this stage's refill comes later)
+        const int64_t last = (s + NS - 2 < nsteps - 1) ? s + NS - 2 : nsteps - 1;
+        wait_stages<kLoadsPerWave>(last - (s + 1));
+        barrier();
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
+      const int64_t kn = kbeg + (s + NS - 1) * kBK;
+      const uint32_t stn = lds_base + static_cast<uint32_t>(((s + NS - 1) % NS) * kStageBytes);
+      const lds_char* st1 = lds + ((s + 1) % NS) * kStageBytes;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.a[i], f1.b[j], acc[i][j], 0, 0, 0);
+          if constexpr (REFILL) {
+            if (j == 0) oa.issue_one(stn, kn, wave, i);
+            if (j == 2) ob.issue_one(stn + kTileBytes, kn, wave, i);
+          }
+        }
+        if constexpr (NEXT) {
+          f0.a[i] = oa.read(st1, i, 0);
+          f0.b[i] = ob.read(st1 + kTileBytes, i, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
 
-  if (nsteps > 0) {
-    // stages 0 .. min(NS - 1, nsteps) - 1 were issued; stage 0 must be in
-    const int64_t issued = (nsteps < NS - 1) ? nsteps : NS - 1;
-    wait_stages<kLoadsPerWave>(issued - 1);
-    barrier();
-    read_frags(f0, 0, 0);
-    // Nothing pending in LGKM at the loop entry (scalar argument loads
-    // included), so the loop's waits count only its own in-order LDS reads.
-    __builtin_amdgcn_s_waitcnt(0xC07F);
+    if (nsteps > 0) {
+      // stages 0 .. min(NS - 1, nsteps) - 1 were issued; stage 0 must be in
+      const int64_t issued = (nsteps < NS - 1) ? nsteps : NS - 1;
+      wait_stages<kLoadsPerWave>(issued - 1);
+      barrier();
+      read_frags(f0, 0, 0);
+      // Nothing pending in LGKM at the loop entry (scalar argument loads
+      // included), so the loop's waits count only its own in-order LDS reads.
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+    }
+    int64_t s = 0;
+    for (; s + NS - 1 < nsteps; s++) stage(s, std::true_type{}, std::true_type{});
+    for (; s + 1 < nsteps; s++) stage(s, std::false_type{}, std::true_type{});
+    if (s < nsteps) stage(s, std::false_type{}, std::false_type{});
+  } else {
+    // The K loop, for a wave that multiplies its A blocks 0 .. NI-1 with its B
+    // blocks 0 .. NJ-1.  Blocks that lie wholly past the matrix edge (a tail
+    // tile: 2080 = 8 x 256 + 32 output columns leave one 32-wide block in the
+    // last tile column) are neither fetched from LDS nor multiplied; the wave
+    // still issues its share of the tile loads and meets every barrier.
+    auto kloop = [&](auto ni_tag, auto nj_tag) {
+      constexpr int NI = decltype(ni_tag)::value;
+      constexpr int NJ = decltype(nj_tag)::value;
+      // Operand fragments of one k sub-step: A blocks 0..3, B blocks 0..3.
+      struct Frags {
+        bf16x8_t a[4], b[4];
+      };
+      auto read_frags = [&](Frags& f, int64_t s, int q) {
+        const lds_char* st = lds + (s % NS) * kStageBytes;
+#pragma unroll
+        for (int i = 0; i < NI; i++) f.a[i] = oa.read(st, i, q);
+#pragma unroll
+        for (int j = 0; j < NJ; j++) f.b[j] = ob.read(st + kTileBytes, j, q);
+      };
+      // Stage s: multiply sub-step 0 (read one sub-step earlier) with the reads
+      // of sub-step 1's fragments spread between the MFMAs; then -- mid-stage --
+      // wait for stage s + 1's loads and
+      // pass the barrier: every wave's loads of stage s + 1 are then in LDS and
+      // every wave has finished reading stage s - 1, whose LDS the loads of stage
+      // s + NS - 1 refill.  Sub-step 1's MFMAs follow, with those loads (REFILL)
+      // and the reads of stage s + 1's sub-step 0 fragments spread between them,
+      // where the wave has issue slots to spare.  Every MFMA's operands were read
+      // 16 MFMAs earlier.  At the mid-stage wait the loads issued after stage
+      // s + 1's are those of stages s + 2 .. s + NS - 2 that exist.
+      // Scheduling barriers keep this issue order (left alone, the scheduler
+      // sinks the fragment reads next to their MFMAs and waits on each).
+      Frags f0, f1;
+      auto stage = [&](int64_t s, auto refill_tag, auto next_tag) {
+        constexpr bool REFILL = decltype(refill_tag)::value;  // load stage s + NS - 1
+        constexpr bool NEXT = decltype(next_tag)::value;      // stage s + 1 exists
+        const lds_char* st0 = lds + (s % NS) * kStageBytes;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            if (i < NI && j < NJ)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.a[i], f0.b[j], acc[i][j], 0, 0, 0);
+          if (i < NI) f1.a[i] = oa.read(st0, i, 1);
+          if (i < NJ) f1.b[i] = ob.read(st0 + kTileBytes, i, 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (NEXT) {
+          // stages issued after s + 1: up to s + NS - 2 (this stage's refill comes later)
+          const int64_t last = (s + NS - 2 < nsteps - 1) ? s + NS - 2 : nsteps - 1;
+          wait_stages<kLoadsPerWave>(last - (s + 1));
+          barrier();
+        }
+        const int64_t kn = kbeg + (s + NS - 1) * kBK;
+        const uint32_t stn = lds_base + static_cast<uint32_t>(((s + NS - 1) % NS) * kStageBytes);
+        const lds_char* st1 = lds + ((s + 1) % NS) * kStageBytes;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            if (i < NI && j < NJ)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.a[i], f1.b[j], acc[i][j], 0, 0, 0);
+            if constexpr (REFILL) {
+              if (j == 0) oa.issue_one(stn, kn, wave, i);
+              if (j == 2) ob.issue_one(stn + kTileBytes, kn, wave, i);
+            }
+          }
+          if constexpr (NEXT) {
+            if (i < NI) f0.a[i] = oa.read(st1, i, 0);
+            if (i < NJ) f0.b[i] = ob.read(st1 + kTileBytes, i, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+
+      if (nsteps > 0) {
+        // stages 0 .. min(NS - 1, nsteps) - 1 were issued; stage 0 must be in
+        const int64_t issued = (nsteps < NS - 1) ? nsteps : NS - 1;
+        wait_stages<kLoadsPerWave>(issued - 1);
+        barrier();
+        read_frags(f0, 0, 0);
+        // Nothing pending in LGKM at the loop entry (scalar argument loads
+        // included), so the loop's waits count only its own in-order LDS reads.
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+      }
+      int64_t s = 0;
+      for (; s + NS - 1 < nsteps; s++) stage(s, std::true_type{}, std::true_type{});
+      for (; s + 1 < nsteps; s++) stage(s, std::false_type{}, std::true_type{});
+      if (s < nsteps) stage(s, std::false_type{}, std::false_type{});
+    };
+    // Blocks of 32 rows (A) and columns (B) of this wave that hold output:
+    // 4 inside the matrix, 0 .. 3 at a tail; 2 and 3 run the full loop.
+    auto nblk = [](int64_t left) -> int { return left >= 128 ? 4 : left <= 0 ? 0 : left <= 32 ? 1 : 4; };
+    const int bi = nblk(M - (m0 + wm * 128)), bj = nblk(Nc - (n0 + wn * 128));
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I4 = std::integral_constant<int, 4>;
+    if (bi == 4) {
+      if (bj == 4) kloop(I4{}, I4{});
+      else if (bj == 1) kloop(I4{}, I1{});
+      else kloop(I4{}, I0{});
+    } else if (bi == 1) {
+      kloop(I1{}, I4{});
+    } else {
+      kloop(I0{}, I4{});
+    }
   }
-  int64_t s = 0;
-  for (; s + NS - 1 < nsteps; s++) stage(s, std::true_type{}, std::true_type{});
-  for (; s + 1 < nsteps; s++) stage(s, std::false_type{}, std::true_type{});
-  if (s < nsteps) stage(s, std::false_type{}, std::false_type{});
 
   // Epilogue.  Lane l holds, in acc[i][j][r], row m0 + 128 wm + 32 i +
   // 8 (r / 4) + 4 (l / 32) + r % 4 of column n0 + 128 wn + 32 j + l % 32.  The

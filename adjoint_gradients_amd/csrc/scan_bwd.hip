@@ -403,12 +403,28 @@ __global__ __launch_bounds__(256) void k_bwd_carry(int64_t K, int64_t P, int64_t
   const int64_t p = e / N;
   const float al2 = alpha[e] * kLog2e;
   float cin = 0.0f;
-#pragma unroll 8
-  for (int64_t k = K - 1; k >= 0; k--) {
+  // Blocks of 8 chunks: all loads of a block are issued before its stores
+  // (umu may alias carry, so the compiler would not move a load above an
+  // earlier store by itself).
+  constexpr int B = 8;
+  int64_t k = K - 1;
+  for (; k >= B - 1; k -= B) {
+    float u[B], sk[B];
+#pragma unroll
+    for (int r = 0; r < B; r++) {
+      u[r] = umu[(k - r) * PN + e];
+      sk[r] = static_cast<float>(ssum[(k - r) * P + p]);
+    }
+#pragma unroll
+    for (int r = 0; r < B; r++) {
+      carry[(k - r) * PN + e] = cin;
+      cin = fmaf(fast_exp2(-sk[r] * al2), cin, u[r]);
+    }
+  }
+  for (; k >= 0; k--) {
     const float u = umu[k * PN + e];
     carry[k * PN + e] = cin;
-    const float A = fast_exp2(-static_cast<float>(ssum[k * P + p]) * al2);
-    cin = fmaf(A, cin, u);
+    cin = fmaf(fast_exp2(-static_cast<float>(ssum[k * P + p]) * al2), cin, u);
   }
 }
 
@@ -425,27 +441,36 @@ __global__ __launch_bounds__(256) void k_bwd_carry(int64_t K, int64_t P, int64_t
 // k_bwd_carry then turns into carries in place).  Lanes of state 0 also write
 // the fp64 sum of s over the W tokens that follow each chunk, for the main
 // kernel.
+constexpr int64_t kComposeSpan = 32;  // chunks per thread of k_bwd_window_compose (at least)
+
 __global__ __launch_bounds__(256) void k_bwd_window_compose(int64_t K, int64_t P, int64_t N, int64_t q,
+                                                            int64_t span,
                                                             const float* __restrict__ alpha,
                                                             const double* __restrict__ ps64,
                                                             const float* __restrict__ umu,
                                                             float* __restrict__ out,
                                                             double* __restrict__ hwin) {
   const int64_t PN = P * N;
-  const int64_t e = static_cast<int64_t>(blockIdx.y) * blockDim.x + threadIdx.x;
-  const int64_t k = blockIdx.x;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= PN) return;
   const int64_t p = e / N;
-  float u = umu[k * PN + e];
-  if (k + q < K) {
-    const float Ew = static_cast<float>(ps64[(k + q) * P + p] - ps64[k * P + p]);
-    u = fmaf(-fast_exp2(-Ew * (alpha[e] * kLog2e)), umu[(k + q) * PN + e], u);
-  }
-  out[k * PN + e] = u;
-  if (e - p * N == 0) {
-    const int64_t kb = (k + q + 1 < K) ? k + q + 1 : K;
-    const int64_t ka = (k + 1 < K) ? k + 1 : K;
-    hwin[k * P + p] = ps64[kb * P + p] - ps64[ka * P + p];
+  const bool first_state = (e - p * N) == 0;
+  const float al2 = alpha[e] * kLog2e;
+  const int64_t k0 = static_cast<int64_t>(blockIdx.y) * span;
+  const int64_t k1 = (k0 + span < K) ? k0 + span : K;
+#pragma unroll 4
+  for (int64_t k = k0; k < k1; k++) {
+    float u = umu[k * PN + e];
+    if (k + q < K) {
+      const float Ew = static_cast<float>(ps64[(k + q) * P + p] - ps64[k * P + p]);
+      u = fmaf(-fast_exp2(-Ew * al2), umu[(k + q) * PN + e], u);
+    }
+    out[k * PN + e] = u;
+    if (first_state) {
+      const int64_t kb = (k + q + 1 < K) ? k + q + 1 : K;
+      const int64_t ka = (k + 1 < K) ? k + 1 : K;
+      hwin[k * P + p] = ps64[kb * P + p] - ps64[ka * P + p];
+    }
   }
 }
 
@@ -592,8 +617,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   a.marks.rec(1, st);
   const int64_t PN = a.P * a.N;
   if (compose) {
-    k_bwd_window_compose<<<dim3(static_cast<unsigned>(K), static_cast<unsigned>((PN + 255) / 256)), 256, 0, st>>>(
-        K, a.P, a.N, a.W / a.C, a.alpha, a.ps64, a.umu, a.carry, a.hwin);
+    int64_t span = (K + 65534) / 65535;  // grid y stays within its limit
+    if (span < kComposeSpan) span = kComposeSpan;
+    k_bwd_window_compose<<<dim3(static_cast<unsigned>((PN + 255) / 256), static_cast<unsigned>((K + span - 1) / span)),
+                           256, 0, st>>>(K, a.P, a.N, a.W / a.C, span, a.alpha, a.ps64, a.umu, a.carry, a.hwin);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   k_bwd_carry<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, a.alpha, a.ssum,

@@ -222,50 +222,69 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
   float* hsg = (FINAL && hsub && cb < NB) ? hsub + hsub_offset(k, cb, 0, NB, nsub_max, NL) + lane : nullptr;
   static_assert(D % kSub == 0, "ring length a multiple of the sub-chunk");
   double ss = 0.0;
-  for (int q8 = 0; q8 < len; q8 += D) {
+  // One token of the walk; `ahead` is the token whose s and x the ring
+  // fetches now (D - 1 tokens on).
+  auto token = [&](int r, int tau, bool fetch, int64_t ahead) {
+    if (FINAL && r % kSub == 0 && hsg) {
 #pragma unroll
-    for (int r = 0; r < D; r++) {
-      const int tau = q8 + r;
-      if (tau < len) {
-        if (FINAL && r % kSub == 0 && hsg) {
+      for (int j = 0; j < NL; j++) hsg[(tau / kSub * NL + j) * 64] = h[j];
+    }
+    if (fetch) ld((r + D - 1) % D, ahead);
+    const float ns = -rs[r];
+    const float xv = raw_to_f32(rx[r]);
+    const float* rb = rows + tau * NN + n0;
+    float bt[NL];
 #pragma unroll
-          for (int j = 0; j < NL; j++) hsg[(tau / kSub * NL + j) * 64] = h[j];
+    for (int j = 0; j < NL; j += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(rb + j);
+      bt[j] = v.x; bt[j + 1] = v.y; bt[j + 2] = v.z; bt[j + 3] = v.w;
+    }
+    if constexpr (FINAL) {
+      const float* rc = rows + static_cast<size_t>(C) * NN + tau * NN + n0;
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NL; j += 4) {
+        const float4 cv = *reinterpret_cast<const float4*>(rc + j);
+        const float cq[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const float a = fast_exp2(ns * al2[j + jj]);
+          h[j + jj] = fmaf(a, h[j + jj], bt[j + jj] * xv);
+          acc = fmaf(cq[jj], h[j + jj], acc);
         }
-        if (tau + D - 1 < len) ld((r + D - 1) % D, t0 + tau + D - 1);
-        const float ns = -rs[r];
-        const float xv = raw_to_f32(rx[r]);
-        const float* rb = rows + tau * NN + n0;
-        float bt[NL];
+      }
+      acc = group_sum<G, CH>(acc);
+      if (valid && grp == 0)
+        *reinterpret_cast<float*>(reinterpret_cast<char*>(y + (t0 + tau) * P) + ob4) = acc;
+    } else {
 #pragma unroll
-        for (int j = 0; j < NL; j += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(rb + j);
-          bt[j] = v.x; bt[j + 1] = v.y; bt[j + 2] = v.z; bt[j + 3] = v.w;
-        }
-        if constexpr (FINAL) {
-          const float* rc = rows + static_cast<size_t>(C) * NN + tau * NN + n0;
-          float acc = 0.0f;
+      for (int j = 0; j < NL; j++) {
+        const float a = fast_exp2(ns * al2[j]);
+        h[j] = fmaf(a, h[j], bt[j] * xv);
+      }
+      ss -= static_cast<double>(ns);
+    }
+  };
+  if (!FINAL && len % D == 0) {
+    // whole ring turns: no per-token bounds branches (the fetches past the
+    // chunk end re-read its last token), so the state stays in place rather
+    // than being copied back at every token.  (The final pass keeps the
+    // checked loop: its per-token branches remain for the y and sub-chunk
+    // state stores, and there the checked form addresses its loads better.)
+    for (int q8 = 0; q8 < len; q8 += D) {
 #pragma unroll
-          for (int j = 0; j < NL; j += 4) {
-            const float4 cv = *reinterpret_cast<const float4*>(rc + j);
-            const float cq[4] = {cv.x, cv.y, cv.z, cv.w};
+      for (int r = 0; r < D; r++) {
+        const int tau = q8 + r;
+        const int ahead = (tau + D - 1 < len) ? tau + D - 1 : len - 1;
+        token(r, tau, true, t0 + ahead);
+      }
+    }
+  } else {
+    for (int q8 = 0; q8 < len; q8 += D) {
 #pragma unroll
-            for (int jj = 0; jj < 4; jj++) {
-              const float a = fast_exp2(ns * al2[j + jj]);
-              h[j + jj] = fmaf(a, h[j + jj], bt[j + jj] * xv);
-              acc = fmaf(cq[jj], h[j + jj], acc);
-            }
-          }
-          acc = group_sum<G, CH>(acc);
-          if (valid && grp == 0)
-            *reinterpret_cast<float*>(reinterpret_cast<char*>(y + (t0 + tau) * P) + ob4) = acc;
-        } else {
-#pragma unroll
-          for (int j = 0; j < NL; j++) {
-            const float a = fast_exp2(ns * al2[j]);
-            h[j] = fmaf(a, h[j], bt[j] * xv);
-          }
-          ss -= static_cast<double>(ns);
-        }
+      for (int r = 0; r < D; r++) {
+        const int tau = q8 + r;
+        if (tau < len) token(r, tau, tau + D - 1 < len, t0 + tau + D - 1);
       }
     }
   }

@@ -24,6 +24,12 @@ struct Tok {
   float s, x, g, sm, gm;
 };
 
+// Fourth word of a raw buffer resource on gfx9 parts (offsets in bytes,
+// range-checked against the record count: an access at or past it is
+// dropped for stores), and an offset past any row this kernel stores into.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kBufOutside = 0x7ffffff0;
+
 typedef __attribute__((address_space(3))) char lds_byte;
 
 // LDS byte address of a pointer into the kernel's dynamic LDS.
@@ -126,8 +132,9 @@ struct RevState {
 template <typename IO, int NL, int G, bool WIN>
 __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, const Tok& tk, const float (&bt)[NL],
                                           const float (&ct)[NL], const float (&cm)[NL], const float (&hp)[NL],
-                                          const float (&hc)[NL], int64_t i, uint32_t off, bool valid, int grp,
-                                          int pl, int lane, float* red, int rd_off, float* xw_tau) {
+                                          const float (&hc)[NL], int64_t i, bool live, uint32_t off, bool valid, int grp,
+                                          int pl, int lane, float* red, int rd_off, int voff_dy, int voff_dx,
+                                          float* dxb, float* xw_tau) {
   constexpr int CH = 64 / G;
   constexpr int NN = NL * G;
   constexpr int OUT = 2 * NN;
@@ -138,17 +145,21 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
     mu[j] = fmaf(tk.g, ct[j], st.inc[j]);
   }
   if constexpr (WIN) {
-    if (i + a.W < a.T) {  // uniform: the partner token i + W exists
-      // drop the token leaving the window: - g_{i+W} c_{i+W} prod_{j=i+1}^{i+W} a_j
-      const float E = static_cast<float>(st.E64);
+    // drop the token leaving the window: - g_{i+W} c_{i+W} prod_{j=i+1}^{i+W} a_j.
+    // Where the partner token i + W lies past the sequence end there is no
+    // such term: its g and s are taken as zero (a select, not a branch, so
+    // the token's code stays one block).
+    const bool part = i + a.W < a.T;
+    const float gm = part ? tk.gm : 0.0f;
+    const float sm = part ? tk.sm : 0.0f;
+    const float E = static_cast<float>(st.E64);
 #pragma unroll
-      for (int j = 0; j < NL; j++) {
-        const float D = fast_exp2(-E * st.al2[j]);
-        mu[j] = fmaf(-tk.gm * cm[j], D, mu[j]);
-      }
-      st.E64 -= static_cast<double>(tk.sm);  // token i + W leaves the window of token i - 1
+    for (int j = 0; j < NL; j++) {
+      const float D = fast_exp2(-E * st.al2[j]);
+      mu[j] = fmaf(-gm * cm[j], D, mu[j]);
     }
-    st.E64 += static_cast<double>(tk.s);  // token i enters it
+    // token i + W leaves the window of token i - 1, token i enters it
+    st.E64 += static_cast<double>(tk.s) - static_cast<double>(sm);
   }
   float ds = 0.0f, dxd = 0.0f;
 #pragma unroll
@@ -170,9 +181,22 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
     dxd = group_sum<G, CH>(dxd);
   }
   const float dD = -(ds * (1.0f / kLog2e)) * one_minus_exp_neg(tk.s);
-  if (valid) {
-    if (grp == 0) store_io(row_ptr(static_cast<IO*>(a.dY), i, a.ldy) + off, dD);
-    if (a.dxdir && grp == (G == 2 ? 1 : 0)) row_ptr(a.dxdir, i, a.P)[off] = dxd;
+  // Stores through buffer resources over token i's rows: lanes that store
+  // nothing carry an offset past the row, and the hardware drops such a
+  // store, so no lane mask (and no branch) splits the token's code.
+  // A token past the chunk end (live false) gets empty resources: its row
+  // may lie past the arrays, and nothing of it is stored.
+  {
+    IO* yrow = row_ptr(static_cast<IO*>(a.dY), i, a.ldy);
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc(yrow, 0, live ? static_cast<int>(a.P * sizeof(IO)) : 0, kBufWord3);
+    if constexpr (sizeof(IO) == 2)
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, f32_to_bf16(dD)), ry, voff_dy, 0, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dD), ry, voff_dy, 0, 0);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        row_ptr(dxb, i, a.P), 0, (live && a.dxdir) ? static_cast<int>(a.P * 4) : 0, kBufWord3);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dxd), rx, voff_dx, 0, 0);
   }
   st.dbias += dD;
   // channel sums of db = mu x and dc = g h through an LDS transpose (placement
@@ -266,6 +290,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   // this lane's read position in the transpose buffer (swizzled layout),
   // fixed for the whole kernel
   const int rd_off = redl::Layout<NL, G>::kSwz ? redl::Layout<NL, G>::chunk(lane >> 1, 4 * (lane & 1)) : 0;
+  // byte offsets of this lane's dDelta and dx_dir stores within a token row;
+  // lanes that store nothing get an offset past every row (dropped store).
+  // dDelta comes from lane group 0; dx_dir from group 1 with two groups (the
+  // paired group sum leaves it there), else from group 0.
+  const int voff_dy = (valid && grp == 0) ? static_cast<int>(off * sizeof(IO)) : kBufOutside;
+  const int voff_dx = (valid && grp == (G == 2 ? 1 : 0)) ? static_cast<int>(off * 4) : kBufOutside;
+  // base of the dx_dir rows (any valid pointer when there is no dx_dir: its
+  // resources are then empty)
+  float* const dxb = a.dxdir ? a.dxdir : static_cast<float*>(a.dY);
   float* xw = lds + 2 * STG + kWpb * RED;  // [kWpb][S][OUT]
   float* hsg = a.hsub + hsub_offset(k, wave_live ? cb : 0, 0, NB, nsub_max, NL);
   const IO* xp = static_cast<const IO*>(a.x);
@@ -328,17 +361,23 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
     } else {
 #pragma unroll
       for (int i = 0; i < SPL; i++) {
-        int64_t t = ta + G * i + grp;
-        if (t >= t1) t = t1 - 1;  // past the chunk end: staged, never read
+        const int64_t t = ta + G * i + grp;
         const uint32_t d = dst + 4u * (G * i * CH);
-        dma_v(a.s + t * P + pc, d);
-        dma_v(xp + t * P + pc, d + 4u * SQ);
-        dma_v(a.g + t * P + pc, d + 8u * SQ);
-        if constexpr (WIN) {
-          const int64_t m = t + a.W;
-          const int64_t mm = m < T ? m : t;
-          dma_v(a.s + mm * P + pc, d + 12u * SQ);
-          dma_v(a.g + mm * P + pc, d + 16u * SQ);
+        if (t < t1) {
+          dma_v(a.s + t * P + pc, d);
+          dma_v(xp + t * P + pc, d + 4u * SQ);
+          dma_v(a.g + t * P + pc, d + 8u * SQ);
+          if constexpr (WIN) {
+            const int64_t m = t + a.W;
+            const int64_t mm = m < T ? m : t;
+            dma_v(a.s + mm * P + pc, d + 12u * SQ);
+            dma_v(a.g + mm * P + pc, d + 16u * SQ);
+          }
+        } else {
+          // past the chunk end: zeros (the walk then passes the token by)
+          float* z = sc0 + (u & 1) * (NQS * SQ) + G * i * CH + lane;
+#pragma unroll
+          for (int q = 0; q < NQS; q++) z[q * SQ] = 0.0f;
         }
       }
     }
@@ -439,96 +478,57 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         for (int j = 0; j < NL; j++) hn[j] = wave_live ? hsg[((u - 1) * NL + j) * 64 + lane] : 0.0f;
       }
     };
+    // A partial sub-chunk (the end of a ragged chunk) runs the same code:
+    // its tokens past the chunk end were staged as zeros (s = x = g = 0 and
+    // no partner), so they leave the states and the adjoint unchanged, add
+    // nothing to any sum, and their stores are dropped.
     float hr[S][NL];
-    if (len == S) {
-      // recompute the sub-chunk's states
-      {
-        float hh[NL];
+    // recompute the sub-chunk's states
+    {
+      float hh[NL];
 #pragma unroll
-        for (int j = 0; j < NL; j++) hh[j] = hs[j];
-        float cs = scal(0, 0), cx = scal_x(0);
+      for (int j = 0; j < NL; j++) hh[j] = hs[j];
+      float cs = scal(0, 0), cx = scal_x(0);
 #pragma unroll
-        for (int tau = 0; tau < S; tau++) {
-          token_fence();
-          const float ns = -cs;
-          const float xv = cx;
-          if (tau + 1 < S) {
-            cs = scal(0, tau + 1);
-            cx = scal_x(tau + 1);
-          }
-          float bt[NL];
-          lds_row<NL>(sb + tau * NN + n0, bt);
-#pragma unroll
-          for (int j = 0; j < NL; j++) {
-            hh[j] = fmaf(fast_exp2(ns * st.al2[j]), hh[j], bt[j] * xv);
-            hr[tau][j] = hh[j];
-          }
-        }
-      }
-      prefetch();
-      // reverse walk
-      Tok cur = read_tok(S - 1);
-#pragma unroll
-      for (int tau = S - 1; tau >= 0; tau--) {
+      for (int tau = 0; tau < S; tau++) {
         token_fence();
-        Tok nxt = cur;
-        if (tau > 0) nxt = read_tok(tau - 1);
-        float bt[NL], ct[NL], cm[NL];
+        const float ns = -cs;
+        const float xv = cx;
+        if (tau + 1 < S) {
+          cs = scal(0, tau + 1);
+          cx = scal_x(tau + 1);
+        }
+        float bt[NL];
         lds_row<NL>(sb + tau * NN + n0, bt);
-        lds_row<NL>(sb + S * NN + tau * NN + n0, ct);
-        if constexpr (WIN) lds_row<NL>(sb + 2 * S * NN + tau * NN + n0, cm);
-        else {
 #pragma unroll
-          for (int j = 0; j < NL; j++) cm[j] = 0.0f;
-        }
-        float hp[NL];
-#pragma unroll
-        for (int j = 0; j < NL; j++) hp[j] = (tau > 0) ? hr[tau > 0 ? tau - 1 : 0][j] : hs[j];
-        rev_token<IO, NL, G, WIN>(st, a, cur, bt, ct, cm, hp, hr[tau], ta + tau, off, valid, grp, pl, lane, red,
-                                  rd_off, xw + (w * S + tau) * OUT);
-        cur = nxt;
-      }
-    } else {
-      // partial sub-chunk (end of a ragged chunk)
-      {
-        float hh[NL];
-#pragma unroll
-        for (int j = 0; j < NL; j++) hh[j] = hs[j];
-#pragma unroll
-        for (int tau = 0; tau < S; tau++) {
-          if (tau < len) {
-            const float ns = -scal(0, tau);
-            const float xv = scal_x(tau);
-            float bt[NL];
-            lds_row<NL>(sb + tau * NN + n0, bt);
-#pragma unroll
-            for (int j = 0; j < NL; j++) {
-              hh[j] = fmaf(fast_exp2(ns * st.al2[j]), hh[j], bt[j] * xv);
-              hr[tau][j] = hh[j];
-            }
-          }
+        for (int j = 0; j < NL; j++) {
+          hh[j] = fmaf(fast_exp2(ns * st.al2[j]), hh[j], bt[j] * xv);
+          hr[tau][j] = hh[j];
         }
       }
-      prefetch();
+    }
+    prefetch();
+    // reverse walk
+    Tok cur = read_tok(S - 1);
 #pragma unroll
-      for (int tau = S - 1; tau >= 0; tau--) {
-        if (tau < len) {
-          const Tok tk = read_tok(tau);
-          float bt[NL], ct[NL], cm[NL];
-          lds_row<NL>(sb + tau * NN + n0, bt);
-          lds_row<NL>(sb + S * NN + tau * NN + n0, ct);
-          if constexpr (WIN) lds_row<NL>(sb + 2 * S * NN + tau * NN + n0, cm);
-          else {
+    for (int tau = S - 1; tau >= 0; tau--) {
+      token_fence();
+      Tok nxt = cur;
+      if (tau > 0) nxt = read_tok(tau - 1);
+      float bt[NL], ct[NL], cm[NL];
+      lds_row<NL>(sb + tau * NN + n0, bt);
+      lds_row<NL>(sb + S * NN + tau * NN + n0, ct);
+      if constexpr (WIN) lds_row<NL>(sb + 2 * S * NN + tau * NN + n0, cm);
+      else {
 #pragma unroll
-            for (int j = 0; j < NL; j++) cm[j] = 0.0f;
-          }
-          float hp[NL];
-#pragma unroll
-          for (int j = 0; j < NL; j++) hp[j] = (tau > 0) ? hr[tau > 0 ? tau - 1 : 0][j] : hs[j];
-          rev_token<IO, NL, G, WIN>(st, a, tk, bt, ct, cm, hp, hr[tau], ta + tau, off, valid, grp, pl, lane, red,
-                                    rd_off, xw + (w * S + tau) * OUT);
-        }
+        for (int j = 0; j < NL; j++) cm[j] = 0.0f;
       }
+      float hp[NL];
+#pragma unroll
+      for (int j = 0; j < NL; j++) hp[j] = (tau > 0) ? hr[tau > 0 ? tau - 1 : 0][j] : hs[j];
+      rev_token<IO, NL, G, WIN>(st, a, cur, bt, ct, cm, hp, hr[tau], ta + tau, tau < len, off, valid, grp, pl, lane,
+                                red, rd_off, voff_dy, voff_dx, dxb, xw + (w * S + tau) * OUT);
+      cur = nxt;
     }
     wait_vm_all();
     __syncthreads();  // staged data of u - 1 visible; token sums complete

@@ -132,9 +132,9 @@ struct RevState {
 template <typename IO, int NL, int G, bool WIN>
 __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, const Tok& tk, const float (&bt)[NL],
                                           const float (&ct)[NL], const float (&cm)[NL], const float (&hp)[NL],
-                                          const float (&hc)[NL], int64_t i, bool live, uint32_t off, bool valid, int grp,
-                                          int pl, int lane, float* red, int rd_off, int voff_dy, int voff_dx,
-                                          float* dxb, float* xw_tau) {
+                                          const float (&hc)[NL], char* yrow, char* xrow, bool live, bool part,
+                                          bool valid, int grp, int pl, int lane, float* red, int rd_off,
+                                          int voff_dy, int voff_dx, float* xw_tau) {
   constexpr int CH = 64 / G;
   constexpr int NN = NL * G;
   constexpr int OUT = 2 * NN;
@@ -149,7 +149,6 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
     // Where the partner token i + W lies past the sequence end there is no
     // such term: its g and s are taken as zero (a select, not a branch, so
     // the token's code stays one block).
-    const bool part = i + a.W < a.T;
     const float gm = part ? tk.gm : 0.0f;
     const float sm = part ? tk.sm : 0.0f;
     const float E = static_cast<float>(st.E64);
@@ -187,15 +186,14 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
   // A token past the chunk end (live false) gets empty resources: its row
   // may lie past the arrays, and nothing of it is stored.
   {
-    IO* yrow = row_ptr(static_cast<IO*>(a.dY), i, a.ldy);
     const __amdgpu_buffer_rsrc_t ry =
         __builtin_amdgcn_make_buffer_rsrc(yrow, 0, live ? static_cast<int>(a.P * sizeof(IO)) : 0, kBufWord3);
     if constexpr (sizeof(IO) == 2)
       __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, f32_to_bf16(dD)), ry, voff_dy, 0, 0);
     else
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dD), ry, voff_dy, 0, 0);
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        row_ptr(dxb, i, a.P), 0, (live && a.dxdir) ? static_cast<int>(a.P * 4) : 0, kBufWord3);
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(xrow, 0, (live && a.dxdir) ? static_cast<int>(a.P * 4) : 0, kBufWord3);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dxd), rx, voff_dx, 0, 0);
   }
   st.dbias += dD;
@@ -299,6 +297,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   // base of the dx_dir rows (any valid pointer when there is no dx_dir: its
   // resources are then empty)
   float* const dxb = a.dxdir ? a.dxdir : static_cast<float*>(a.dY);
+  const int64_t ldy_b = a.ldy * static_cast<int64_t>(sizeof(IO)), ldx_b = P * 4;
   float* xw = lds + 2 * STG + kWpb * RED;  // [kWpb][S][OUT]
   float* hsg = a.hsub + hsub_offset(k, wave_live ? cb : 0, 0, NB, nsub_max, NL);
   const IO* xp = static_cast<const IO*>(a.x);
@@ -453,6 +452,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
 
   // ---------------- phase 2: sub-chunks right to left
   float hs[NL], hn[NL];  // start states of the current and of the next sub-chunk
+  // the last sub-chunk's start state, loaded as the walk's prefetches load
+  // the others (one code path at the loop head: a load on one path only
+  // would make the compiler drain every load in flight where the paths meet)
+#pragma unroll
+  for (int j = 0; j < NL; j++) hn[j] = hsg[((nsub - 1) * NL + j) * 64 + lane];
   for (int u = nsub - 1; u >= 0; u--) {
     const int buf = u & 1;
     const float* sb = lds + buf * STG;  // b rows [S][NN], then c rows, then partner c rows
@@ -462,20 +466,21 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
     // A wavefront past the last channel block has no states of its own; it
     // starts from zero (it must not read another wavefront's, which a
     // different workgroup may still be writing) and contributes zeros.
-    if (u == nsub - 1) {
 #pragma unroll
-      for (int j = 0; j < NL; j++) hs[j] = wave_live ? hsg[(u * NL + j) * 64 + lane] : 0.0f;
-    } else {
-#pragma unroll
-      for (int j = 0; j < NL; j++) hs[j] = hn[j];
-    }
+    for (int j = 0; j < NL; j++) hs[j] = wave_live ? hn[j] : 0.0f;
     // after the recompute: bring sub-chunk u - 1's data and start state
     auto prefetch = [&]() {
       if (u > 0) {
         dma_rows(u - 1);
         dma_scal(u - 1);
 #pragma unroll
-        for (int j = 0; j < NL; j++) hn[j] = wave_live ? hsg[((u - 1) * NL + j) * 64 + lane] : 0.0f;
+        for (int j = 0; j < NL; j++) {
+          // loaded by every wavefront (hsg is a valid address for all) and
+          // kept only by live ones, where the next sub-chunk starts: an
+          // unconditional load issued here, ahead of the walk, with nothing
+          // waiting for it until then
+          hn[j] = hsg[((u - 1) * NL + j) * 64 + lane];
+        }
       }
     };
     // A partial sub-chunk (the end of a ragged chunk) runs the same code:
@@ -488,18 +493,24 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
       float hh[NL];
 #pragma unroll
       for (int j = 0; j < NL; j++) hh[j] = hs[j];
+      // each token's LDS reads (s, x and the b row) are issued one token
+      // ahead, so their latency hides behind the previous token's arithmetic
       float cs = scal(0, 0), cx = scal_x(0);
+      float bn[NL];
+      lds_row<NL>(sb + n0, bn);
 #pragma unroll
       for (int tau = 0; tau < S; tau++) {
         token_fence();
         const float ns = -cs;
         const float xv = cx;
+        float bt[NL];
+#pragma unroll
+        for (int j = 0; j < NL; j++) bt[j] = bn[j];
         if (tau + 1 < S) {
           cs = scal(0, tau + 1);
           cx = scal_x(tau + 1);
+          lds_row<NL>(sb + (tau + 1) * NN + n0, bn);
         }
-        float bt[NL];
-        lds_row<NL>(sb + tau * NN + n0, bt);
 #pragma unroll
         for (int j = 0; j < NL; j++) {
           hh[j] = fmaf(fast_exp2(ns * st.al2[j]), hh[j], bt[j] * xv);
@@ -508,29 +519,62 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
       }
     }
     prefetch();
-    // reverse walk
+    // reverse walk; a token's per-lane values and its b, c (and partner c)
+    // rows are read from LDS one token ahead
+    struct Rows {
+      float b[NL], c[NL], m[NL];
+    };
+    auto read_rows = [&](int tau, Rows& r) {
+      lds_row<NL>(sb + tau * NN + n0, r.b);
+      lds_row<NL>(sb + S * NN + tau * NN + n0, r.c);
+      if constexpr (WIN) lds_row<NL>(sb + 2 * S * NN + tau * NN + n0, r.m);
+      else {
+#pragma unroll
+        for (int j = 0; j < NL; j++) r.m[j] = 0.0f;
+      }
+    };
     Tok cur = read_tok(S - 1);
+    Rows rcur;
+    read_rows(S - 1, rcur);
+    // rows of the token being walked (dDelta in dY, dx_dir), stepped down by
+    // one row per token; tokens tau < npart have their window partner inside
+    // the sequence
+    char* yrow = reinterpret_cast<char*>(static_cast<IO*>(a.dY) + (ta + S - 1) * a.ldy);
+    char* xrow = reinterpret_cast<char*>(dxb + (ta + S - 1) * P);
+    const int64_t np64 = T - a.W - ta;
+    const int npart = np64 < 0 ? 0 : np64 > S ? S : static_cast<int>(np64);
 #pragma unroll
     for (int tau = S - 1; tau >= 0; tau--) {
       token_fence();
       Tok nxt = cur;
-      if (tau > 0) nxt = read_tok(tau - 1);
+      Rows rnxt = rcur;
+      if (tau > 0) {
+        nxt = read_tok(tau - 1);
+        read_rows(tau - 1, rnxt);
+      }
       float bt[NL], ct[NL], cm[NL];
-      lds_row<NL>(sb + tau * NN + n0, bt);
-      lds_row<NL>(sb + S * NN + tau * NN + n0, ct);
-      if constexpr (WIN) lds_row<NL>(sb + 2 * S * NN + tau * NN + n0, cm);
-      else {
 #pragma unroll
-        for (int j = 0; j < NL; j++) cm[j] = 0.0f;
+      for (int j = 0; j < NL; j++) {
+        bt[j] = rcur.b[j];
+        ct[j] = rcur.c[j];
+        cm[j] = rcur.m[j];
       }
       float hp[NL];
 #pragma unroll
       for (int j = 0; j < NL; j++) hp[j] = (tau > 0) ? hr[tau > 0 ? tau - 1 : 0][j] : hs[j];
-      rev_token<IO, NL, G, WIN>(st, a, cur, bt, ct, cm, hp, hr[tau], ta + tau, tau < len, off, valid, grp, pl, lane,
-                                red, rd_off, voff_dy, voff_dx, dxb, xw + (w * S + tau) * OUT);
+      rev_token<IO, NL, G, WIN>(st, a, cur, bt, ct, cm, hp, hr[tau], yrow, xrow, tau < len, tau < npart, valid, grp,
+                                pl, lane, red, rd_off, voff_dy, voff_dx, xw + (w * S + tau) * OUT);
+      yrow -= ldy_b;
+      xrow -= ldx_b;
       cur = nxt;
+      rcur = rnxt;
     }
-    wait_vm_all();
+    // Wait for the prefetch of sub-chunk u - 1 (and the start states): the
+    // vector memory counter retires in issue order, and the only operations
+    // issued after the prefetch are the walk's 2 stores per token, which may
+    // stay in flight.
+    static_assert(2 * S <= 63, "vmcnt field");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S) : "memory");
     __syncthreads();  // staged data of u - 1 visible; token sums complete
     // sum over the workgroup's wavefronts -> one partial per (token, workgroup)
     const int tot = len * OUT;

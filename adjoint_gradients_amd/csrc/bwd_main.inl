@@ -468,7 +468,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
     // different workgroup may still be writing) and contributes zeros.
 #pragma unroll
     for (int j = 0; j < NL; j++) hs[j] = wave_live ? hn[j] : 0.0f;
-    // after the recompute: bring sub-chunk u - 1's data and start state
     auto prefetch = [&]() {
       if (u > 0) {
         dma_rows(u - 1);
@@ -488,6 +487,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
     // no partner), so they leave the states and the adjoint unchanged, add
     // nothing to any sum, and their stores are dropped.
     float hr[S][NL];
+    // bring sub-chunk u - 1's data and start state now: the buffers it
+    // fills were last read before the previous sub-chunk's end barrier, and
+    // the loads get the whole sub-chunk to land
+    prefetch();
     // recompute the sub-chunk's states
     {
       float hh[NL];
@@ -518,7 +521,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         }
       }
     }
-    prefetch();
     // reverse walk; a token's per-lane values and its b, c (and partner c)
     // rows are read from LDS one token ahead
     struct Rows {

@@ -24,11 +24,6 @@ struct Tok {
   float s, x, g, sm, gm;
 };
 
-// Fourth word of a raw buffer resource on gfx9 parts (offsets in bytes,
-// range-checked against the record count: an access at or past it is
-// dropped for stores), and an offset past any row this kernel stores into.
-constexpr int kBufWord3 = 0x00020000;
-constexpr int kBufOutside = 0x7ffffff0;
 
 typedef __attribute__((address_space(3))) char lds_byte;
 

@@ -254,50 +254,65 @@ __global__ __launch_bounds__(256) void k_bwd_local_staged(BwdArgs a, int64_t NB)
   for (int q = 0; q < D - 1; q++)
     if (q < len) ld(q, t1 - 1 - q);
   __syncthreads();  // staged rows visible
-  for (int q8 = 0; q8 < len; q8 += D) {
+  // one token of the walk at position idx; the ring fetches position ahead
+  auto tok = [&](int r, int idx, bool fetch, int ahead) {
+    if (fetch) ld((r + D - 1) % D, t1 - 1 - ahead);
+    const int tau = len - 1 - idx;  // token i = t0 + tau
+    const int64_t i = t0 + tau;
+    const float sv = rs[r], gv = rg[r];
+    float ct[NL];
+    const float* rc = rows + tau * NN + n0;
 #pragma unroll
-    for (int r = 0; r < D; r++) {
-      const int idx = q8 + r;  // position in the reverse walk
-      if (idx < len) {
-        if (idx + D - 1 < len) ld((r + D - 1) % D, t1 - 1 - (idx + D - 1));
-        const int tau = len - 1 - idx;  // token i = t0 + tau
-        const int64_t i = t0 + tau;
-        const float sv = rs[r], gv = rg[r];
-        float ct[NL];
-        const float* rc = rows + tau * NN + n0;
+    for (int j = 0; j < NL; j += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(rc + j);
+      ct[j] = v.x; ct[j + 1] = v.y; ct[j + 2] = v.z; ct[j + 3] = v.w;
+    }
+    float mu[NL], av[NL];
+#pragma unroll
+    for (int j = 0; j < NL; j++) {
+      av[j] = fast_exp2(-sv * al2[j]);
+      mu[j] = fmaf(gv, ct[j], inc[j]);
+    }
+    if constexpr (WIN) {
+      if (i + W < T) {
+        float cm[NL];
+        const float* rm = rows + static_cast<size_t>(C) * NN + tau * NN + n0;
 #pragma unroll
         for (int j = 0; j < NL; j += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(rc + j);
-          ct[j] = v.x; ct[j + 1] = v.y; ct[j + 2] = v.z; ct[j + 3] = v.w;
+          const float4 v = *reinterpret_cast<const float4*>(rm + j);
+          cm[j] = v.x; cm[j + 1] = v.y; cm[j + 2] = v.z; cm[j + 3] = v.w;
         }
-        float mu[NL], av[NL];
+        const float E = static_cast<float>(sigma - suffix);
+        const float gm = rgm[r];
 #pragma unroll
         for (int j = 0; j < NL; j++) {
-          av[j] = fast_exp2(-sv * al2[j]);
-          mu[j] = fmaf(gv, ct[j], inc[j]);
+          const float Dw = fast_exp2(-E * al2[j]);
+          mu[j] = fmaf(-gm * cm[j], Dw, mu[j]);
         }
-        if constexpr (WIN) {
-          if (i + W < T) {
-            float cm[NL];
-            const float* rm = rows + static_cast<size_t>(C) * NN + tau * NN + n0;
+        suffix += static_cast<double>(rsm[r]);
+      }
+      sigma += static_cast<double>(sv);
+    }
 #pragma unroll
-            for (int j = 0; j < NL; j += 4) {
-              const float4 v = *reinterpret_cast<const float4*>(rm + j);
-              cm[j] = v.x; cm[j + 1] = v.y; cm[j + 2] = v.z; cm[j + 3] = v.w;
-            }
-            const float E = static_cast<float>(sigma - suffix);
-            const float gm = rgm[r];
+    for (int j = 0; j < NL; j++) inc[j] = av[j] * mu[j];
+  };
+  if (len % D == 0) {
+    // whole ring turns: no per-token branches (fetches past the chunk start
+    // re-read its first token), so no merge of paths makes the compiler wait
+    // for the ring's loads in flight
+    for (int q8 = 0; q8 < len; q8 += D) {
 #pragma unroll
-            for (int j = 0; j < NL; j++) {
-              const float Dw = fast_exp2(-E * al2[j]);
-              mu[j] = fmaf(-gm * cm[j], Dw, mu[j]);
-            }
-            suffix += static_cast<double>(rsm[r]);
-          }
-          sigma += static_cast<double>(sv);
-        }
+      for (int r = 0; r < D; r++) {
+        const int idx = q8 + r;
+        tok(r, idx, true, (idx + D - 1 < len) ? idx + D - 1 : len - 1);
+      }
+    }
+  } else {
+    for (int q8 = 0; q8 < len; q8 += D) {
 #pragma unroll
-        for (int j = 0; j < NL; j++) inc[j] = av[j] * mu[j];
+      for (int r = 0; r < D; r++) {
+        const int idx = q8 + r;  // position in the reverse walk
+        if (idx < len) tok(r, idx, idx + D - 1 < len, idx + D - 1);
       }
     }
   }

@@ -52,6 +52,14 @@ template <typename T> __device__ __forceinline__ void store_io(T* p, float v);
 template <> __device__ __forceinline__ void store_io<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void store_io<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
+// Fourth word of a raw buffer resource on gfx9 parts (offsets in bytes,
+// range-checked against the record count: a store at or past it is dropped),
+// and a lane offset past any row the kernels store into.  Kernels store
+// through such resources where some lanes or some iterations store nothing,
+// so that no lane mask or branch splits their loop bodies.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kBufOutside = 0x7ffffff0;
+
 // 2^x on the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -145,6 +145,8 @@ def test_sub_states(orc, label, T, P, N, io, window, chunk):
     (300, 40, 8, "f32", 120, 100),
     (1024, 96, 16, "bf16", 200, 256),
     (700, 70, 32, "f32", 700, 64),
+    (1000, 96, 16, "bf16", 256, 128),  # window of whole chunks, ragged last chunk, an idle wavefront
+    (700, 40, 8, "f32", 200, 100),     # window of whole chunks, one lane group
 ])
 def test_poisoned_buffers(orc, T, P, N, io, window, chunk, sub_states):
     # workspaces and saved buffers filled with NaN bytes beforehand: a read of

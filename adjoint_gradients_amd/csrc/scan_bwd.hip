@@ -418,10 +418,11 @@ __global__ __launch_bounds__(256) void k_bwd_carry(int64_t K, int64_t P, int64_t
   const int64_t p = e / N;
   const float al2 = alpha[e] * kLog2e;
   float cin = 0.0f;
-  // Blocks of 8 chunks: all loads of a block are issued before its stores
+  // Blocks of 32 chunks: all loads of a block are issued before its stores
   // (umu may alias carry, so the compiler would not move a load above an
-  // earlier store by itself).
-  constexpr int B = 8;
+  // earlier store by itself); the walk is latency-bound with one thread per
+  // (channel, state), so the deeper the block, the more loads in flight.
+  constexpr int B = 32;
   int64_t k = K - 1;
   for (; k >= B - 1; k -= B) {
     float u[B], sk[B];

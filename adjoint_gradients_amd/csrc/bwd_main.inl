@@ -127,7 +127,7 @@ struct RevState {
 template <typename IO, int NL, int G, bool WIN>
 __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, const Tok& tk, const float (&bt)[NL],
                                           const float (&ct)[NL], const float (&cm)[NL], const float (&hp)[NL],
-                                          const float (&hc)[NL], char* yrow, char* xrow, bool live, bool part,
+                                          const float (&hc)[NL], float sg, char* yrow, char* xrow, bool live, bool part,
                                           bool valid, int grp, int pl, int lane, float* red, int rd_off,
                                           int voff_dy, int voff_dx, float* xw_tau) {
   constexpr int CH = 64 / G;
@@ -174,7 +174,7 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
     ds = group_sum<G, CH>(ds);
     dxd = group_sum<G, CH>(dxd);
   }
-  const float dD = -(ds * (1.0f / kLog2e)) * one_minus_exp_neg(tk.s);
+  const float dD = -(ds * (1.0f / kLog2e)) * sg;  // sg = sigma(Delta_i) = 1 - e^{-s_i}
   // Stores through buffer resources over token i's rows: lanes that store
   // nothing carry an offset past the row, and the hardware drops such a
   // store, so no lane mask (and no branch) splits the token's code.
@@ -516,6 +516,20 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         }
       }
     }
+    // sigma(Delta) = 1 - e^{-s} of the sub-chunk's tokens.  With two lane
+    // groups only group 0 needs it (it stores dDelta and keeps dbias): group 0
+    // evaluates tokens 0 .. S/2-1 and group 1 tokens S/2 .. S-1 of the same
+    // channel, and one lane exchange per pair hands group 1's values over.
+    float sig[S];
+    if constexpr (G == 2) {
+#pragma unroll
+      for (int q = 0; q < S / 2; q++) {
+        const float v = one_minus_exp_neg(scal(0, grp * (S / 2) + q));
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        sig[q] = __uint_as_float(r[0]);          // lanes 0..31: own value (token q)
+        sig[S / 2 + q] = __uint_as_float(r[1]);  // lanes 0..31: group 1's (token S/2 + q)
+      }
+    }
     // reverse walk; a token's per-lane values and its b, c (and partner c)
     // rows are read from LDS one token ahead
     struct Rows {
@@ -559,7 +573,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
       float hp[NL];
 #pragma unroll
       for (int j = 0; j < NL; j++) hp[j] = (tau > 0) ? hr[tau > 0 ? tau - 1 : 0][j] : hs[j];
-      rev_token<IO, NL, G, WIN>(st, a, cur, bt, ct, cm, hp, hr[tau], yrow, xrow, tau < len, tau < npart, valid, grp,
+      const float sg = (G == 2) ? sig[tau] : one_minus_exp_neg(cur.s);
+      rev_token<IO, NL, G, WIN>(st, a, cur, bt, ct, cm, hp, hr[tau], sg, yrow, xrow, tau < len, tau < npart, valid, grp,
                                 pl, lane, red, rd_off, voff_dy, voff_dx, xw + (w * S + tau) * OUT);
       yrow -= ldy_b;
       xrow -= ldx_b;

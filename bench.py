@@ -382,8 +382,10 @@ def main():
         print(source_hash(args.source_hash))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
-              "the time-sharded design is described in DESIGN.md.", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Sharded over time, each GPU would scan its own tokens and exchange one chunk aggregate per "
+              "direction (a halo of W tokens for a truncated window) and all-reduce the weight gradients.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -20,14 +20,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 WORKLOADS = {
-    # name: (config index, window, chunk)
-    "cfg3": (3, 4096, 256),
-    "cfg2": (2, 8192, 256),
-    "cfg2w1k": (2, 1024, 256),
-    "cfg1": (1, 2048, 256),
-    "cfg1exact": (1, 16384, 256),
-    "cfg4": (4, 4096, 256),  # the 4-layer residual stack (ssm_stack_grad), timed whole
-    "cfg4norm": (4, 4096, 256),  # the same stack, every layer reading the RMS-normalised stream
+    # name: (index in ssm_inputs.CASES, window, chunk)
+    "layer1m": (3, 4096, 256),       # 1M tokens, P = 2048, N = 16, bf16
+    "layer128k": (2, 8192, 256),     # 128K tokens, P = 2048, N = 16, bf16
+    "layer128k_w1k": (2, 1024, 256),
+    "layer16k": (1, 2048, 256),      # 16K tokens, P = 1024, N = 16, fp32
+    "layer16k_exact": (1, 16384, 256),
+    "stack4": (4, 4096, 256),  # the 4-layer residual stack (ssm_stack_grad), timed whole
+    "stack4_norm": (4, 4096, 256),  # the same stack, every layer reading the RMS-normalised stream
 }
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -250,11 +250,11 @@ def study_memory():
     import torch
 
     import adjoint_gradients_amd as agm
-    from ssm_inputs import CONFIGS, make_layer_device
+    from ssm_inputs import CASES, make_layer_device
 
     gib = float(1 << 30)
-    for cfg_idx, window in ((2, 1024), (3, 4096)):
-        case = CONFIGS[cfg_idx]
+    for case_idx, window in ((2, 1024), (3, 4096)):
+        case = CASES[case_idx]
         T, P, N, io = case.T, case.P, case.N, case.io
         dims = agm.make_dims(T, P, N, 256, io)
         for sub in (False, True):
@@ -289,7 +289,7 @@ def study_memory():
             del y, saved, grads, inp, x, g, lay
 
 
-def bench_stack(args, cfg_idx, window, chunk, norm=False):
+def bench_stack(args, case_idx, window, chunk, norm=False):
     """One step of the K-layer residual stack: ssm_stack_grad (K forwards, then
     the K gradients in reverse with the cotangent passed down), timed whole
     with events on the library's stream.  Inputs as in the stack tests."""
@@ -297,9 +297,9 @@ def bench_stack(args, cfg_idx, window, chunk, norm=False):
     import torch
 
     import adjoint_gradients_amd as agm
-    from ssm_inputs import CONFIGS, _alpha, _weights
+    from ssm_inputs import CASES, _alpha, _weights
 
-    case = CONFIGS[cfg_idx]
+    case = CASES[case_idx]
     T, P, N, K = case.T, case.P, case.N, case.K
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -362,7 +362,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="cfg3", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="layer1m", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens of the workload the fp64 oracle is timed on (the CPU baseline sample)")
@@ -407,13 +407,13 @@ def main():
         return
 
     import adjoint_gradients_amd as agm
-    from ssm_inputs import CONFIGS, make_layer_device
+    from ssm_inputs import CASES, make_layer_device
 
-    cfg_idx, window, chunk = WORKLOADS[args.workload]
-    if CONFIGS[cfg_idx].K > 1:
-        bench_stack(args, cfg_idx, window, chunk, norm=args.workload.endswith("norm"))
+    case_idx, window, chunk = WORKLOADS[args.workload]
+    if CASES[case_idx].K > 1:
+        bench_stack(args, case_idx, window, chunk, norm=args.workload.endswith("norm"))
         return
-    case = CONFIGS[cfg_idx]
+    case = CASES[case_idx]
     dev = "cuda:0"
     torch.cuda.set_device(0)
     inp = make_layer_device(case, device=dev)

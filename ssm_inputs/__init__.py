@@ -28,7 +28,7 @@ import numpy as np
 
 __all__ = [
     "LayerCase",
-    "CONFIGS",
+    "CASES",
     "bf16_round",
     "make_layer",
     "make_stack",
@@ -69,13 +69,13 @@ class LayerCase:
 
 # The five workloads of the hot path (sizes from the method's problem
 # statement: one layer at 16K / 128K / 1M tokens, and a 4-layer stack).
-CONFIGS = {
-    0: LayerCase("cfg0_tiny_f32", 256, 16, 8, "f32", (256,), seed=0),
-    1: LayerCase("cfg1_16k_f32", 16384, 1024, 16, "f32", (16384, 2048), seed=1),
-    2: LayerCase("cfg2_128k_bf16", 131072, 2048, 16, "bf16", (1024, 8192), seed=2),
-    3: LayerCase("cfg3_1m_bf16", 1048576, 2048, 16, "bf16", (4096,),
+CASES = {
+    0: LayerCase("layer_256tok_f32", 256, 16, 8, "f32", (256,), seed=0),
+    1: LayerCase("layer_16k_f32", 16384, 1024, 16, "f32", (16384, 2048), seed=1),
+    2: LayerCase("layer_128k_bf16", 131072, 2048, 16, "bf16", (1024, 8192), seed=2),
+    3: LayerCase("layer_1m_bf16", 1048576, 2048, 16, "bf16", (4096,),
                  bias="softplus_uniform", seed=3),
-    4: LayerCase("cfg4_stack4_bf16", 262144, 1536, 64, "bf16", (262144, 4096), K=4, seed=4,
+    4: LayerCase("stack4_256k_bf16", 262144, 1536, 64, "bf16", (262144, 4096), K=4, seed=4,
                  x_scale=0.125),
 }
 

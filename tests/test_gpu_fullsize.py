@@ -22,7 +22,7 @@ import numpy as np
 import pytest
 
 from gpu_util import GRAD_KEYS, TOL, compare, gpu_layer, oracle_inputs, rel_err, say
-from ssm_inputs import CONFIGS, make_layer, make_layer_device
+from ssm_inputs import CASES, make_layer, make_layer_device
 
 pytestmark = pytest.mark.gpu
 
@@ -47,8 +47,8 @@ def orc():
 
 
 @pytest.mark.parametrize("window,want_dx", [(1024, True), (8192, False)])
-def test_cfg2_full_oracle(orc, window, want_dx):
-    case = CONFIGS[2]
+def test_layer128k_full_oracle(orc, window, want_dx):
+    case = CASES[2]
     inp = make_layer(case)
     say(f"case {case.name} full: T={case.T} P={case.P} N={case.N} W={window} C={CHUNK} dx={want_dx}")
     got = gpu_layer(inp, window, CHUNK, want_dx=want_dx, sub_states=True)
@@ -142,16 +142,16 @@ def _check_sampled(orc, case, window):
     assert not bad, f"over tolerance {TOL[case.io]}: {bad}"
 
 
-def test_cfg3_bench_workload_sampled(orc):
-    _check_sampled(orc, CONFIGS[3], 4096)
+def test_layer1m_bench_workload_sampled(orc):
+    _check_sampled(orc, CASES[3], 4096)
 
 
 @pytest.mark.parametrize("window", [4096, 262144])
-def test_cfg4_layer_n64_sampled(orc, window):
-    _check_sampled(orc, CONFIGS[4], window)
+def test_stack4_layer_n64_sampled(orc, window):
+    _check_sampled(orc, CASES[4], window)
 
 
-def test_cfg4_stack_equals_layer_composition():
+def test_stack4_equals_layer_composition():
     """ssm_stack_grad (K=4, T=262144, P=1536, N=64, window 4096) against the
     same stack assembled from ssm_forward / ssm_adjoint_grad calls with the
     residual adds, the bf16 cast and the cotangent passing done in torch."""
@@ -160,7 +160,7 @@ def test_cfg4_stack_equals_layer_composition():
     import adjoint_gradients_amd as agm
     from ssm_inputs import _alpha, _weights
 
-    case = CONFIGS[4]
+    case = CASES[4]
     T, P, N, K, W = case.T, case.P, case.N, case.K, 4096
     say(f"case {case.name} stack composition: K={K} T={T} P={P} N={N} W={W} C={CHUNK}")
     dev = "cuda"
@@ -213,7 +213,7 @@ def test_cfg4_stack_equals_layer_composition():
 
 
 @pytest.mark.parametrize("window,norm", [(4096, False), (1024, False), (4096, True)])
-def test_cfg4_stack_prefix_oracle(orc, window, norm):
+def test_stack4_prefix_oracle(orc, window, norm):
     """The 4-layer, P=1536, N=64 bf16 stack on its first 4096 tokens against
     the oracle's stack (cotangent passing, bf16 layer inputs); with norm, every
     layer reads the RMS-normalised stream (scale gamma ~ U(0.5, 1.5) / sqrt(N),
@@ -224,7 +224,7 @@ def test_cfg4_stack_prefix_oracle(orc, window, norm):
     import adjoint_gradients_amd as agm
     import torch
 
-    case = CONFIGS[4]
+    case = CASES[4]
     T = 4096
     st = make_stack(case, T=T)
     K, P, N = st["K"], st["P"], st["N"]

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from gpu_util import GRAD_KEYS, TOL, compare, gpu_layer, oracle_inputs, rel_err, say
-from ssm_inputs import CONFIGS, LayerCase, make_layer, make_stack, small_case, window_pin_case
+from ssm_inputs import CASES, LayerCase, make_layer, make_stack, small_case, window_pin_case
 
 pytestmark = pytest.mark.gpu
 
@@ -49,9 +49,9 @@ def _run_case(orc, inp, window, chunk, label, tol=None, sub_states=False):
     return got, ref
 
 
-def test_cfg0_exact(orc):
-    inp = make_layer(CONFIGS[0])
-    _run_case(orc, inp, 256, 256, "cfg0 W=T")
+def test_layer256_exact(orc):
+    inp = make_layer(CASES[0])
+    _run_case(orc, inp, 256, 256, "256-token layer W=T")
 
 
 @pytest.mark.parametrize("chunk", [1, 3, 16, 100, 256, 512])
@@ -225,10 +225,10 @@ def test_determinism_and_linearity():
         assert np.array_equal(c[k], 2.0 * a[k]), k
 
 
-def test_cfg1(orc):
-    inp = make_layer(CONFIGS[1])
+def test_layer16k(orc):
+    inp = make_layer(CASES[1])
     for W in (16384, 2048):
-        _run_case(orc, inp, W, 256, f"cfg1 W={W}")
+        _run_case(orc, inp, W, 256, f"16K-token layer W={W}")
 
 
 def _gpu_stack(st, window, chunk):

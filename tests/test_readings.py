@@ -12,7 +12,7 @@ import dataclasses
 import numpy as np
 
 import oracle
-from ssm_inputs import CONFIGS, make_stack
+from ssm_inputs import CASES, make_stack
 
 F32_MAX = float(np.finfo(np.float32).max)
 
@@ -22,13 +22,13 @@ def _rms(a):
 
 
 def test_stack_unit_inputs_overflow_f32():
-    case = dataclasses.replace(CONFIGS[4], x_scale=1.0)
+    case = dataclasses.replace(CASES[4], x_scale=1.0)
     fw = oracle.stack_forward(make_stack(case, T=48))
     assert np.max(np.abs(fw["r_final"])) > F32_MAX
 
 
 def test_stack_scaled_inputs_stay_in_range():
-    case = CONFIGS[4]
+    case = CASES[4]
     assert case.x_scale == 1.0 / np.sqrt(case.N)
     fw = oracle.stack_forward(make_stack(case, T=48))
     r = [_rms(x) for x in fw["x_layers"]] + [_rms(fw["r_final"])]

@@ -9,14 +9,21 @@
 //            walk beforehand at higher occupancy and this phase is skipped;
 //   phase 2  sub-chunks right to left: recompute the S states into registers,
 //            then walk them in reverse with the adjoint recurrence and the
-//            local VJPs (equations in scan_bwd.hip).
+//            local VJPs (equations in scan_bwd.hip).  A sub-chunk compiles to
+//            one basic block: a partial one runs the same code on tokens
+//            staged as zeros, stores go through buffer resources whose
+//            out-of-range lanes are dropped, and the window partner's terms
+//            are taken by select.
 // Latency hiding: everything a sub-chunk reads from memory is brought by LDS
-// DMA during the previous sub-chunk (issued after its recompute, waited for
-// at its end) -- the per-token rows b_t, c_t and c_{t+W} (shared by all
-// channels) into a double-buffered area, the per-lane quantities (s, x, g and
-// the partner token's s, g) into a double-buffered area of each wavefront's
-// own -- so no register holds prefetched data; only the next sub-chunk's
-// start state is loaded into registers ahead of time.
+// DMA during the previous sub-chunk (issued at its start, waited for at its
+// end, where the wait lets the walk's own stores stay in flight) -- the
+// per-token rows b_t, c_t and c_{t+W} (shared by all channels) into a
+// double-buffered area, the per-lane quantities (s, x, g and the partner
+// token's s, g) into a double-buffered area of each wavefront's own -- so no
+// register holds prefetched data; only the next sub-chunk's start state is
+// loaded into registers ahead of time, on a single code path (a load on one
+// path only would make the compiler wait for every load in flight where the
+// paths meet).
 
 namespace {
 

@@ -31,6 +31,10 @@ struct Tok {
   float s, x, g, sm, gm;
 };
 
+// Vector-memory operations the reverse walk issues per token (rev_token's
+// dDelta and dx_dir stores).
+constexpr int kWalkStoresPerToken = 2;
+
 
 typedef __attribute__((address_space(3))) char lds_byte;
 
@@ -182,6 +186,8 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
     dxd = group_sum<G, CH>(dxd);
   }
   const float dD = -(ds * (1.0f / kLog2e)) * sg;  // sg = sigma(Delta_i) = 1 - e^{-s_i}
+  // Exactly kWalkStoresPerToken vector-memory operations per token (the two
+  // stores below): the end-of-sub-chunk wait in k_bwd_main counts on it.
   // Stores through buffer resources over token i's rows: lanes that store
   // nothing carry an offset past the row, and the hardware drops such a
   // store, so no lane mask (and no branch) splits the token's code.
@@ -590,10 +596,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
     }
     // Wait for the prefetch of sub-chunk u - 1 (and the start states): the
     // vector memory counter retires in issue order, and the only operations
-    // issued after the prefetch are the walk's 2 stores per token, which may
-    // stay in flight.
-    static_assert(2 * S <= 63, "vmcnt field");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S) : "memory");
+    // issued after the prefetch are the walk's stores (kWalkStoresPerToken
+    // per token), which may stay in flight.  Were the walk to issue fewer,
+    // this wait would end before the prefetch has landed.
+    static_assert(kWalkStoresPerToken * S <= 63, "vmcnt field");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWalkStoresPerToken * S) : "memory");
     __syncthreads();  // staged data of u - 1 visible; token sums complete
     // sum over the workgroup's wavefronts -> one partial per (token, workgroup)
     const int tot = len * OUT;

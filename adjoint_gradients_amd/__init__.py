@@ -6,6 +6,12 @@ entry points keep the C names (ssm_forward, ssm_adjoint_grad, ssm_stack_grad,
 ssm_workspace_bytes, ...).  Importing this module raises if the library has
 not been built -- there is no fallback path.
 
+Before a tensor's address crosses the ABI, the binding checks that it lives
+on a GPU, is contiguous, has the dtype the call expects (the io dtype for x
+and the weights, float32 or float64 elsewhere) and the element count the
+dims imply; a mismatch raises SsmError(SSM_ERR_ARG) and nothing is launched
+(the library itself sees only pointers and cannot tell a short buffer).
+
 Method: gradient of a diagonal selective state-space layer as the sum of
 per-token vector-Jacobian products driven by adjoint states, optionally
 truncated to a window (review of "Adjoint sharding for very long context
@@ -30,7 +36,9 @@ EXPORTED = (
     "ssm_saved_bytes",
     "ssm_sub_state_bytes",
     "ssm_grad_workspace_bytes_sub",
+    "ssm_grad_slab_count",
     "ssm_workspace_bytes",
+    "ssm_stack_workspace_bytes",
     "ssm_forward",
     "ssm_adjoint_grad",
     "ssm_stack_grad",
@@ -84,6 +92,10 @@ def _load():
     lib.ssm_grad_workspace_bytes_sub.restype = ctypes.c_size_t
     lib.ssm_workspace_bytes.argtypes = [P(Dims), ctypes.c_int64, ctypes.c_int32]
     lib.ssm_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssm_stack_workspace_bytes.argtypes = [ctypes.c_int32, P(Dims), P(Layer), ctypes.c_int64]
+    lib.ssm_stack_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssm_grad_slab_count.argtypes = [P(Dims), ctypes.c_int64, ctypes.c_int32]
+    lib.ssm_grad_slab_count.restype = ctypes.c_int32
     lib.ssm_forward.argtypes = [P(Dims), P(Layer), ctypes.c_void_p, ctypes.c_void_p, P(Saved),
                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.ssm_forward.restype = ctypes.c_int
@@ -132,8 +144,54 @@ def ssm_workspace_bytes(dims: Dims, window: int = 0, K: int = 0) -> int:
     return int(lib.ssm_workspace_bytes(ctypes.byref(dims), int(window), int(K)))
 
 
+def ssm_stack_workspace_bytes(K: int, dims: Dims, layers, window: int) -> int:
+    arr = (Layer * K)(*layers)
+    return int(lib.ssm_stack_workspace_bytes(int(K), ctypes.byref(dims), arr, int(window)))
+
+
+def ssm_grad_slab_count(dims: Dims, window: int, sub_states_given: bool) -> int:
+    return int(lib.ssm_grad_slab_count(ctypes.byref(dims), int(window), 1 if sub_states_given else 0))
+
+
 def _ptr(t) -> int | None:
     return None if t is None else int(t.data_ptr())
+
+
+def _need(t, name: str, numel: int, dtype, optional: bool = False, at_least: bool = False):
+    """Checks a tensor before its address is passed to the library."""
+    import torch
+
+    if t is None:
+        if optional:
+            return
+        raise SsmError(1, f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise SsmError(1, f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise SsmError(1, f"{name}: must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise SsmError(1, f"{name}: must be contiguous")
+    if t.dtype != dtype:
+        raise SsmError(1, f"{name}: dtype {t.dtype}, expected {dtype}")
+    n = t.numel()
+    if (n < numel) if at_least else (n != numel):
+        raise SsmError(1, f"{name}: {n} elements, expected {'at least ' if at_least else ''}{numel}")
+
+
+def _io(dims: Dims):
+    import torch
+
+    return torch.bfloat16 if dims.io == SSM_BF16 else torch.float32
+
+
+def _nchunks(dims: Dims) -> int:
+    return (dims.T + dims.chunk - 1) // dims.chunk
+
+
+def _check_ws(ws, ws_bytes: int):
+    import torch
+
+    _need(ws, "workspace", int(ws_bytes), torch.uint8, at_least=True)
 
 
 def _stream(stream) -> int | None:
@@ -153,28 +211,70 @@ def make_dims(T: int, P: int, N: int, chunk: int = 256, io: str = "f32") -> Dims
     return Dims(T, P, N, chunk, SSM_BF16 if io == "bf16" else SSM_F32)
 
 
-def layer_struct(W_delta, W_B, W_C, alpha, delta_bias=None, norm_scale=None) -> Layer:
+def layer_struct(dims: Dims, W_delta, W_B, W_C, alpha, delta_bias=None, norm_scale=None) -> Layer:
+    import torch
+
+    P, N, io = dims.P, dims.N, _io(dims)
+    _need(W_delta, "W_delta", P * P, io)
+    _need(W_B, "W_B", N * P, io)
+    _need(W_C, "W_C", N * P, io)
+    _need(alpha, "alpha", P * N, torch.float32)
+    _need(delta_bias, "delta_bias", P, torch.float32, optional=True)
+    _need(norm_scale, "norm_scale", P, torch.float32, optional=True)
     return Layer(_ptr(W_delta), _ptr(W_B), _ptr(W_C), _ptr(alpha), _ptr(delta_bias), _ptr(norm_scale))
 
 
-def saved_struct(saved: dict) -> Saved:
+def saved_struct(saved: dict, dims: Dims) -> Saved:
+    import torch
+
+    T, P, N, K = dims.T, dims.P, dims.N, _nchunks(dims)
+    f32 = torch.float32
+    _need(saved.get("s"), "saved s", T * P, f32)
+    _need(saved.get("b"), "saved b", T * N, f32)
+    _need(saved.get("c"), "saved c", T * N, f32)
+    _need(saved.get("h_ckpt"), "saved h_ckpt", K * P * N, f32)
+    _need(saved.get("s_sum"), "saved s_sum", K * P, torch.float64)
+    if saved.get("h_sub") is not None:
+        _need(saved["h_sub"], "saved h_sub", ssm_sub_state_bytes(dims) // 4, f32, at_least=True)
     return Saved(_ptr(saved["s"]), _ptr(saved["b"]), _ptr(saved["c"]), _ptr(saved["h_ckpt"]),
                  _ptr(saved["s_sum"]), _ptr(saved.get("h_sub")))
 
 
-def grads_struct(grads: dict) -> Grads:
+def grads_struct(grads: dict, dims: Dims) -> Grads:
+    import torch
+
+    T, P, N = dims.T, dims.P, dims.N
+    f32 = torch.float32
+    _need(grads.get("dW_delta"), "dW_delta", P * P, f32)
+    _need(grads.get("dW_B"), "dW_B", N * P, f32)
+    _need(grads.get("dW_C"), "dW_C", N * P, f32)
+    _need(grads.get("dalpha"), "dalpha", P * N, f32, optional=True)
+    _need(grads.get("dbias"), "dbias", P, f32, optional=True)
+    _need(grads.get("dx"), "dx", T * P, f32, optional=True)
+    _need(grads.get("dnorm_scale"), "dnorm_scale", P, f32, optional=True)
     return Grads(_ptr(grads.get("dW_delta")), _ptr(grads.get("dW_B")), _ptr(grads.get("dW_C")),
                  _ptr(grads.get("dalpha")), _ptr(grads.get("dbias")), _ptr(grads.get("dx")),
                  _ptr(grads.get("dnorm_scale")))
 
 
 def ssm_forward(dims: Dims, layer: Layer, x, y, saved: Saved, ws, ws_bytes: int, stream=None):
+    """layer and saved come from LayerTensors.struct / saved_struct, which check their tensors."""
+    import torch
+
+    _need(x, "x", dims.T * dims.P, _io(dims))
+    _need(y, "y", dims.T * dims.P, torch.float32)
+    _check_ws(ws, ws_bytes)
     _check(lib.ssm_forward(ctypes.byref(dims), ctypes.byref(layer), _ptr(x), _ptr(y), ctypes.byref(saved),
                            _ptr(ws), int(ws_bytes), _stream(stream)), "ssm_forward")
 
 
 def ssm_adjoint_grad(dims: Dims, layer: Layer, x, saved: Saved, g, window: int, grads: Grads, ws,
                      ws_bytes: int, stream=None):
+    import torch
+
+    _need(x, "x", dims.T * dims.P, _io(dims))
+    _need(g, "g", dims.T * dims.P, torch.float32)
+    _check_ws(ws, ws_bytes)
     _check(lib.ssm_adjoint_grad(ctypes.byref(dims), ctypes.byref(layer), _ptr(x), ctypes.byref(saved), _ptr(g),
                                 int(window), ctypes.byref(grads), _ptr(ws), int(ws_bytes), _stream(stream)),
            "ssm_adjoint_grad")
@@ -189,6 +289,11 @@ def _event_array(events):
 
 
 def ssm_forward_timed(dims: Dims, layer: Layer, x, y, saved: Saved, ws, ws_bytes: int, events, stream=None):
+    import torch
+
+    _need(x, "x", dims.T * dims.P, _io(dims))
+    _need(y, "y", dims.T * dims.P, torch.float32)
+    _check_ws(ws, ws_bytes)
     arr = _event_array(events)
     _check(lib.ssm_forward_timed(ctypes.byref(dims), ctypes.byref(layer), _ptr(x), _ptr(y), ctypes.byref(saved),
                                  _ptr(ws), int(ws_bytes), _stream(stream), arr, len(events)),
@@ -197,6 +302,13 @@ def ssm_forward_timed(dims: Dims, layer: Layer, x, y, saved: Saved, ws, ws_bytes
 
 def ssm_adjoint_grad_timed(dims: Dims, layer: Layer, x, saved: Saved, g, window: int, grads: Grads, ws,
                            ws_bytes: int, events, stream=None):
+    """events: [0..6] phase marks, then two per slab around the fused reverse
+    kernel's launches (see the C header)."""
+    import torch
+
+    _need(x, "x", dims.T * dims.P, _io(dims))
+    _need(g, "g", dims.T * dims.P, torch.float32)
+    _check_ws(ws, ws_bytes)
     arr = _event_array(events)
     _check(lib.ssm_adjoint_grad_timed(ctypes.byref(dims), ctypes.byref(layer), _ptr(x), ctypes.byref(saved),
                                       _ptr(g), int(window), ctypes.byref(grads), _ptr(ws), int(ws_bytes),
@@ -206,6 +318,16 @@ def ssm_adjoint_grad_timed(dims: Dims, layer: Layer, x, saved: Saved, g, window:
 
 def ssm_stack_grad(K: int, dims: Dims, layers, x0, g, window: int, grads, dx0, xK, ws, ws_bytes: int,
                    stream=None):
+    import torch
+
+    if len(layers) != K or len(grads) != K:
+        raise SsmError(1, f"ssm_stack_grad: {len(layers)} layers and {len(grads)} gradient sets for K={K}")
+    TP = dims.T * dims.P
+    _need(x0, "x0", TP, _io(dims))
+    _need(g, "g", TP, torch.float32)
+    _need(dx0, "dx0", TP, torch.float32, optional=True)
+    _need(xK, "xK", TP, torch.float32, optional=True)
+    _check_ws(ws, ws_bytes)
     LArr = Layer * K
     GArr = Grads * K
     la = LArr(*layers)
@@ -226,8 +348,8 @@ class LayerTensors:
     delta_bias: object = None
     norm_scale: object = None  # [P] float32: stack layers that read the RMS-normalised stream
 
-    def struct(self) -> Layer:
-        return layer_struct(self.W_delta, self.W_B, self.W_C, self.alpha, self.delta_bias, self.norm_scale)
+    def struct(self, dims: Dims) -> Layer:
+        return layer_struct(dims, self.W_delta, self.W_B, self.W_C, self.alpha, self.delta_bias, self.norm_scale)
 
 
 def io_dtype(io: str):
@@ -275,7 +397,7 @@ def forward(dims: Dims, layer: LayerTensors, x, ws=None, saved=None, y=None, str
     ws = alloc_workspace(nbytes, x.device) if ws is None else ws
     saved = alloc_saved(dims, x.device, sub_states) if saved is None else saved
     y = torch.empty(dims.T, dims.P, device=x.device, dtype=torch.float32) if y is None else y
-    ssm_forward(dims, layer.struct(), x, y, saved_struct(saved), ws, ws.numel(), stream)
+    ssm_forward(dims, layer.struct(dims), x, y, saved_struct(saved, dims), ws, ws.numel(), stream)
     return y, saved
 
 
@@ -305,8 +427,8 @@ def adjoint_grad(dims: Dims, layer: LayerTensors, x, saved: dict, g, window: int
         raise SsmError(4, "ssm_workspace_bytes")
     ws = alloc_workspace(nbytes, x.device) if ws is None else ws
     grads = alloc_grads(dims, want_dx=want_dx, device=x.device) if grads is None else grads
-    ssm_adjoint_grad(dims, layer.struct(), x, saved_struct(saved), g, window, grads_struct(grads), ws,
-                     ws.numel(), stream)
+    ssm_adjoint_grad(dims, layer.struct(dims), x, saved_struct(saved, dims), g, window, grads_struct(grads, dims),
+                     ws, ws.numel(), stream)
     return grads
 
 
@@ -316,9 +438,10 @@ def stack_grad(dims: Dims, layers: list, x0, g, window: int, ws=None, want_dx0=T
     import torch
 
     K = len(layers)
-    nbytes = ssm_workspace_bytes(dims, window, K)
+    structs = [lay.struct(dims) for lay in layers]
+    nbytes = ssm_stack_workspace_bytes(K, dims, structs, window)
     if nbytes == 0:
-        raise SsmError(4, "ssm_workspace_bytes")
+        raise SsmError(4, "ssm_stack_workspace_bytes")
     ws = alloc_workspace(nbytes, x0.device) if ws is None else ws
     grads = [alloc_grads(dims, device=x0.device) for _ in range(K)]
     for gr, lay in zip(grads, layers):
@@ -327,6 +450,6 @@ def stack_grad(dims: Dims, layers: list, x0, g, window: int, ws=None, want_dx0=T
     f = dict(device=x0.device, dtype=torch.float32)
     dx0 = torch.empty(dims.T, dims.P, **f) if want_dx0 else None
     xK = torch.empty(dims.T, dims.P, **f) if want_xK else None
-    ssm_stack_grad(K, dims, [lay.struct() for lay in layers], x0, g, window, [grads_struct(gr) for gr in grads],
+    ssm_stack_grad(K, dims, structs, x0, g, window, [grads_struct(gr, dims) for gr in grads],
                    dx0, xK, ws, ws.numel(), stream)
     return grads, dx0, xK

@@ -141,7 +141,7 @@ int splitk_for(const ssm_dims* d) {
 struct BwdWs {
   void* wcat;      // only when dx is needed
   void* dY;
-  float* dxdir;    // only when dx is needed
+  float* dxdir;    // only in the stack (a single layer writes dx_dir into its dx output)
   float* part;
   float* umu;
   float* carry;
@@ -150,12 +150,16 @@ struct BwdWs {
   float* dal_part;
   float* dbias_part;
   float* hsub;
+  int64_t hsub_chunks;  // chunks the hsub region holds (one slab)
   float* wpart;
   int splits;
 };
 
-// own_hsub: the workspace holds the sub-chunk states (the caller did not keep them)
-BwdWs carve_bwd(Carver& cv, const ssm_dims* d, int64_t W, bool need_dx, bool own_hsub = true) {
+// own_hsub: the workspace holds a slab of sub-chunk states (the caller did
+// not keep them); own_dxdir: the direct input cotangent needs a buffer of its
+// own (the stack, whose cotangent stream is read while it is written)
+BwdWs carve_bwd(Carver& cv, const ssm_dims* d, int64_t W, bool need_dx, bool own_hsub = true,
+                bool own_dxdir = false) {
   BwdWs w;
   BwdPlan pl;
   ssm::bwd_plan(d->P, d->N, d->chunk, &pl);
@@ -164,7 +168,7 @@ BwdWs carve_bwd(Carver& cv, const ssm_dims* d, int64_t W, bool need_dx, bool own
   const bool win = W < T;
   w.wcat = need_dx ? cv.take<char>(static_cast<size_t>(M * P) * io_size(d)) : nullptr;
   w.dY = cv.take<char>(static_cast<size_t>(T * M) * io_size(d));
-  w.dxdir = need_dx ? cv.take<float>(static_cast<size_t>(T * P)) : nullptr;
+  w.dxdir = (need_dx && own_dxdir) ? cv.take<float>(static_cast<size_t>(T * P)) : nullptr;
   w.part = cv.take<float>(static_cast<size_t>(T * pl.NBW * 2 * N));
   w.umu = cv.take<float>(static_cast<size_t>(K * P * N + P));  // + P: also the chunk-reduction scratch
   w.carry = cv.take<float>(static_cast<size_t>(K * P * N));
@@ -172,7 +176,8 @@ BwdWs carve_bwd(Carver& cv, const ssm_dims* d, int64_t W, bool need_dx, bool own
   w.hwin = win ? cv.take<double>(static_cast<size_t>(K * P)) : nullptr;
   w.dal_part = cv.take<float>(static_cast<size_t>(K * P * N));
   w.dbias_part = cv.take<float>(static_cast<size_t>(K * P));
-  w.hsub = own_hsub ? cv.take<float>(ssm::bwd_hsub_floats(T, P, N, d->chunk)) : nullptr;
+  w.hsub_chunks = own_hsub ? ssm::bwd_hsub_slab_chunks(T, P, N, d->chunk) : K;
+  w.hsub = own_hsub ? cv.take<float>(ssm::bwd_hsub_floats_chunks(w.hsub_chunks, P, N, d->chunk)) : nullptr;
   w.splits = splitk_for(d);
   w.wpart = cv.take<float>(static_cast<size_t>(w.splits) * M * P);
   return w;
@@ -196,43 +201,53 @@ size_t fwd_ws_bytes(const ssm_dims* d) {
   return cv.off;
 }
 
-size_t bwd_ws_bytes(const ssm_dims* d, int64_t W, bool need_dx, bool own_hsub = true) {
+size_t bwd_ws_bytes(const ssm_dims* d, int64_t W, bool need_dx, bool own_hsub = true, bool own_dxdir = false) {
   Carver cv(nullptr);
-  carve_bwd(cv, d, W, need_dx, own_hsub);
+  carve_bwd(cv, d, W, need_dx, own_hsub, own_dxdir);
   return cv.off;
 }
 
-// Normalisation buffers of the stack: per layer the residual r^k and 1/rms per
-// token (kept for the VJP), the layer's dx, and the VJP's row scratch.
+// Normalisation buffers of the stack, present only when KN >= 1 of its layers
+// normalise: per such layer the residual r^k and 1/rms per token (kept for
+// the VJP, slot = the layer's rank among the normalising ones), the layer's
+// dx, and the VJP's row scratch.
 struct NormWs {
-  float* rk;      // [K][T][P]
-  float* rinv;    // [K][T]
+  float* rk;      // [KN][T][P]
+  float* rinv;    // [KN][T]
   float* dx;      // [T][P]
   float* m;       // [T]
   float* part;    // [row blocks][P]
 };
 
-NormWs carve_norm(Carver& cv, const ssm_dims* d, int32_t K) {
-  NormWs n;
+NormWs carve_norm(Carver& cv, const ssm_dims* d, int32_t KN) {
+  NormWs n{};
+  if (KN < 1) return n;
   const int64_t T = d->T, P = d->P;
-  n.rk = cv.take<float>(static_cast<size_t>(K) * T * P);
-  n.rinv = cv.take<float>(static_cast<size_t>(K) * T);
+  n.rk = cv.take<float>(static_cast<size_t>(KN) * T * P);
+  n.rinv = cv.take<float>(static_cast<size_t>(KN) * T);
   n.dx = cv.take<float>(static_cast<size_t>(T * P));
   n.m = cv.take<float>(static_cast<size_t>(T));
   n.part = cv.take<float>(static_cast<size_t>(ssm::norm_row_blocks(T) * P));
   return n;
 }
 
-size_t stack_ws_bytes(const ssm_dims* d, int64_t W, int32_t K) {
+// Workspace of a stack of K layers of which KN normalise their input.
+size_t stack_ws_bytes(const ssm_dims* d, int64_t W, int32_t K, int32_t KN) {
   Carver cv(nullptr);
   for (int32_t k = 0; k < K; k++) carve_saved(cv, d);
   cv.take<char>(static_cast<size_t>(K) * d->T * d->P * io_size(d));
   cv.take<float>(static_cast<size_t>(d->T * d->P));
   cv.take<float>(static_cast<size_t>(d->T * d->P));
   cv.take<float>(static_cast<size_t>(d->T * d->P));
-  carve_norm(cv, d, K);
-  const size_t f = fwd_ws_bytes(d), b = bwd_ws_bytes(d, W, true);
+  carve_norm(cv, d, KN);
+  const size_t f = fwd_ws_bytes(d), b = bwd_ws_bytes(d, W, true, true, true);
   return cv.off + (f > b ? f : b);
+}
+
+int32_t count_norm(int32_t K, const ssm_layer* layers) {
+  int32_t n = 0;
+  for (int32_t k = 0; k < K; k++) n += layers[k].norm_scale ? 1 : 0;
+  return n;
 }
 
 // ---------------------------------------------------------------- internal passes
@@ -283,8 +298,13 @@ hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, co
   a.dal_part = w.dal_part; a.dbias_part = w.dbias_part;
   a.hsub = sv->h_sub ? sv->h_sub : w.hsub;
   a.hsub_given = sv->h_sub ? 1 : 0;
+  a.hsub_chunks = w.hsub_chunks;
   a.dY = w.dY; a.ldy = M;
-  a.dxdir = need_dx ? w.dxdir : nullptr;
+  // the direct input cotangent: the stack's own buffer (its cotangent stream
+  // is g here, read while dx_dir is written), else the dx output itself,
+  // which the input-cotangent GEMM then completes in place
+  float* dxdir = delta_io ? w.dxdir : gr->dx;
+  a.dxdir = need_dx ? dxdir : nullptr;
   a.dalpha = gr->dalpha; a.dbias = gr->dbias;
   a.marks = mk;
   hipError_t e = ssm::launch_backward_scan(a, bf, st);
@@ -301,7 +321,7 @@ hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, co
     if (e != hipSuccess) return e;
     // dx = dY W_cat + dxdir  (+ delta for the stack, in place)
     ssm::GemmOperands opx{T, P, M, w.dY, M, true, w.wcat, P, false};
-    ssm::EpiAddArgs ea{w.dxdir, delta_io, delta_io ? delta_io : gr->dx};
+    ssm::EpiAddArgs ea{dxdir, delta_io, delta_io ? delta_io : gr->dx};
     e = ssm::gemm_add(opx, bf, ea, st);
   }
   mk.rec(6, st);
@@ -337,6 +357,19 @@ size_t ssm_sub_state_bytes(const ssm_dims* d) {
   return ssm::bwd_hsub_floats(d->T, d->P, d->N, d->chunk) * sizeof(float);
 }
 
+size_t ssm_stack_workspace_bytes(int32_t K, const ssm_dims* d, const ssm_layer* layers, int64_t window) {
+  if (check_dims(d) != SSM_OK || K < 1 || K > 64 || !layers || window < 1) return 0;
+  return stack_ws_bytes(d, window < d->T ? window : d->T, K, count_norm(K, layers));
+}
+
+int32_t ssm_grad_slab_count(const ssm_dims* d, int64_t window, int32_t sub_states_given) {
+  if (check_dims(d) != SSM_OK || window < 1) return 0;
+  if (sub_states_given) return 1;
+  const int64_t K = nchunks(d);
+  const int64_t slab = ssm::bwd_hsub_slab_chunks(d->T, d->P, d->N, d->chunk);
+  return static_cast<int32_t>((K + slab - 1) / slab);
+}
+
 size_t ssm_grad_workspace_bytes_sub(const ssm_dims* d, int64_t window) {
   if (check_dims(d) != SSM_OK || window < 1) return 0;
   return bwd_ws_bytes(d, window < d->T ? window : d->T, true, false);
@@ -347,7 +380,7 @@ size_t ssm_workspace_bytes(const ssm_dims* d, int64_t window, int32_t K) {
   if (K < 0 || window < 0) return 0;
   if (K >= 1) {
     if (window < 1) return 0;
-    return stack_ws_bytes(d, window, K);
+    return stack_ws_bytes(d, window, K, 0);
   }
   if (window == 0) return fwd_ws_bytes(d);
   return bwd_ws_bytes(d, window, true);
@@ -415,7 +448,11 @@ ssm_status ssm_adjoint_grad_timed(const ssm_dims* d, const ssm_layer* L, const v
                                   void* stream, void* const* events, int32_t n_events) {
   ssm::Marks mk;
   mk.ev = events;
-  mk.n = n_events;
+  mk.n = n_events < 7 ? n_events : 7;
+  if (events && n_events > 7) {
+    mk.slab_ev = events + 7;
+    mk.slab_n = n_events - 7;
+  }
   return adjoint_impl(d, L, x, sv, g, window, gr, ws, ws_bytes, stream, mk);
 }
 
@@ -425,6 +462,7 @@ ssm_status ssm_stack_grad(int32_t K, const ssm_dims* d, const ssm_layer* layers,
   ssm_status s = check_dims(d);
   if (s != SSM_OK) return s;
   if (K < 1 || !layers || !grads) return SSM_ERR_ARG;
+  if (K > 64) return SSM_ERR_UNSUPPORTED;
   for (int32_t k = 0; k < K; k++) {
     if ((s = check_layer(&layers[k])) != SSM_OK) return s;
     if ((s = check_grads(&grads[k])) != SSM_OK) return s;
@@ -434,7 +472,8 @@ ssm_status ssm_stack_grad(int32_t K, const ssm_dims* d, const ssm_layer* layers,
   if ((dx0 && !aligned16(dx0)) || (xK && !aligned16(xK))) return SSM_ERR_ARG;
   if (window < 1) return SSM_ERR_ARG;
   const int64_t W = window < d->T ? window : d->T;
-  if ((s = check_ws(ws, ws_bytes, stack_ws_bytes(d, W, K))) != SSM_OK) return s;
+  const int32_t KN = count_norm(K, layers);
+  if ((s = check_ws(ws, ws_bytes, stack_ws_bytes(d, W, K, KN))) != SSM_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = d->io == SSM_BF16;
   const int64_t TP = d->T * d->P;
@@ -443,13 +482,14 @@ ssm_status ssm_stack_grad(int32_t K, const ssm_dims* d, const ssm_layer* layers,
   Carver cv(ws);
   ssm_saved saved[64];
   ssm_saved* sv = saved;
-  if (K > 64) return SSM_ERR_UNSUPPORTED;
   for (int32_t k = 0; k < K; k++) sv[k] = carve_saved(cv, d);
   char* xs = cv.take<char>(static_cast<size_t>(K) * xbytes);
   float* r = cv.take<float>(static_cast<size_t>(TP));
   float* y = cv.take<float>(static_cast<size_t>(TP));
   float* delta = cv.take<float>(static_cast<size_t>(TP));
-  NormWs nw = carve_norm(cv, d, K);
+  NormWs nw = carve_norm(cv, d, KN);
+  int32_t nslot[64];  // rank of each normalising layer among them (its r^k, 1/rms slot)
+  for (int32_t k = 0, q = 0; k < K; k++) nslot[k] = layers[k].norm_scale ? q++ : -1;
   const size_t shared_off = cv.off;
   const int64_t T = d->T, P = d->P;
   // x^k = io(r^k), or the normalised stream for a layer with norm_scale
@@ -457,8 +497,8 @@ ssm_status ssm_stack_grad(int32_t K, const ssm_dims* d, const ssm_layer* layers,
   auto make_input = [&](int32_t k) -> hipError_t {
     void* xk = xs + static_cast<size_t>(k) * xbytes;
     if (layers[k].norm_scale)
-      return ssm::rmsnorm_forward(T, P, r, layers[k].norm_scale, ssm::kNormEps, xk, bf, nw.rinv + k * T,
-                                  nw.rk + static_cast<size_t>(k) * TP, st);
+      return ssm::rmsnorm_forward(T, P, r, layers[k].norm_scale, ssm::kNormEps, xk, bf, nw.rinv + nslot[k] * T,
+                                  nw.rk + static_cast<size_t>(nslot[k]) * TP, st);
     return ssm::residual_update(TP, r, nullptr, xk, bf, st);
   };
 
@@ -485,7 +525,7 @@ ssm_status ssm_stack_grad(int32_t K, const ssm_dims* d, const ssm_layer* layers,
   for (int32_t k = K - 1; k >= 0; k--) {
     void* xk = xs + static_cast<size_t>(k) * xbytes;
     Carver bc(static_cast<char*>(ws) + shared_off);
-    BwdWs bw = carve_bwd(bc, d, W, true);
+    BwdWs bw = carve_bwd(bc, d, W, true, true, true);
     // layer k is driven by delta^{k+1}; then delta^k = delta^{k+1} + dx^k, or
     // + the normalisation's VJP of dx^k
     if (layers[k].norm_scale) {
@@ -493,7 +533,8 @@ ssm_status ssm_stack_grad(int32_t K, const ssm_dims* d, const ssm_layer* layers,
       gl.dx = nw.dx;
       if ((e = run_backward(d, &layers[k], xk, &sv[k], delta, W, &gl, nullptr, bw, st)) != hipSuccess)
         return SSM_ERR_HIP;
-      if ((e = ssm::rmsnorm_vjp(T, P, nw.rk + static_cast<size_t>(k) * TP, nw.rinv + k * T, layers[k].norm_scale,
+      if ((e = ssm::rmsnorm_vjp(T, P, nw.rk + static_cast<size_t>(nslot[k]) * TP, nw.rinv + nslot[k] * T,
+                                layers[k].norm_scale,
                                 nw.dx, nw.m, delta, nw.part, grads[k].dnorm_scale, st)) != hipSuccess)
         return SSM_ERR_HIP;
     } else {

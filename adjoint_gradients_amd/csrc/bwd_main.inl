@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   const int grp = lane / CH, pl = lane % CH;
   const int64_t T = a.T, P = a.P;
   const int C = a.C;
-  const int64_t k = blockIdx.x;
+  const int64_t k = a.k_lo + blockIdx.x;  // chunk (the launch covers one slab)
   const int64_t cb = static_cast<int64_t>(blockIdx.y) * kWpb + w;
   const bool wave_live = cb < NB;
   const int64_t p = cb * CH + pl;
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   float* const dxb = a.dxdir ? a.dxdir : static_cast<float*>(a.dY);
   const int64_t ldy_b = a.ldy * static_cast<int64_t>(sizeof(IO)), ldx_b = P * 4;
   float* xw = lds + 2 * STG + kWpb * RED;  // [kWpb][S][OUT]
-  float* hsg = a.hsub + hsub_offset(k, wave_live ? cb : 0, 0, NB, nsub_max, NL);
+  float* hsg = a.hsub + hsub_offset(k - a.hsub_k0, wave_live ? cb : 0, 0, NB, nsub_max, NL);
   const IO* xp = static_cast<const IO*>(a.x);
   const int64_t t0 = k * C;
   const int64_t t1 = (t0 + C < T) ? t0 + C : T;

@@ -15,6 +15,8 @@
 // on the same XCD (the hardware deals workgroups round-robin over the 8 XCDs),
 // which keeps the shared operand band in that XCD's L2.
 
+#include <type_traits>
+
 namespace gbf {
 
 constexpr int BM = 256, BN = 256, BK = 64;
@@ -215,11 +217,16 @@ hipError_t run_t(const GemmOperands& op, int splits, int64_t kps, Epi epi, hipSt
 
 // The three layouts this library uses: projections (A, B both K-contiguous),
 // weight gradient (both K-outer), input cotangent (A K-contiguous, B K-outer).
+// Each epilogue is instantiated for its own GEMM's layout only.
 template <class Epi>
 hipError_t run(const GemmOperands& op, int splits, int64_t kps, Epi epi, hipStream_t st) {
-  if (op.a_kc && op.b_kc) return run_t<Epi, true, true>(op, splits, kps, epi, st);
-  if (!op.a_kc && !op.b_kc) return run_t<Epi, false, false>(op, splits, kps, epi, st);
-  if (op.a_kc && !op.b_kc) return run_t<Epi, true, false>(op, splits, kps, epi, st);
+  if constexpr (std::is_same_v<Epi, EpiProj>) {
+    if (op.a_kc && op.b_kc) return run_t<Epi, true, true>(op, splits, kps, epi, st);
+  } else if constexpr (std::is_same_v<Epi, EpiPart>) {
+    if (!op.a_kc && !op.b_kc) return run_t<Epi, false, false>(op, splits, kps, epi, st);
+  } else {
+    if (op.a_kc && !op.b_kc) return run_t<Epi, true, false>(op, splits, kps, epi, st);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -482,11 +482,18 @@ hipError_t run_t(const GemmOperands& op, int splits, int64_t kps, Epi epi, hipSt
   return hipGetLastError();
 }
 
+// Each epilogue is instantiated for the operand layouts its GEMM has: the
+// projection X W_cat^T (both K-contiguous), the weight gradient dY^T X (both
+// K-outer) and the input cotangent dY W_cat (A K-contiguous, B K-outer).
 template <class Epi>
 hipError_t run(const GemmOperands& op, int splits, int64_t kps, Epi epi, hipStream_t st) {
-  if (op.a_kc && op.b_kc) return run_t<Epi, true, true>(op, splits, kps, epi, st);
-  if (!op.a_kc && !op.b_kc) return run_t<Epi, false, false>(op, splits, kps, epi, st);
-  if (op.a_kc && !op.b_kc) return run_t<Epi, true, false>(op, splits, kps, epi, st);
+  if constexpr (std::is_same_v<Epi, EpiProj>) {
+    if (op.a_kc && op.b_kc) return run_t<Epi, true, true>(op, splits, kps, epi, st);
+  } else if constexpr (std::is_same_v<Epi, EpiPart>) {
+    if (!op.a_kc && !op.b_kc) return run_t<Epi, false, false>(op, splits, kps, epi, st);
+  } else {
+    if (op.a_kc && !op.b_kc) return run_t<Epi, true, false>(op, splits, kps, epi, st);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void k_bwd_hsub(BwdArgs a, int64_t NB) {
   const int grp = lane / CH, pl = lane % CH;
   const int64_t T = a.T, P = a.P;
   const int C = a.C;
-  const int64_t k = blockIdx.x;
+  const int64_t k = a.k_lo + blockIdx.x;  // chunk (the launch covers one slab)
   const int64_t cb = static_cast<int64_t>(blockIdx.y) * kWpb + w;
   const bool wave_live = cb < NB;
   const int64_t p = cb * CH + pl;
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256) void k_bwd_hsub(BwdArgs a, int64_t NB) {
   const int64_t t1 = (t0 + C < T) ? t0 + C : T;
   const int len = static_cast<int>(t1 - t0);
   const int nsub_max = (C + S - 1) / S;
-  float* hsg = a.hsub + hsub_offset(k, wave_live ? cb : 0, 0, NB, nsub_max, NL);
+  float* hsg = a.hsub + hsub_offset(k - a.hsub_k0, wave_live ? cb : 0, 0, NB, nsub_max, NL);
   {
     const int per = len * NN / 4;
     const float4* s4 = reinterpret_cast<const float4*>(a.b + t0 * NN);
@@ -569,12 +569,25 @@ bool bwd_plan(int64_t P, int64_t N, int C, BwdPlan* pl) {
   return true;
 }
 
-size_t bwd_hsub_floats(int64_t T, int64_t P, int64_t N, int C) {
+size_t bwd_hsub_floats_chunks(int64_t chunks, int64_t P, int64_t N, int C) {
   BwdPlan pl;
   if (!bwd_plan(P, N, C, &pl)) return 0;
-  const int64_t K = (T + C - 1) / C;
   const int64_t nsub = (C + pl.S - 1) / pl.S;
-  return static_cast<size_t>(K * pl.NB * nsub) * pl.NL * 64;
+  return static_cast<size_t>(chunks * pl.NB * nsub) * pl.NL * 64;
+}
+
+size_t bwd_hsub_floats(int64_t T, int64_t P, int64_t N, int C) {
+  return bwd_hsub_floats_chunks((T + C - 1) / C, P, N, C);
+}
+
+int64_t bwd_hsub_slab_chunks(int64_t T, int64_t P, int64_t N, int C) {
+  const int64_t K = (T + C - 1) / C;
+  const size_t per = bwd_hsub_floats_chunks(1, P, N, C) * sizeof(float);
+  if (per == 0) return K;
+  int64_t n = static_cast<int64_t>(kHsubSlabBytes / per);
+  if (n >= 32) n -= n % 32;  // whole rounds of resident workgroups when the channel blocks allow
+  if (n < 1) n = 1;
+  return n < K ? n : K;
 }
 
 // ----------------------------------------------------------------- launchers
@@ -614,22 +627,6 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     }
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  BwdArgs am = a;  // arguments of the main kernel
-  am.hsub_ready = a.hsub_given ? 1 : 0;
-  if (!a.hsub_given) {
-    constexpr int NNc = NL * G;
-    const size_t rows_b = static_cast<size_t>(a.C) * NNc * 4;
-    if (NNc % 4 == 0 && rows_b <= kHsubRowLds) {
-      auto hk = k_bwd_hsub<IO, NL, G>;
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(hk), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(rows_b));
-      if (e != hipSuccess) return e;
-      k_bwd_hsub<IO, NL, G>
-          <<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(pl.NBW)), 64 * kWpb, rows_b, st>>>(a, NB);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      am.hsub_ready = 1;
-    }
-  }
   a.marks.rec(1, st);
   const int64_t PN = a.P * a.N;
   if (compose) {
@@ -643,13 +640,44 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
                                                                       compose ? a.carry : a.umu, a.carry);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.marks.rec(2, st);
+  // Sub-chunk start states and the fused reverse walk.  States kept by the
+  // forward cover every chunk: one launch.  Otherwise the gradient rebuilds
+  // them slab by slab into a region that holds a.hsub_chunks chunks, each
+  // slab's rebuild pass followed by the reverse walk over the same chunks,
+  // so the region's size does not grow with T.
   auto kern = k_bwd_main<IO, NL, G, WIN>;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(pl.lds_bytes));
   if (e != hipSuccess) return e;
-  kern<<<dim3(static_cast<unsigned>(K), static_cast<unsigned>(pl.NBW)), pl.wpb * 64, pl.lds_bytes, st>>>(am, pl.NB,
-                                                                                                    pl.NBW);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  constexpr int NNh = NL * G;
+  const size_t rows_h = static_cast<size_t>(a.C) * NNh * 4;
+  const bool hpass = !a.hsub_given && NNh % 4 == 0 && rows_h <= kHsubRowLds;
+  if (hpass) {
+    auto hk = k_bwd_hsub<IO, NL, G>;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(hk), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(rows_h));
+    if (e != hipSuccess) return e;
+  }
+  const int64_t slab = a.hsub_given ? K : a.hsub_chunks;
+  if (slab < 1) return hipErrorInvalidValue;
+  int si = 0;
+  for (int64_t k_lo = 0; k_lo < K; k_lo += slab, si++) {
+    const int64_t nk = (K - k_lo < slab) ? K - k_lo : slab;
+    BwdArgs am = a;  // arguments of this slab's launches
+    am.k_lo = k_lo;
+    am.hsub_k0 = a.hsub_given ? 0 : k_lo;
+    am.hsub_ready = a.hsub_given ? 1 : 0;
+    const dim3 grid(static_cast<unsigned>(nk), static_cast<unsigned>(pl.NBW));
+    if (hpass) {
+      k_bwd_hsub<IO, NL, G><<<grid, 64 * kWpb, rows_h, st>>>(am, NB);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      am.hsub_ready = 1;
+    }
+    a.marks.rec_slab(2 * si, st);
+    kern<<<grid, pl.wpb * 64, pl.lds_bytes, st>>>(am, pl.NB, pl.NBW);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    a.marks.rec_slab(2 * si + 1, st);
+  }
   a.marks.rec(3, st);
   const int OUT = 2 * static_cast<int>(a.N);
   k_bwd_reduce_dbdc<IO><<<static_cast<unsigned>((a.T * OUT + 255) / 256), 256, 0, st>>>(

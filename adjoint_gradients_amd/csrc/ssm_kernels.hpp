@@ -9,20 +9,29 @@ namespace ssm {
 
 // Optional timing marks: caller-owned hipEvent_t handles recorded on the
 // stream at the boundaries of the internal phases (NULL entries skipped).
+// Optional per-launch marks bracket each launch of the fused reverse kernel
+// (entries 2 s and 2 s + 1 around the launch over chunk slab s).
 struct Marks {
   void* const* ev = nullptr;
   int n = 0;
+  void* const* slab_ev = nullptr;
+  int slab_n = 0;
   void rec(int i, hipStream_t st) const {
     if (ev && i < n && ev[i]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), st);
+  }
+  void rec_slab(int i, hipStream_t st) const {
+    if (slab_ev && i < slab_n && slab_ev[i]) (void)hipEventRecord(static_cast<hipEvent_t>(slab_ev[i]), st);
   }
 };
 
 // Sub-chunk start states of the gradient kernel: the state entering token
 // kC + kSub u of chunk k, for channel block cb (CH = 64 / G channels) and lane
 // l = grp CH + pl of the scan layout, state n = grp NL + j, stored at float
-// offset hsub_offset(k, cb, u, NB, nsub_max, NL) + j 64 + l, nsub_max =
-// ceil(C / kSub).  Written either by the final forward scan (when the caller
-// keeps them) or by a pass of the gradient.
+// offset hsub_offset(k - k0, cb, u, NB, nsub_max, NL) + j 64 + l, nsub_max =
+// ceil(C / kSub), where k0 is the first chunk the region holds.  Written
+// either by the final forward scan for every chunk (k0 = 0, when the caller
+// keeps them) or by a pass of the gradient, one slab of chunks at a time
+// into a region of the workspace that holds one slab.
 constexpr int kSub = 8;  // tokens per recomputed sub-chunk
 __host__ __device__ constexpr int64_t hsub_offset(int64_t k, int64_t cb, int64_t u, int64_t NB, int64_t nsub_max,
                                                   int NL) {
@@ -64,9 +73,12 @@ struct BwdArgs {
   float* part;          // [T][NBW][2N] per-workgroup partial sums of db | dc
   float* dal_part;      // [K][P][N]
   float* dbias_part;    // [K][P]
-  float* hsub;          // per-wavefront sub-chunk start states (bwd_hsub_floats)
+  float* hsub;          // per-wavefront sub-chunk start states (hsub_offset layout)
   int hsub_ready;       // 1: a separate pass already wrote hsub (the main kernel skips its walk)
-  int hsub_given;       // 1: hsub was written by the forward (no pass needed)
+  int hsub_given;       // 1: hsub was written by the forward for every chunk (no pass needed)
+  int64_t hsub_chunks;  // chunks the hsub region holds (the slab; all chunks when given)
+  int64_t k_lo;         // first chunk of a launch over a slab (set by the launcher)
+  int64_t hsub_k0;      // chunk held by the region's first slot (set by the launcher)
   // outputs of the scan
   void* dY;             // [T][ldy] io: columns [0,P) = dDelta, [P,P+N) = db, [P+N,P+2N) = dc
   int64_t ldy;
@@ -85,7 +97,15 @@ struct BwdPlan {
   size_t lds_bytes;     // dynamic LDS of the main kernel
 };
 bool bwd_plan(int64_t P, int64_t N, int C, BwdPlan* plan);
+// Floats of sub-chunk states for `chunks` chunks.
+size_t bwd_hsub_floats_chunks(int64_t chunks, int64_t P, int64_t N, int C);
+// Floats of sub-chunk states for every chunk of T tokens (the forward's h_sub).
 size_t bwd_hsub_floats(int64_t T, int64_t P, int64_t N, int C);
+// Chunks per slab of the gradient's own sub-chunk-state region: at most
+// kHsubSlabBytes of states, a multiple of 32 chunks when that many fit, never
+// more than the chunk count.
+constexpr size_t kHsubSlabBytes = size_t(1) << 30;
+int64_t bwd_hsub_slab_chunks(int64_t T, int64_t P, int64_t N, int C);
 
 hipError_t launch_forward_scan(const FwdArgs& a, bool bf16, hipStream_t st);
 

@@ -5,7 +5,8 @@ One step = ssm_forward (projection GEMM, chunked forward scan with h
 checkpoints, y) + ssm_adjoint_grad (windowed reverse adjoint scan fused with
 the local VJPs, channel/chunk reductions, weight-gradient GEMM) on a
 1,048,576-token, 2048-channel, N=16 layer with bf16 x and weights, fp32
-state, window 4096 and checkpoints every 256 tokens.  Inputs are synthetic,
+state, window 4096 and h stored only at the 256-token chunk boundaries (the
+gradient rebuilds the states inside each chunk).  Inputs are synthetic,
 seeded and resident in HBM before the timed region.  Prints one JSON line.
 """
 import argparse
@@ -20,14 +21,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 WORKLOADS = {
-    # name: (index in ssm_inputs.CASES, window, chunk)
-    "layer1m": (3, 4096, 256),       # 1M tokens, P = 2048, N = 16, bf16
-    "layer128k": (2, 8192, 256),     # 128K tokens, P = 2048, N = 16, bf16
-    "layer128k_w1k": (2, 1024, 256),
-    "layer16k": (1, 2048, 256),      # 16K tokens, P = 1024, N = 16, fp32
-    "layer16k_exact": (1, 16384, 256),
-    "stack4": (4, 4096, 256),  # the 4-layer residual stack (ssm_stack_grad), timed whole
-    "stack4_norm": (4, 4096, 256),  # the same stack, every layer reading the RMS-normalised stream
+    # name: (index in ssm_inputs.CASES, window, chunk, sub-chunk states kept by the forward)
+    "layer1m": (3, 4096, 256, False),        # 1M tokens, P = 2048, N = 16, bf16, chunk checkpoints only
+    "layer1m_substates": (3, 4096, 256, True),  # the same, the forward also keeps every 8th token's state
+    "layer128k": (2, 8192, 256, False),      # 128K tokens, P = 2048, N = 16, bf16
+    "layer128k_w1k": (2, 1024, 256, False),
+    "layer16k": (1, 2048, 256, False),       # 16K tokens, P = 1024, N = 16, fp32
+    "layer16k_exact": (1, 16384, 256, False),
+    "stack4": (4, 4096, 256, False),  # the 4-layer residual stack (ssm_stack_grad), timed whole
+    "stack4_norm": (4, 4096, 256, False),  # the same stack, every layer reading the RMS-normalised stream
 }
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -37,7 +39,9 @@ MFMA_F32_PEAK_TFS = 157.3
 VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
 
 FWD_PHASES = ["proj_gemm", "fwd_local", "fwd_carry", "fwd_final"]
-BWD_PHASES = ["bwd_local", "bwd_carry", "bwd_main", "bwd_reduce", "wgrad_gemm", "dx_gemm"]
+# bwd_hsub (the sub-chunk-state rebuild passes) and bwd_main (the fused
+# reverse kernel) alternate slab by slab between the carry and reduction marks
+BWD_PHASES = ["bwd_local", "bwd_carry", "bwd_hsub", "bwd_main", "bwd_reduce", "wgrad_gemm", "dx_gemm"]
 
 
 def algorithmic(name, T, P, N, C, W, s_io, sub_states=False):
@@ -78,6 +82,9 @@ def algorithmic(name, T, P, N, C, W, s_io, sub_states=False):
         return (T * (8 * P + 4 * N) + K * P * N * 4, 0, (10 if win and not compose else 5) * E)
     if name == "bwd_carry":
         return (K * P * N * 8 + K * P * 8, 0, (9 if compose else 4) * K * P * N)
+    if name == "bwd_hsub":
+        # recompute from the checkpoints: no bytes or work of the method's own
+        return (0, 0, 0)
     if name == "bwd_main":
         # per token: x, s, g, b, c, dDelta (io) and db/dc, plus h_ckpt once per chunk
         return (T * (P * s_io + 4 * P + 4 * P + 8 * N + P * s_io + 8 * N) + K * P * N * 4 + sub, 0,
@@ -194,8 +201,10 @@ def cpu_baseline(case, window, chunk, tokens):
     oracle.layer_grad(o, window=window if window < tokens else None, want_dx=False)
     wall = time.perf_counter() - t0
     return {"value": tokens / wall, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"fp64 oracle forward+adjoint+VJP+weight grads on the first {tokens} tokens of the "
-                      f"{case.name} workload (P={case.P}, N={case.N}, window={window}); wall {wall:.2f} s"}
+            "sample": f"fp64 oracle forward+adjoint+VJP+weight grads on the first {tokens} of the "
+                      f"{case.T} tokens of the {case.name} workload (P={case.P}, N={case.N}, window={window}); "
+                      f"wall {wall:.2f} s; value = that prefix's tokens / wall (the oracle's cost is linear "
+                      f"in T at a fixed window)"}
 
 
 def study_truncation():
@@ -319,15 +328,15 @@ def bench_stack(args, case_idx, window, chunk, norm=False):
     x0 = (torch.randn(T, P, generator=gen, device=dev) * case.x_scale).to(torch.bfloat16)
     g = torch.randn(T, P, generator=gen, device=dev)
     dims = agm.make_dims(T, P, N, chunk, "bf16")
-    ws = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, window, K), dev)
+    L = [lay.struct(dims) for lay in lays]
+    ws = agm.alloc_workspace(agm.ssm_stack_workspace_bytes(K, dims, L, window), dev)
     grads = [agm.alloc_grads(dims, device=dev) for _ in range(K)]
     if norm:
         for gr in grads:
             gr["dnorm_scale"] = torch.empty(P, device=dev, dtype=torch.float32)
     dx0 = torch.empty(T, P, device=dev, dtype=torch.float32)
     xK = torch.empty(T, P, device=dev, dtype=torch.float32)
-    L = [lay.struct() for lay in lays]
-    G = [agm.grads_struct(gr) for gr in grads]
+    G = [agm.grads_struct(gr, dims) for gr in grads]
 
     def step():
         agm.ssm_stack_grad(K, dims, L, x0, g, window, G, dx0, xK, ws, ws.numel())
@@ -369,9 +378,6 @@ def main():
     ap.add_argument("--source-hash", metavar="PHASE", default=None,
                     help="print the hash of the sources a phase's kernels are built from and exit")
     ap.add_argument("--phases", action="store_true", help="print the per-phase breakdown to stderr")
-    ap.add_argument("--no-sub-states", action="store_true",
-                    help="the forward keeps only the chunk checkpoints (the gradient rebuilds the "
-                         "sub-chunk states in a pass of its own)")
     ap.add_argument("--study", choices=("truncation", "memory"), default=None,
                     help="run a measurement study instead of the benchmark (JSON lines on stdout)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -409,7 +415,7 @@ def main():
     import adjoint_gradients_amd as agm
     from ssm_inputs import CASES, make_layer_device
 
-    case_idx, window, chunk = WORKLOADS[args.workload]
+    case_idx, window, chunk, sub_states = WORKLOADS[args.workload]
     if CASES[case_idx].K > 1:
         bench_stack(args, case_idx, window, chunk, norm=args.workload.endswith("norm"))
         return
@@ -429,14 +435,15 @@ def main():
     x, g = inp["x_dev"], inp["g_dev"]
     dims = agm.make_dims(T, P, N, chunk, io)
     ws_f = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, 0, 0), dev)
-    saved = agm.alloc_saved(dims, dev, sub_states=not args.no_sub_states)
-    ws_b = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, window, 0) if args.no_sub_states
-                               else agm.ssm_grad_workspace_bytes_sub(dims, window), dev)
+    saved = agm.alloc_saved(dims, dev, sub_states=sub_states)
+    ws_b = agm.alloc_workspace(agm.ssm_grad_workspace_bytes_sub(dims, window) if sub_states
+                               else agm.ssm_workspace_bytes(dims, window, 0), dev)
     grads = agm.alloc_grads(dims, device=dev)
     y = torch.empty(T, P, device=dev, dtype=torch.float32)
-    L = lay.struct()
-    S = agm.saved_struct(saved)
-    G = agm.grads_struct(grads)
+    L = lay.struct(dims)
+    S = agm.saved_struct(saved, dims)
+    G = agm.grads_struct(grads, dims)
+    nslab = agm.ssm_grad_slab_count(dims, window, sub_states)
     stream = torch.cuda.current_stream()
 
     hev = HipEvents()
@@ -457,7 +464,7 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, phase events recorded on the library's stream
-    evs = [(new_events(5), new_events(7)) for _ in range(args.steps)]
+    evs = [(new_events(5), new_events(7 + 2 * nslab)) for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -470,17 +477,25 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
 
+    # gradient marks: [0] start [1] local [2] carry [3] slabs done [4] reductions
+    # [5] wgrad [6] dx, then [7 + 2 s], [8 + 2 s] around the fused kernel's launch
+    # over slab s; the rebuild passes fill the rest of [2]..[3]
     phase_ms = {k: 0.0 for k in FWD_PHASES + BWD_PHASES}
+    marks = {"bwd_local": (0, 1), "bwd_carry": (1, 2), "bwd_reduce": (3, 4), "wgrad_gemm": (4, 5),
+             "dx_gemm": (5, 6)}
     for evf, evb in evs:
         for i, k in enumerate(FWD_PHASES):
             phase_ms[k] += hev.ms(evf[i], evf[i + 1]) / args.steps
-        for i, k in enumerate(BWD_PHASES):
-            phase_ms[k] += hev.ms(evb[i], evb[i + 1]) / args.steps
+        for k, (i, j) in marks.items():
+            phase_ms[k] += hev.ms(evb[i], evb[j]) / args.steps
+        main = sum(hev.ms(evb[7 + 2 * q], evb[8 + 2 * q]) for q in range(nslab))
+        phase_ms["bwd_main"] += main / args.steps
+        phase_ms["bwd_hsub"] += (hev.ms(evb[2], evb[3]) - main) / args.steps
     hev.destroy()
 
     rows = []
     for k, ms in phase_ms.items():
-        by, fl, ops = algorithmic(k, T, P, N, chunk, window, s_io, not args.no_sub_states)
+        by, fl, ops = algorithmic(k, T, P, N, chunk, window, s_io, sub_states)
         rows.append((k, ms, by / (ms * 1e-3) / 1e9 if ms > 0 else 0.0, fl / (ms * 1e-3) / 1e12 if ms > 0 else 0.0,
                      ops / (ms * 1e-3) / 1e9 if ms > 0 else 0.0))
     if args.phases:
@@ -489,22 +504,29 @@ def main():
             print(f"{k:12s} {ms:9.3f} {gbs:9.1f} {tfs:9.1f} {gops:11.1f}", file=sys.stderr)
         print(f"step {ms_per_step:.3f} ms (events), host wall {wall_ms / args.steps:.3f} ms/step", file=sys.stderr)
 
-    dom = max(rows, key=lambda r: r[1])
+    # the dominant kernel among the phases of the method's own work (the
+    # rebuild passes are recompute, with no algorithmic bytes or work)
+    dom = max((r for r in rows if r[0] != "bwd_hsub"), key=lambda r: r[1])
     name, ms = dom[0], dom[1]
-    by, fl, ops = algorithmic(name, T, P, N, chunk, window, s_io, not args.no_sub_states)
+    by, fl, ops = algorithmic(name, T, P, N, chunk, window, s_io, sub_states)
+    # per launch: the fused reverse kernel runs once per slab of chunks (equal
+    # slabs at this workload), every other phase once per step
+    nl = nslab if name == "bwd_main" else 1
+    ms_l, by_l, fl_l, ops_l = ms / nl, by / nl, fl / nl, ops / nl
+    hbm_ach = by_l / (ms_l * 1e-3) / 1e9
     if fl > 0:
         peak = MFMA_BF16_PEAK_TFS if io == "bf16" else MFMA_F32_PEAK_TFS
-        ach = fl / (ms * 1e-3) / 1e12
+        ach = fl_l / (ms_l * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak}
     else:
-        ach = ops / (ms * 1e-3) / 1e9
+        ach = ops_l / (ms_l * 1e-3) / 1e9
         roof = {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_GOPS, "unit": "Gop/s",
-                "frac": ach / VALU_PEAK_GOPS}
+                "frac": ach / VALU_PEAK_GOPS, "valu_frac": ach / VALU_PEAK_GOPS}
     # HBM bytes per launch from the stored counter reading (None if the kernel changed since)
-    roof["traffic"] = stored_traffic(name, args.workload)
+    st = stored_traffic(name, args.workload)
+    roof["traffic"] = None if st is None else st
     roof["traffic_unit"] = "bytes/launch"
-    hbm_ach = by / (ms * 1e-3) / 1e9
-    roof.update(kernel=name, ms=ms, algorithmic_bytes=by, hbm_achieved_gbs=hbm_ach,
+    roof.update(kernel=name, launches_per_step=nl, ms=ms_l, algorithmic_bytes=by_l, hbm_achieved_gbs=hbm_ach,
                 hbm_frac=hbm_ach / HBM_PEAK_GBS)
 
     out = {
@@ -521,9 +543,11 @@ def main():
         "dtype": "bf16" if io == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": f"{case.name}: one selective SSM layer, T={T}, P={P}, N={N}, io={io}, "
-                               f"fp32 state, window={window}, checkpoint every {chunk} tokens",
+                               f"fp32 state, window={window}, h stored only at {chunk}-token chunk boundaries"
+                               + (" and before every 8th token (the forward keeps the sub-chunk states)"
+                                  if sub_states else " (the gradient rebuilds the states inside each chunk)"),
                    "T": T, "P": P, "N": N, "window": window, "chunk": chunk,
-                   "sub_states_saved": not args.no_sub_states},
+                   "sub_states_saved": sub_states, "fused_kernel_launches": nslab},
         "roofline": roof,
         "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
     }

@@ -109,7 +109,8 @@ typedef struct {
  * ssm_adjoint_grad reads it instead of re-walking each chunk to rebuild it:
  * more saved memory (T*P*N/8 floats, 16 GiB at T = 2^20, P = 2048, N = 16,
  * against 0.5 GiB of chunk checkpoints) for one pass less in the gradient,
- * whose workspace then shrinks by as much (ssm_grad_workspace_bytes_sub).
+ * whose workspace then drops the region in which it would rebuild them
+ * (ssm_grad_workspace_bytes_sub).
  * h_sub must be NULL in both calls or, in the gradient call, hold what
  * ssm_forward wrote for the same dims, x and layer. */
 typedef struct {
@@ -148,14 +149,37 @@ size_t ssm_saved_bytes(const ssm_dims *dims);
 size_t ssm_sub_state_bytes(const ssm_dims *dims);
 
 /* Workspace bytes needed by ssm_forward (window = 0, K = 0), by
- * ssm_adjoint_grad (window >= 1, K = 0) or by ssm_stack_grad (K >= 1).
- * 0 if the arguments are invalid or unsupported. */
+ * ssm_adjoint_grad (window >= 1, K = 0) or by ssm_stack_grad (K >= 1) for a
+ * stack in which no layer normalises its input (for other stacks see
+ * ssm_stack_workspace_bytes).  0 if the arguments are invalid or unsupported.
+ *
+ * The gradient's workspace does not hold the state sequence: when the
+ * forward kept no sub-chunk states (saved->h_sub NULL), the gradient rebuilds
+ * them from the chunk checkpoints slab by slab of chunks into a region of at
+ * most 1 GiB (the segment recomputation of "Training Deep Nets with
+ * Sublinear Memory Cost"), so apart from that region the workspace is
+ * O(T (P + 2N)) for the GEMM operand and the channel partials plus
+ * O((T / C) P N) for the chunk aggregates. */
 size_t ssm_workspace_bytes(const ssm_dims *dims, int64_t window, int32_t K);
+
+/* Workspace bytes of ssm_stack_grad for these K layers (host array of
+ * structs): like ssm_workspace_bytes(dims, window, K), plus the buffers of
+ * the layers that normalise their input (norm_scale set): the residual
+ * stream r^k (T*P floats) and 1/rms (T floats) per such layer, and one dx
+ * and row scratch.  0 if the arguments are invalid. */
+size_t ssm_stack_workspace_bytes(int32_t K, const ssm_dims *dims, const ssm_layer *layers, int64_t window);
 
 /* Workspace bytes of ssm_adjoint_grad (window >= 1) when saved->h_sub is set:
  * smaller than ssm_workspace_bytes(dims, window, 0) by the region that would
- * otherwise hold the sub-chunk states.  0 if the arguments are invalid. */
+ * otherwise hold a slab of sub-chunk states.  0 if the arguments are invalid. */
 size_t ssm_grad_workspace_bytes_sub(const ssm_dims *dims, int64_t window);
+
+/* Number of slabs of chunks ssm_adjoint_grad processes (each slab: the
+ * rebuild of its sub-chunk states, then the fused reverse adjoint + VJP
+ * kernel over it): 1 when the forward kept the sub-chunk states
+ * (sub_states_given != 0).  Instrumentation (see ssm_adjoint_grad_timed);
+ * 0 if the arguments are invalid. */
+int32_t ssm_grad_slab_count(const ssm_dims *dims, int64_t window, int32_t sub_states_given);
 
 /*
  * Forward pass of one layer: the projections, the chunked scan of the
@@ -173,7 +197,9 @@ ssm_status ssm_forward(const ssm_dims *dims, const ssm_layer *layer, const void 
  * to the window W (truncated adjoint sharding).  Needs the saved state of
  * ssm_forward for the same x and layer.
  *   g [T][P] float32 cotangent of y; window >= 1 (>= T means exact).
- *   grads: outputs (see ssm_grads).
+ *   grads: outputs (see ssm_grads).  grads->dx, when set, also serves as
+ *   the buffer of the direct term sum_n mu b before the input-cotangent GEMM
+ *   adds the projections' part in place, so it must not overlap any input.
  *   ws: at least ssm_workspace_bytes(dims, window, 0) bytes, or, when
  *       saved->h_sub is set, ssm_grad_workspace_bytes_sub(dims, window).
  */
@@ -198,8 +224,10 @@ ssm_status ssm_adjoint_grad(const ssm_dims *dims, const ssm_layer *layer, const 
  *   x0 [T][P] io; g [T][P] float32
  *   dx0 [T][P] float32 or NULL: dL/dx0
  *   xK  [T][P] float32 or NULL: the final residual stream r^K
- *   ws: at least ssm_workspace_bytes(dims, window, K) bytes; it also holds
- *   the saved states of all K layers.
+ *   ws: at least ssm_stack_workspace_bytes(K, dims, layers, window) bytes
+ *   (= ssm_workspace_bytes(dims, window, K) when no layer normalises); it
+ *   also holds the saved states of all K layers.  SSM_ERR_WORKSPACE if it is
+ *   smaller.
  */
 ssm_status ssm_stack_grad(int32_t K, const ssm_dims *dims, const ssm_layer *layers, const void *x0,
                           const float *g, int64_t window, const ssm_grads *grads, float *dx0,
@@ -213,10 +241,13 @@ ssm_status ssm_stack_grad(int32_t K, const ssm_dims *dims, const ssm_layer *laye
  *   forward : [0] start  [1] after the projection GEMM  [2] after the
  *             chunk-local scan  [3] after the chunk carry  [4] after the final scan
  *   gradient: [0] start  [1] after the chunk-local adjoint aggregates
- *             [2] after the adjoint carry  [3] after the fused adjoint + VJP
- *             kernel  [4] after the channel / chunk reductions  [5] after the
- *             weight-gradient GEMM  [6] after the input-cotangent GEMM (or
- *             its absence).
+ *             [2] after the adjoint carry  [3] after the last slab's fused
+ *             adjoint + VJP kernel  [4] after the channel / chunk reductions
+ *             [5] after the weight-gradient GEMM  [6] after the input-cotangent
+ *             GEMM (or its absence); then [7 + 2 s] and [8 + 2 s] just before
+ *             and just after the fused kernel's launch over slab s
+ *             (s < ssm_grad_slab_count), so that [2]..[3] less those launches
+ *             is the time of the sub-chunk-state rebuild passes.
  * events may be NULL only when n_events == 0.
  */
 ssm_status ssm_forward_timed(const ssm_dims *dims, const ssm_layer *layer, const void *x, float *y,

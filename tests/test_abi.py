@@ -78,7 +78,7 @@ def _fake(addr=0x100000):
 
 def _layer(agm, misalign=False):
     a = 0x200000 + (4 if misalign else 0)
-    return agm.Layer(a, 0x300000, 0x400000, 0x500000, None)
+    return agm.Layer(a, 0x300000, 0x400000, 0x500000, None, None)
 
 
 def _saved(agm, null_field=None):
@@ -157,3 +157,63 @@ def test_stack_validation(agm):
     with_dx = (agm.Grads * K)(_grads(agm), agm.Grads(0xB00000, 0xC00000, 0xD00000, None, None, 0xE00000))
     assert call(gs=with_dx) == 1
     assert call(nbytes=256) == 2
+
+
+def test_gradient_workspace_is_bounded(agm):
+    # the 1M-token layer (T = 2^20, P = 2048, N = 16, bf16, chunk 256, window
+    # 4096): without sub-chunk states kept by the forward, the gradient
+    # rebuilds them slab by slab in a region of at most 1 GiB; dx_dir lives
+    # in the dx output, so the workspace is the GEMM operand, the channel
+    # partials, the chunk aggregates and that region
+    gib = 1 << 30
+    d = agm.make_dims(1 << 20, 2048, 16, 256, "bf16")
+    full = agm.ssm_workspace_bytes(d, 4096, 0)
+    sub = agm.ssm_grad_workspace_bytes_sub(d, 4096)
+    assert full <= 10 * gib, full / gib
+    assert 0 < full - sub <= gib
+    assert agm.ssm_sub_state_bytes(d) == (1 << 20) // 8 * 2048 * 16 * 4
+    slabs = agm.ssm_grad_slab_count(d, 4096, False)
+    assert slabs == 16 and agm.ssm_grad_slab_count(d, 4096, True) == 1
+    # doubling T doubles the slab count, not the region
+    d2 = agm.make_dims(1 << 21, 2048, 16, 256, "bf16")
+    assert agm.ssm_grad_slab_count(d2, 4096, False) == 2 * slabs
+    assert agm.ssm_workspace_bytes(d2, 4096, 0) - agm.ssm_grad_workspace_bytes_sub(d2, 4096) == full - sub
+    # a short sequence: one slab holding every chunk
+    d3 = agm.make_dims(1000, 48, 16, 64, "f32")
+    assert agm.ssm_grad_slab_count(d3, 100, False) == 1
+
+
+def test_stack_workspace_counts_normalising_layers(agm):
+    d = agm.make_dims(1000, 48, 16, 64, "f32")
+    plain = (agm.Layer * 3)(_layer(agm), _layer(agm), _layer(agm))
+    one = (agm.Layer * 3)(_layer(agm), agm.Layer(0x200000, 0x300000, 0x400000, 0x500000, None, 0xF00000),
+                          _layer(agm))
+    base = agm.lib.ssm_stack_workspace_bytes(3, ctypes.byref(d), plain, 100)
+    assert base == agm.ssm_workspace_bytes(d, 100, 3) > 0
+    with_norm = agm.lib.ssm_stack_workspace_bytes(3, ctypes.byref(d), one, 100)
+    # one layer's r^k (T P floats) and 1/rms (T floats), one dx (T P), row scratch
+    assert with_norm - base >= (2 * 1000 * 48 + 2 * 1000) * 4
+    # a stack with a normalising layer and only the plain size is refused
+    grads = (agm.Grads * 3)(_grads(agm), _grads(agm), _grads(agm))
+    rc = agm.lib.ssm_stack_grad(3, ctypes.byref(d), one, 0x1000000, 0x2000000, 100, grads, None, None,
+                                0x3000000, base, None)
+    assert rc == 2
+
+
+def test_binding_checks_tensors_before_the_call(agm):
+    import torch
+
+    d = agm.make_dims(64, 8, 4, 16)
+    x = torch.zeros(64, 8)
+    with pytest.raises(agm.SsmError, match="GPU tensor"):
+        agm._need(x, "x", 64 * 8, torch.float32)
+    if torch.cuda.is_available():
+        x = x.cuda()
+        with pytest.raises(agm.SsmError, match="contiguous"):
+            agm._need(x.t(), "x", 64 * 8, torch.float32)
+        with pytest.raises(agm.SsmError, match="dtype"):
+            agm._need(x.to(torch.bfloat16), "x", 64 * 8, torch.float32)
+        with pytest.raises(agm.SsmError, match="elements"):
+            agm._need(x[:32], "x", 64 * 8, torch.float32)
+    with pytest.raises(agm.SsmError, match="required"):
+        agm.saved_struct({}, d)

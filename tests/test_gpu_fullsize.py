@@ -1,8 +1,11 @@
 """Parity at the full workload sizes, in the launch configuration the
-benchmark times (checkpoint interval 256, bf16 x and weights, fp32 state).
+benchmark times (checkpoint interval 256, bf16 x and weights, fp32 state),
+with the states inside each chunk rebuilt by the gradient from the chunk
+checkpoints (the benchmark's mode; slabs of 256 chunks at P = 2048, N = 16)
+and with the sub-chunk states kept by the forward.
 
 - 128K-token layer (T=131072, P=2048, N=16): the whole oracle, every output,
-  windows 1024 and 8192.
+  windows 1024 and 8192 (two slabs).
 - 1M-token layer (T=1048576, P=2048, N=16, window 4096, the benchmark's
   workload with its device-drawn inputs): every output the oracle can
   compute per channel (y, saved s, dW_delta rows, dalpha, dbias) on sampled
@@ -46,12 +49,14 @@ def orc():
     return oracle
 
 
+@pytest.mark.parametrize("sub_states", [False, True])
 @pytest.mark.parametrize("window,want_dx", [(1024, True), (8192, False)])
-def test_layer128k_full_oracle(orc, window, want_dx):
+def test_layer128k_full_oracle(orc, window, want_dx, sub_states):
     case = CASES[2]
     inp = make_layer(case)
-    say(f"case {case.name} full: T={case.T} P={case.P} N={case.N} W={window} C={CHUNK} dx={want_dx}")
-    got = gpu_layer(inp, window, CHUNK, want_dx=want_dx, sub_states=True)
+    say(f"case {case.name} full: T={case.T} P={case.P} N={case.N} W={window} C={CHUNK} dx={want_dx} "
+        f"sub_states={sub_states}")
+    got = gpu_layer(inp, window, CHUNK, want_dx=want_dx, sub_states=sub_states)
     o = oracle_inputs(inp)
     ref = orc.layer_grad(o, window=window, want_dx=want_dx)
     keys = [k for k in GRAD_KEYS if want_dx or k[0] != "dx"]
@@ -62,7 +67,7 @@ def test_layer128k_full_oracle(orc, window, want_dx):
     say(f"  max error {max(errs.values()):.2e}")
 
 
-def _device_layer(case, window, chans):
+def _device_layer(case, window, chans, sub_states):
     """Runs forward + adjoint gradient on device-drawn inputs; returns the
     per-channel GPU outputs of `chans` and the host inputs the oracle needs."""
     import torch
@@ -81,7 +86,7 @@ def _device_layer(case, window, chans):
                            w(inp["delta_bias"]))
     dims = agm.make_dims(T, P, N, CHUNK, case.io)
     x, g = inp["x_dev"], inp["g_dev"]
-    y, saved = agm.forward(dims, lay, x, sub_states=True)  # as the benchmark runs it
+    y, saved = agm.forward(dims, lay, x, sub_states=sub_states)
     grads = agm.adjoint_grad(dims, lay, x, saved, g, window, want_dx=False)
     torch.cuda.synchronize()
     ci = torch.as_tensor(chans, device=dev, dtype=torch.long)
@@ -112,14 +117,15 @@ def _sampled_channels(case, bias):
     return np.array(sorted(chans), dtype=np.int64)
 
 
-def _check_sampled(orc, case, window):
+def _check_sampled(orc, case, window, sub_states=False):
     from ssm_inputs import _bias, _weights  # noqa: F401  (bias is needed before the GPU run)
 
     rng = np.random.Generator(np.random.PCG64(case.seed))
     _weights(rng, case)
     chans = _sampled_channels(case, _bias(rng, case))
-    say(f"case {case.name} sampled: T={case.T} P={case.P} N={case.N} W={window} C={CHUNK} chans={chans.tolist()}")
-    got, host, g_cols = _device_layer(case, window, chans)
+    say(f"case {case.name} sampled: T={case.T} P={case.P} N={case.N} W={window} C={CHUNK} "
+        f"sub_states={sub_states} chans={chans.tolist()}")
+    got, host, g_cols = _device_layer(case, window, chans, sub_states)
     assert got["finite"], "non-finite gradient"
     T = case.T
     win = None if window >= T else window
@@ -142,8 +148,9 @@ def _check_sampled(orc, case, window):
     assert not bad, f"over tolerance {TOL[case.io]}: {bad}"
 
 
-def test_layer1m_bench_workload_sampled(orc):
-    _check_sampled(orc, CASES[3], 4096)
+@pytest.mark.parametrize("sub_states", [False, True])
+def test_layer1m_bench_workload_sampled(orc, sub_states):
+    _check_sampled(orc, CASES[3], 4096, sub_states)
 
 
 @pytest.mark.parametrize("window", [4096, 262144])

@@ -225,6 +225,24 @@ def test_determinism_and_linearity():
         assert np.array_equal(c[k], 2.0 * a[k]), k
 
 
+def test_slabs_ragged(orc):
+    # 300 chunks of 256 tokens at P = 1024, N = 32 (4 MiB of sub-chunk states
+    # per chunk): the gradient rebuilds them in slabs of 256 chunks (1 GiB),
+    # so the second slab is a ragged one of 44.  fp32, a window (1000) that is
+    # not a whole number of chunks and the exact gradient, with the states
+    # rebuilt slab by slab and with them kept by the forward.
+    T, P, N, C = 300 * 256, 1024, 32, 256
+    inp = make_layer(small_case(T, P, N, 51))
+    o = oracle_inputs(inp)
+    for W in (1000, T):
+        ref = orc.layer_grad(o, window=None if W >= T else W)
+        for sub in (False, True):
+            label = f"slabs T={T} P={P} N={N} W={W} sub_states={sub}"
+            say(f"case {label}")
+            got = gpu_layer(inp, W, C, sub_states=sub)
+            compare(got, ref, GRAD_KEYS, TOL["f32"], label)
+
+
 def test_layer16k(orc):
     inp = make_layer(CASES[1])
     for W in (16384, 2048):

@@ -41,6 +41,7 @@ EXPORTED = (
     "ssm_stack_workspace_bytes",
     "ssm_forward",
     "ssm_adjoint_grad",
+    "ssm_adjoint_grad_noalloc",
     "ssm_stack_grad",
     "ssm_forward_timed",
     "ssm_adjoint_grad_timed",
@@ -103,6 +104,9 @@ def _load():
                                      ctypes.c_int64, P(Grads), ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p]
     lib.ssm_adjoint_grad.restype = ctypes.c_int
+    lib.ssm_adjoint_grad_noalloc.argtypes = [P(Dims), P(Layer), ctypes.c_void_p, P(Saved), ctypes.c_void_p,
+                                             ctypes.c_int64, P(Grads), ctypes.c_void_p]
+    lib.ssm_adjoint_grad_noalloc.restype = ctypes.c_int
     lib.ssm_stack_grad.argtypes = [ctypes.c_int32, P(Dims), P(Layer), ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_int64, P(Grads), ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
@@ -278,6 +282,21 @@ def ssm_adjoint_grad(dims: Dims, layer: Layer, x, saved: Saved, g, window: int, 
     _check(lib.ssm_adjoint_grad(ctypes.byref(dims), ctypes.byref(layer), _ptr(x), ctypes.byref(saved), _ptr(g),
                                 int(window), ctypes.byref(grads), _ptr(ws), int(ws_bytes), _stream(stream)),
            "ssm_adjoint_grad")
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20  # SSM_NOALLOC_SCRATCH_BYTES of the C header
+
+
+def ssm_adjoint_grad_noalloc(dims: Dims, layer: Layer, x, saved: Saved, g, window: int, grads: Grads,
+                             stream=None):
+    """ssm_adjoint_grad with the library's own device array as workspace."""
+    import torch
+
+    _need(x, "x", dims.T * dims.P, _io(dims))
+    _need(g, "g", dims.T * dims.P, torch.float32)
+    _check(lib.ssm_adjoint_grad_noalloc(ctypes.byref(dims), ctypes.byref(layer), _ptr(x), ctypes.byref(saved),
+                                        _ptr(g), int(window), ctypes.byref(grads), _stream(stream)),
+           "ssm_adjoint_grad_noalloc")
 
 
 def _event_array(events):

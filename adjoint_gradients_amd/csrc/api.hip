@@ -16,6 +16,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/ssm_adjoint.h"
 #include "ssm_kernels.hpp"
 
@@ -157,9 +159,10 @@ struct BwdWs {
 
 // own_hsub: the workspace holds a slab of sub-chunk states (the caller did
 // not keep them); own_dxdir: the direct input cotangent needs a buffer of its
-// own (the stack, whose cotangent stream is read while it is written)
+// own (the stack, whose cotangent stream is read while it is written);
+// slab_chunks > 0: chunks per slab instead of the default
 BwdWs carve_bwd(Carver& cv, const ssm_dims* d, int64_t W, bool need_dx, bool own_hsub = true,
-                bool own_dxdir = false) {
+                bool own_dxdir = false, int64_t slab_chunks = 0) {
   BwdWs w;
   BwdPlan pl;
   ssm::bwd_plan(d->P, d->N, d->chunk, &pl);
@@ -176,7 +179,9 @@ BwdWs carve_bwd(Carver& cv, const ssm_dims* d, int64_t W, bool need_dx, bool own
   w.hwin = win ? cv.take<double>(static_cast<size_t>(K * P)) : nullptr;
   w.dal_part = cv.take<float>(static_cast<size_t>(K * P * N));
   w.dbias_part = cv.take<float>(static_cast<size_t>(K * P));
-  w.hsub_chunks = own_hsub ? ssm::bwd_hsub_slab_chunks(T, P, N, d->chunk) : K;
+  w.hsub_chunks = !own_hsub ? K
+                  : slab_chunks > 0 ? (slab_chunks < K ? slab_chunks : K)
+                                    : ssm::bwd_hsub_slab_chunks(T, P, N, d->chunk);
   w.hsub = own_hsub ? cv.take<float>(ssm::bwd_hsub_floats_chunks(w.hsub_chunks, P, N, d->chunk)) : nullptr;
   w.splits = splitk_for(d);
   w.wpart = cv.take<float>(static_cast<size_t>(w.splits) * M * P);
@@ -201,9 +206,10 @@ size_t fwd_ws_bytes(const ssm_dims* d) {
   return cv.off;
 }
 
-size_t bwd_ws_bytes(const ssm_dims* d, int64_t W, bool need_dx, bool own_hsub = true, bool own_dxdir = false) {
+size_t bwd_ws_bytes(const ssm_dims* d, int64_t W, bool need_dx, bool own_hsub = true, bool own_dxdir = false,
+                    int64_t slab_chunks = 0) {
   Carver cv(nullptr);
-  carve_bwd(cv, d, W, need_dx, own_hsub, own_dxdir);
+  carve_bwd(cv, d, W, need_dx, own_hsub, own_dxdir, slab_chunks);
   return cv.off;
 }
 
@@ -330,6 +336,40 @@ hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, co
 
 }  // namespace
 
+// ---------------------------------------------------------------- no-allocation gradient
+// ssm_adjoint_grad_noalloc takes its workspace from this array instead of the
+// caller.  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address is obtained once per device with
+// hipGetSymbolAddress (each device holds its own copy) and only that address
+// is used.  Calls on one device share the array, so calls that overlap on a
+// device race; nothing in it needs to start at zero (every element the
+// gradient reads was written earlier in the same call).
+constexpr size_t kNoAllocScratchBytes = SSM_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+struct ScratchTable {
+  std::mutex mu;
+  void* ptr[kMaxDevices] = {};
+};
+static ScratchTable g_scratch;
+
+// Device address of the current device's scratch array (looked up on its
+// first use on that device, with that device current).
+static ssm_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SSM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SSM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch.mu);
+  if (!g_scratch.ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SSM_ERR_HIP;
+    g_scratch.ptr[dev] = p;
+  }
+  *out = g_scratch.ptr[dev];
+  return SSM_OK;
+}
+
 extern "C" {
 
 int32_t ssm_version(void) { return 300; }
@@ -402,9 +442,9 @@ static ssm_status forward_impl(const ssm_dims* d, const ssm_layer* L, const void
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
-static ssm_status adjoint_impl(const ssm_dims* d, const ssm_layer* L, const void* x, const ssm_saved* sv,
-                               const float* g, int64_t window, const ssm_grads* gr, void* ws, size_t ws_bytes,
-                               void* stream, ssm::Marks mk) {
+// Argument checks of the single-layer gradient (everything but the workspace).
+static ssm_status check_adjoint(const ssm_dims* d, const ssm_layer* L, const void* x, const ssm_saved* sv,
+                                const float* g, int64_t window, const ssm_grads* gr) {
   ssm_status s = check_dims(d);
   if (s != SSM_OK) return s;
   if ((s = check_layer(L)) != SSM_OK) return s;
@@ -413,15 +453,50 @@ static ssm_status adjoint_impl(const ssm_dims* d, const ssm_layer* L, const void
   if ((s = check_grads(gr)) != SSM_OK) return s;
   if (!x || !g || !aligned16(x) || !aligned16(g)) return SSM_ERR_ARG;
   if (window < 1) return SSM_ERR_ARG;
+  return SSM_OK;
+}
+
+static ssm_status adjoint_impl(const ssm_dims* d, const ssm_layer* L, const void* x, const ssm_saved* sv,
+                               const float* g, int64_t window, const ssm_grads* gr, void* ws, size_t ws_bytes,
+                               void* stream, ssm::Marks mk, int64_t slab_chunks = 0) {
+  ssm_status s = check_adjoint(d, L, x, sv, g, window, gr);
+  if (s != SSM_OK) return s;
   if (mk.n < 0 || (mk.n > 0 && !mk.ev)) return SSM_ERR_ARG;
   const int64_t W = window < d->T ? window : d->T;
   const bool need_dx = gr->dx != nullptr;
   const bool own_hsub = sv->h_sub == nullptr;
-  if ((s = check_ws(ws, ws_bytes, bwd_ws_bytes(d, W, need_dx, own_hsub))) != SSM_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, bwd_ws_bytes(d, W, need_dx, own_hsub, false, slab_chunks))) != SSM_OK) return s;
   Carver cv(ws);
-  BwdWs w = carve_bwd(cv, d, W, need_dx, own_hsub);
+  BwdWs w = carve_bwd(cv, d, W, need_dx, own_hsub, false, slab_chunks);
   hipError_t e = run_backward(d, L, x, sv, g, W, gr, nullptr, w, static_cast<hipStream_t>(stream), mk);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+
+ssm_status ssm_adjoint_grad_noalloc(const ssm_dims* d, const ssm_layer* L, const void* x, const ssm_saved* sv,
+                                    const float* g, int64_t window, const ssm_grads* gr, void* stream) {
+  ssm_status s = check_adjoint(d, L, x, sv, g, window, gr);
+  if (s != SSM_OK) return s;
+  const int64_t W = window < d->T ? window : d->T;
+  const bool need_dx = gr->dx != nullptr;
+  const bool own_hsub = sv->h_sub == nullptr;
+  // everything but the sub-chunk-state slab must fit; the rest of the array
+  // holds as large a slab as fits (at most the default one)
+  const size_t fixed = bwd_ws_bytes(d, W, need_dx, false);
+  if (fixed > kNoAllocScratchBytes) return SSM_ERR_WORKSPACE;
+  int64_t slab = 0;
+  if (own_hsub) {
+    const size_t per = ssm::bwd_hsub_floats_chunks(1, d->P, d->N, d->chunk) * sizeof(float);
+    const size_t room = kNoAllocScratchBytes - fixed;
+    slab = per ? static_cast<int64_t>(room / per) : 0;
+    while (slab > 0 && bwd_ws_bytes(d, W, need_dx, true, false, slab) > kNoAllocScratchBytes) slab--;
+    if (slab < 1) return SSM_ERR_WORKSPACE;
+    const int64_t dflt = ssm::bwd_hsub_slab_chunks(d->T, d->P, d->N, d->chunk);
+    if (slab > dflt) slab = dflt;
+  }
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws)) != SSM_OK) return s;
+  return adjoint_impl(d, L, x, sv, g, window, gr, ws, kNoAllocScratchBytes, stream, ssm::Marks{}, slab);
 }
 
 ssm_status ssm_forward(const ssm_dims* d, const ssm_layer* L, const void* x, float* y, const ssm_saved* sv,

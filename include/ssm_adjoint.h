@@ -48,9 +48,10 @@
  *     SSM_ERR_WORKSPACE or SSM_ERR_UNSUPPORTED nothing has been launched.
  *     SSM_ERR_HIP reports a failed launch; faults inside kernels surface at
  *     the caller's next synchronisation.
- *   - The library keeps no mutable global state: calls on different
- *     workspaces are independent; calls sharing a workspace must be ordered
- *     (same stream).
+ *   - The library keeps no mutable global state except for
+ *     ssm_adjoint_grad_noalloc's device array (see there): calls on
+ *     different workspaces are independent; calls sharing a workspace must be
+ *     ordered (same stream).
  *   - Results are bitwise repeatable for identical inputs, dims and window.
  *
  * Supported shapes: T >= 1, P >= 1, N in {1, 2, 4, 8, 16, 32, 64},
@@ -206,6 +207,28 @@ ssm_status ssm_forward(const ssm_dims *dims, const ssm_layer *layer, const void 
 ssm_status ssm_adjoint_grad(const ssm_dims *dims, const ssm_layer *layer, const void *x,
                             const ssm_saved *saved, const float *g, int64_t window,
                             const ssm_grads *grads, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * ssm_adjoint_grad without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving or
+ * training loops, harnesses that forbid hipMalloc).  It computes the same
+ * gradient with the same kernels (bitwise equal to ssm_adjoint_grad) and
+ * calls no hipMalloc, hipFree or other allocating routine: its workspace is a
+ * device array of SSM_NOALLOC_SCRATCH_BYTES bytes inside the library, one per
+ * device, held until the process ends.  Whatever the gradient's fixed buffers
+ * leave of it holds the slab of rebuilt sub-chunk states, so a larger problem
+ * runs more, smaller slabs.  Returns SSM_ERR_WORKSPACE (nothing launched) when
+ * the fixed buffers -- the GEMM operand dY (T (P + 2N) io elements), the
+ * channel partials, the chunk aggregates and the split-K partials -- plus one
+ * chunk of sub-chunk states exceed the array.  Every call on a device shares
+ * that device's array: calls that may overlap in time on one device (other
+ * streams, other threads) race and must be ordered by the caller.  No part of
+ * the array needs to start at zero.
+ */
+#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+ssm_status ssm_adjoint_grad_noalloc(const ssm_dims *dims, const ssm_layer *layer, const void *x,
+                                    const ssm_saved *saved, const float *g, int64_t window,
+                                    const ssm_grads *grads, void *stream);
 
 /*
  * Residual stack of K layers (Section 3.2, Proposition 3):

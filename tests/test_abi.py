@@ -217,3 +217,17 @@ def test_binding_checks_tensors_before_the_call(agm):
             agm._need(x[:32], "x", 64 * 8, torch.float32)
     with pytest.raises(agm.SsmError, match="required"):
         agm.saved_struct({}, d)
+
+
+def test_noalloc_refuses_oversize_before_launch(agm):
+    # the 1M-token layer's fixed gradient buffers (GB) exceed the library's
+    # array: refused by the size check, before any device call
+    d = agm.make_dims(1 << 20, 2048, 16, 256, "bf16")
+    L, S, G = _layer(agm), _saved(agm), _grads(agm)
+    rc = agm.lib.ssm_adjoint_grad_noalloc(ctypes.byref(d), ctypes.byref(L), 0x1000000, ctypes.byref(S),
+                                          0x2000000, 4096, ctypes.byref(G), None)
+    assert rc == 2
+    # argument errors come first, as in ssm_adjoint_grad
+    rc = agm.lib.ssm_adjoint_grad_noalloc(ctypes.byref(d), ctypes.byref(L), 0x1000000, ctypes.byref(S),
+                                          0x2000000, 0, ctypes.byref(G), None)
+    assert rc == 1

@@ -147,6 +147,7 @@ struct BwdWs {
   float* part;
   float* umu;
   float* carry;
+  float* edge;
   double* ps64;
   double* hwin;
   float* dal_part;
@@ -175,6 +176,7 @@ BwdWs carve_bwd(Carver& cv, const ssm_dims* d, int64_t W, bool need_dx, bool own
   w.part = cv.take<float>(static_cast<size_t>(T * pl.NBW * 2 * N));
   w.umu = cv.take<float>(static_cast<size_t>(K * P * N + P));  // + P: also the chunk-reduction scratch
   w.carry = cv.take<float>(static_cast<size_t>(K * P * N));
+  w.edge = cv.take<float>(static_cast<size_t>(P * N));
   w.ps64 = win ? cv.take<double>(static_cast<size_t>((K + 1) * P)) : nullptr;
   w.hwin = win ? cv.take<double>(static_cast<size_t>(K * P)) : nullptr;
   w.dal_part = cv.take<float>(static_cast<size_t>(K * P * N));
@@ -300,7 +302,7 @@ hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, co
   a.T = T; a.P = P; a.N = N; a.W = W; a.C = d->chunk;
   a.s = sv->s; a.x = x; a.b = sv->b; a.c = sv->c; a.alpha = L->alpha; a.h_ckpt = sv->h_ckpt;
   a.ssum = sv->s_sum; a.g = g;
-  a.ps64 = w.ps64; a.hwin = w.hwin; a.umu = w.umu; a.carry = w.carry; a.part = w.part;
+  a.ps64 = w.ps64; a.hwin = w.hwin; a.umu = w.umu; a.carry = w.carry; a.edge = w.edge; a.part = w.part;
   a.dal_part = w.dal_part; a.dbias_part = w.dbias_part;
   a.hsub = sv->h_sub ? sv->h_sub : w.hsub;
   a.hsub_given = sv->h_sub ? 1 : 0;
@@ -374,7 +376,7 @@ extern "C" {
 
 int32_t ssm_version(void) { return 300; }
 
-const char* ssm_status_str(ssm_status s) {
+const char* ssm_status_str(int32_t s) {
   switch (s) {
     case SSM_OK: return "SSM_OK";
     case SSM_ERR_ARG: return "SSM_ERR_ARG: invalid argument";

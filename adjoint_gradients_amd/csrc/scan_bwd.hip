@@ -402,29 +402,153 @@ __global__ __launch_bounds__(256) void k_bwd_hsub(BwdArgs a, int64_t NB) {
   }
 }
 
+// The chunk-local reverse aggregate and the sub-chunk start states in one
+// forward walk over the chunk (exact aggregates: no window term inside the
+// walk), for slabs processed right to left.  The aggregate of chunk k with a
+// zero carry entering from its right,
+//   umu[k] = a_{t0} mu^loc_{t0} = sum_{t in k} g_t c_t prod_{j=t0}^{t} a_j ,
+// is accumulated in token order with the running product
+// Q_t = prod_{j=t0}^{t} a_j, so the same decay factors serve the state
+// recurrence h_t = a_t h_{t-1} + b_t x_t, whose value entering every kSub-th
+// token goes to the sub-chunk-state slab (layout of k_bwd_hsub).  A 4-wavefront
+// workgroup takes 4 channel blocks of one chunk; the chunk's b and c rows are
+// staged once into LDS, s, x and g come through an 8-token register ring.
+template <typename IO, int NL, int G>
+__global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
+  constexpr int CH = 64 / G;
+  constexpr int NN = NL * G;
+  constexpr int D = kBwdLocRing;
+  constexpr int S = kSub;
+  extern __shared__ float rows[];  // [C][NN] b rows, then [C][NN] c rows
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+  const int grp = lane / CH, pl = lane % CH;
+  const int64_t T = a.T, P = a.P;
+  const int C = a.C;
+  const int64_t k = a.k_lo + blockIdx.x;  // chunk (the launch covers one slab)
+  const int64_t cb = static_cast<int64_t>(blockIdx.y) * kWpb + w;
+  const bool wave_live = cb < NB;
+  const int64_t p = cb * CH + pl;
+  const bool valid = wave_live && p < P;
+  const int64_t pc = p < P ? p : P - 1;
+  const int n0 = grp * NL;
+  const int64_t t0 = k * C;
+  const int64_t t1 = (t0 + C < T) ? t0 + C : T;
+  const int len = static_cast<int>(t1 - t0);
+  const int nsub_max = (C + S - 1) / S;
+  float* hsg = a.hsub + hsub_offset(k - a.hsub_k0, wave_live ? cb : 0, 0, NB, nsub_max, NL);
+  float* crow = rows + static_cast<size_t>(C) * NN;
+  {
+    const int per = len * NN / 4;
+    const float4* b4 = reinterpret_cast<const float4*>(a.b + t0 * NN);
+    const float4* c4 = reinterpret_cast<const float4*>(a.c + t0 * NN);
+    float4* db4 = reinterpret_cast<float4*>(rows);
+    float4* dc4 = reinterpret_cast<float4*>(crow);
+    for (int e = tid; e < per; e += 64 * kWpb) {
+      db4[e] = b4[e];
+      dc4[e] = c4[e];
+    }
+  }
+  float al2[NL], h[NL], Q[NL], U[NL];
+#pragma unroll
+  for (int j = 0; j < NL; j++) {
+    al2[j] = a.alpha[pc * NN + n0 + j] * kLog2e;
+    h[j] = a.h_ckpt[(k * P + pc) * NN + n0 + j];
+    Q[j] = 1.0f;
+    U[j] = 0.0f;
+  }
+  const IO* xp = static_cast<const IO*>(a.x);
+  const uint32_t ob4 = static_cast<uint32_t>(pc) * 4u;
+  const uint32_t obx = static_cast<uint32_t>(pc) * static_cast<uint32_t>(sizeof(IO));
+  float rs[D], rg[D];
+  typename IoRaw<IO>::type rx[D];
+  auto ld = [&](int slot, int64_t t) {
+    rs[slot] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.s + t * P) + ob4);
+    rg[slot] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.g + t * P) + ob4);
+    rx[slot] = load_raw(reinterpret_cast<const IO*>(reinterpret_cast<const char*>(xp + t * P) + obx));
+  };
+#pragma unroll
+  for (int q = 0; q < D - 1; q++)
+    if (q < len) ld(q, t0 + q);
+  __syncthreads();  // staged rows visible
+  static_assert(D % S == 0 || S % D == 0, "ring and sub-chunk sizes");
+  auto tok = [&](int r, int tau, bool fetch, int ahead) {
+    if (tau % S == 0 && wave_live) {
+#pragma unroll
+      for (int j = 0; j < NL; j++) hsg[((tau / S) * NL + j) * 64 + lane] = h[j];
+    }
+    if (fetch) ld((r + D - 1) % D, t0 + ahead);
+    const float ns = -rs[r];
+    const float xv = raw_to_f32(rx[r]);
+    const float gv = rg[r];
+    const float* rb = rows + tau * NN + n0;
+    const float* rc = crow + tau * NN + n0;
+#pragma unroll
+    for (int j = 0; j < NL; j += 4) {
+      const float4 vb = *reinterpret_cast<const float4*>(rb + j);
+      const float4 vc = *reinterpret_cast<const float4*>(rc + j);
+      const float bq[4] = {vb.x, vb.y, vb.z, vb.w};
+      const float cq[4] = {vc.x, vc.y, vc.z, vc.w};
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const float av = fast_exp2(ns * al2[j + jj]);
+        h[j + jj] = fmaf(av, h[j + jj], bq[jj] * xv);
+        Q[j + jj] *= av;
+        U[j + jj] = fmaf(gv * cq[jj], Q[j + jj], U[j + jj]);
+      }
+    }
+  };
+  if (len % D == 0) {
+    // whole ring turns: fetches past the chunk end re-read its last token,
+    // so the ring body has no per-token branch
+    for (int q8 = 0; q8 < len; q8 += D) {
+#pragma unroll
+      for (int r = 0; r < D; r++) {
+        const int tau = q8 + r;
+        tok(r, tau, true, (tau + D - 1 < len) ? tau + D - 1 : len - 1);
+      }
+    }
+  } else {
+    for (int q8 = 0; q8 < len; q8 += D) {
+#pragma unroll
+      for (int r = 0; r < D; r++) {
+        const int tau = q8 + r;
+        if (tau < len) tok(r, tau, tau + D - 1 < len, tau + D - 1);
+      }
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < NL; j++) a.umu[(k * P + p) * NN + n0 + j] = U[j];
+  }
+}
+
 // Carry of the adjoint sums between chunks, right to left:
 //   carry[K-1] = 0,  carry[k-1] = A_k carry[k] + umu[k],  A_k = exp(-alpha sum_{t in k} s_t).
 // carry[k] is a_{e+1} mu_{e+1} for the last token e of chunk k.  umu may be
 // carry itself (windowed aggregates composed in place): each element is read
-// before it is overwritten, by the same thread.
-__global__ __launch_bounds__(256) void k_bwd_carry(int64_t K, int64_t P, int64_t N,
+// before it is overwritten, by the same thread.  One launch walks chunks
+// k_hi - 1 down to k_lo: the carry entering chunk k_hi - 1 comes from `edge`
+// (written by the launch over the chunks to the right; zero when k_hi = K),
+// and the carry the walk hands on to chunk k_lo - 1 is left in `edge`.
+__global__ __launch_bounds__(256) void k_bwd_carry(int64_t K, int64_t P, int64_t N, int64_t k_lo, int64_t k_hi,
                                                    const float* __restrict__ alpha,
                                                    const double* __restrict__ ssum,
                                                    const float* umu,
-                                                   float* carry) {
+                                                   float* carry, float* __restrict__ edge) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t PN = P * N;
   if (e >= PN) return;
   const int64_t p = e / N;
   const float al2 = alpha[e] * kLog2e;
-  float cin = 0.0f;
+  float cin = k_hi < K ? edge[e] : 0.0f;
   // Blocks of 32 chunks: all loads of a block are issued before its stores
   // (umu may alias carry, so the compiler would not move a load above an
   // earlier store by itself); the walk is latency-bound with one thread per
   // (channel, state), so the deeper the block, the more loads in flight.
   constexpr int B = 32;
-  int64_t k = K - 1;
-  for (; k >= B - 1; k -= B) {
+  int64_t k = k_hi - 1;
+  for (; k - k_lo >= B - 1; k -= B) {
     float u[B], sk[B];
 #pragma unroll
     for (int r = 0; r < B; r++) {
@@ -437,11 +561,12 @@ __global__ __launch_bounds__(256) void k_bwd_carry(int64_t K, int64_t P, int64_t
       cin = fmaf(fast_exp2(-sk[r] * al2), cin, u[r]);
     }
   }
-  for (; k >= 0; k--) {
+  for (; k >= k_lo; k--) {
     const float u = umu[k * PN + e];
     carry[k * PN + e] = cin;
     cin = fmaf(fast_exp2(-static_cast<float>(ssum[k * P + p]) * al2), cin, u);
   }
+  if (k_lo > 0) edge[e] = cin;
 }
 
 // Windows of a whole number q = W / C of chunks.  The window term of chunk
@@ -460,7 +585,7 @@ __global__ __launch_bounds__(256) void k_bwd_carry(int64_t K, int64_t P, int64_t
 constexpr int64_t kComposeSpan = 32;  // chunks per thread of k_bwd_window_compose (at least)
 
 __global__ __launch_bounds__(256) void k_bwd_window_compose(int64_t K, int64_t P, int64_t N, int64_t q,
-                                                            int64_t span,
+                                                            int64_t k_lo, int64_t k_hi, int64_t span,
                                                             const float* __restrict__ alpha,
                                                             const double* __restrict__ ps64,
                                                             const float* __restrict__ umu,
@@ -472,8 +597,8 @@ __global__ __launch_bounds__(256) void k_bwd_window_compose(int64_t K, int64_t P
   const int64_t p = e / N;
   const bool first_state = (e - p * N) == 0;
   const float al2 = alpha[e] * kLog2e;
-  const int64_t k0 = static_cast<int64_t>(blockIdx.y) * span;
-  const int64_t k1 = (k0 + span < K) ? k0 + span : K;
+  const int64_t k0 = k_lo + static_cast<int64_t>(blockIdx.y) * span;
+  const int64_t k1 = (k0 + span < k_hi) ? k0 + span : k_hi;
 #pragma unroll 4
   for (int64_t k = k0; k < k1; k++) {
     float u = umu[k * PN + e];
@@ -605,12 +730,18 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // A window of whole chunks is composed from exact chunk aggregates in the
-  // carry pass (k_bwd_carry_win); otherwise the local pass walks the window
-  // term itself.
+  // carry pass; otherwise the local pass walks the window term itself.
   const bool compose = WIN && (a.W % a.C) == 0;
-  {
-    constexpr int NNc = NL * G;
-    const bool wl = WIN && !compose;
+  const bool wl = WIN && !compose;
+  constexpr int NNc = NL * G;
+  // Without sub-chunk states from the forward, exact local aggregates and a
+  // chunk's b and c rows in LDS: the aggregates are formed in the same
+  // forward walk that rebuilds the sub-chunk states, slab by slab from the
+  // right (the carry enters each chunk from its right, so a slab needs only
+  // the aggregates of itself and of the slabs already done).
+  const size_t rows_f = static_cast<size_t>(2) * a.C * NNc * 4;
+  const bool fused = !a.hsub_given && !wl && NNc % 4 == 0 && rows_f <= kHsubRowLds;
+  if (!fused) {
     const size_t rows_b = static_cast<size_t>(wl ? 2 : 1) * a.C * NNc * 4;
     const dim3 gs(static_cast<unsigned>(K), static_cast<unsigned>((NB + kBwdLocWpb - 1) / kBwdLocWpb));
     const dim3 g1(static_cast<unsigned>(K), static_cast<unsigned>(NB));
@@ -625,58 +756,81 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
       if (staged) k_bwd_local_staged<IO, NL, G, false><<<gs, 64 * kBwdLocWpb, rows_b, st>>>(a, NB);
       else k_bwd_local<IO, NL, G, false><<<g1, 64, 0, st>>>(a);
     }
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  a.marks.rec(1, st);
-  const int64_t PN = a.P * a.N;
-  if (compose) {
-    int64_t span = (K + 65534) / 65535;  // grid y stays within its limit
-    if (span < kComposeSpan) span = kComposeSpan;
-    k_bwd_window_compose<<<dim3(static_cast<unsigned>((PN + 255) / 256), static_cast<unsigned>((K + span - 1) / span)),
-                           256, 0, st>>>(K, a.P, a.N, a.W / a.C, span, a.alpha, a.ps64, a.umu, a.carry, a.hwin);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  k_bwd_carry<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, a.alpha, a.ssum,
-                                                                      compose ? a.carry : a.umu, a.carry);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  a.marks.rec(1, st);
+  const int64_t PN = a.P * a.N;
+  // windowed aggregates of chunks [lo, hi) from exact ones (into the carry array)
+  auto compose_range = [&](int64_t lo, int64_t hi) -> hipError_t {
+    int64_t span = (hi - lo + 65534) / 65535;  // grid y stays within its limit
+    if (span < kComposeSpan) span = kComposeSpan;
+    k_bwd_window_compose<<<dim3(static_cast<unsigned>((PN + 255) / 256),
+                                static_cast<unsigned>((hi - lo + span - 1) / span)),
+                           256, 0, st>>>(K, a.P, a.N, a.W / a.C, lo, hi, span, a.alpha, a.ps64, a.umu, a.carry,
+                                         a.hwin);
+    return hipGetLastError();
+  };
+  auto carry_range = [&](int64_t lo, int64_t hi) -> hipError_t {
+    k_bwd_carry<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, lo, hi, a.alpha, a.ssum,
+                                                                        compose ? a.carry : a.umu, a.carry, a.edge);
+    return hipGetLastError();
+  };
+  if (!fused) {
+    if (compose && (e = compose_range(0, K)) != hipSuccess) return e;
+    if ((e = carry_range(0, K)) != hipSuccess) return e;
+  }
   a.marks.rec(2, st);
   // Sub-chunk start states and the fused reverse walk.  States kept by the
   // forward cover every chunk: one launch.  Otherwise the gradient rebuilds
   // them slab by slab into a region that holds a.hsub_chunks chunks, each
-  // slab's rebuild pass followed by the reverse walk over the same chunks,
-  // so the region's size does not grow with T.
+  // slab's rebuild followed by the reverse walk over the same chunks, so the
+  // region's size does not grow with T.
   auto kern = k_bwd_main<IO, NL, G, WIN>;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(pl.lds_bytes));
   if (e != hipSuccess) return e;
-  constexpr int NNh = NL * G;
-  const size_t rows_h = static_cast<size_t>(a.C) * NNh * 4;
-  const bool hpass = !a.hsub_given && NNh % 4 == 0 && rows_h <= kHsubRowLds;
+  const size_t rows_h = static_cast<size_t>(a.C) * NNc * 4;
+  const bool hpass = !a.hsub_given && !fused && NNc % 4 == 0 && rows_h <= kHsubRowLds;
   if (hpass) {
     auto hk = k_bwd_hsub<IO, NL, G>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(hk), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(rows_h));
     if (e != hipSuccess) return e;
   }
+  if (fused) {
+    auto fk = k_bwd_local_hsub<IO, NL, G>;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(fk), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(rows_f));
+    if (e != hipSuccess) return e;
+  }
   const int64_t slab = a.hsub_given ? K : a.hsub_chunks;
   if (slab < 1) return hipErrorInvalidValue;
-  int si = 0;
-  for (int64_t k_lo = 0; k_lo < K; k_lo += slab, si++) {
+  const int64_t nslab = (K + slab - 1) / slab;
+  for (int64_t q = 0; q < nslab; q++) {
+    // slabs right to left when the aggregates are formed slab by slab
+    const int64_t si = fused ? nslab - 1 - q : q;
+    const int64_t k_lo = si * slab;
     const int64_t nk = (K - k_lo < slab) ? K - k_lo : slab;
     BwdArgs am = a;  // arguments of this slab's launches
     am.k_lo = k_lo;
     am.hsub_k0 = a.hsub_given ? 0 : k_lo;
     am.hsub_ready = a.hsub_given ? 1 : 0;
     const dim3 grid(static_cast<unsigned>(nk), static_cast<unsigned>(pl.NBW));
-    if (hpass) {
+    if (fused) {
+      k_bwd_local_hsub<IO, NL, G><<<grid, 64 * kWpb, rows_f, st>>>(am, NB);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (compose && (e = compose_range(k_lo, k_lo + nk)) != hipSuccess) return e;
+      if ((e = carry_range(k_lo, k_lo + nk)) != hipSuccess) return e;
+      am.hsub_ready = 1;
+    } else if (hpass) {
       k_bwd_hsub<IO, NL, G><<<grid, 64 * kWpb, rows_h, st>>>(am, NB);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       am.hsub_ready = 1;
     }
-    a.marks.rec_slab(2 * si, st);
+    a.marks.rec_slab(static_cast<int>(2 * q), st);
     kern<<<grid, pl.wpb * 64, pl.lds_bytes, st>>>(am, pl.NB, pl.NBW);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    a.marks.rec_slab(2 * si + 1, st);
+    a.marks.rec_slab(static_cast<int>(2 * q + 1), st);
   }
   a.marks.rec(3, st);
   const int OUT = 2 * static_cast<int>(a.N);

@@ -70,6 +70,7 @@ struct BwdArgs {
   double* hwin;         // [K][P]   sum of s over the W tokens after each chunk (windowed)
   float* umu;           // [K][P][N] local adjoint aggregates
   float* carry;         // [K][P][N] adjoint carry entering each chunk from the right
+  float* edge;          // [P][N] carry handed from one slab of chunks to the next one left
   float* part;          // [T][NBW][2N] per-workgroup partial sums of db | dc
   float* dal_part;      // [K][P][N]
   float* dbias_part;    // [K][P]

@@ -39,12 +39,14 @@ MFMA_F32_PEAK_TFS = 157.3
 VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
 
 FWD_PHASES = ["proj_gemm", "fwd_local", "fwd_carry", "fwd_final"]
-# bwd_hsub (the sub-chunk-state rebuild passes) and bwd_main (the fused
-# reverse kernel) alternate slab by slab between the carry and reduction marks
-BWD_PHASES = ["bwd_local", "bwd_carry", "bwd_hsub", "bwd_main", "bwd_reduce", "wgrad_gemm", "dx_gemm"]
+# Between the carry and reduction marks the gradient alternates, slab by slab
+# of chunks, bwd_slab_prep (the rebuild of the slab's sub-chunk states, and,
+# when the forward kept none, the slab's chunk aggregates, window composition
+# and carry, formed in the same pass) with bwd_main (the fused reverse kernel).
+BWD_PHASES = ["bwd_local", "bwd_carry", "bwd_slab_prep", "bwd_main", "bwd_reduce", "wgrad_gemm", "dx_gemm"]
 
 
-def algorithmic(name, T, P, N, C, W, s_io, sub_states=False):
+def algorithmic(name, T, P, N, C, W, s_io, sub_states=False, _prep=False):
     """Per-launch algorithmic work of a phase: (bytes, flops, valu_ops).
 
     Bytes count each compulsory HBM stream once.  With sub_states the forward
@@ -78,13 +80,28 @@ def algorithmic(name, T, P, N, C, W, s_io, sub_states=False):
     # a window of whole chunks is composed from exact chunk aggregates in the
     # carry pass, so the local pass then walks no window term
     compose = win and W % C == 0
+    # without states kept by the forward, exact local aggregates whose chunk
+    # rows (b and c) fit the 64 KB staging area are formed slab by slab in
+    # the rebuild walk (phase bwd_slab_prep), with the composition and carry
+    fused = not sub_states and (not win or compose) and 2 * C * N * 4 <= 65536
+    if name in ("bwd_local", "bwd_carry") and fused and not _prep:
+        return (0, 0, 0)
     if name == "bwd_local":
         return (T * (8 * P + 4 * N) + K * P * N * 4, 0, (10 if win and not compose else 5) * E)
     if name == "bwd_carry":
         return (K * P * N * 8 + K * P * 8, 0, (9 if compose else 4) * K * P * N)
-    if name == "bwd_hsub":
-        # recompute from the checkpoints: no bytes or work of the method's own
-        return (0, 0, 0)
+    if name == "bwd_slab_prep":
+        if sub_states:
+            return (0, 0, 0)
+        # the local aggregates (bytes and slots as bwd_local) formed in the
+        # forward walk that rebuilds the states -- the rebuild itself is
+        # recompute, with no bytes or work of the method's own -- plus the
+        # composition and the carry
+        if not fused:
+            return (0, 0, 0)
+        lb, _, lo = algorithmic("bwd_local", T, P, N, C, W, s_io, False, True)
+        cb, _, co = algorithmic("bwd_carry", T, P, N, C, W, s_io, False, True)
+        return (lb + cb, 0, lo + co)
     if name == "bwd_main":
         # per token: x, s, g, b, c, dDelta (io) and db/dc, plus h_ckpt once per chunk
         return (T * (P * s_io + 4 * P + 4 * P + 8 * N + P * s_io + 8 * N) + K * P * N * 4 + sub, 0,
@@ -479,7 +496,7 @@ def main():
 
     # gradient marks: [0] start [1] local [2] carry [3] slabs done [4] reductions
     # [5] wgrad [6] dx, then [7 + 2 s], [8 + 2 s] around the fused kernel's launch
-    # over slab s; the rebuild passes fill the rest of [2]..[3]
+    # over slab s; the slab preparation passes fill the rest of [2]..[3]
     phase_ms = {k: 0.0 for k in FWD_PHASES + BWD_PHASES}
     marks = {"bwd_local": (0, 1), "bwd_carry": (1, 2), "bwd_reduce": (3, 4), "wgrad_gemm": (4, 5),
              "dx_gemm": (5, 6)}
@@ -490,7 +507,7 @@ def main():
             phase_ms[k] += hev.ms(evb[i], evb[j]) / args.steps
         main = sum(hev.ms(evb[7 + 2 * q], evb[8 + 2 * q]) for q in range(nslab))
         phase_ms["bwd_main"] += main / args.steps
-        phase_ms["bwd_hsub"] += (hev.ms(evb[2], evb[3]) - main) / args.steps
+        phase_ms["bwd_slab_prep"] += (hev.ms(evb[2], evb[3]) - main) / args.steps
     hev.destroy()
 
     rows = []
@@ -504,9 +521,8 @@ def main():
             print(f"{k:12s} {ms:9.3f} {gbs:9.1f} {tfs:9.1f} {gops:11.1f}", file=sys.stderr)
         print(f"step {ms_per_step:.3f} ms (events), host wall {wall_ms / args.steps:.3f} ms/step", file=sys.stderr)
 
-    # the dominant kernel among the phases of the method's own work (the
-    # rebuild passes are recompute, with no algorithmic bytes or work)
-    dom = max((r for r in rows if r[0] != "bwd_hsub"), key=lambda r: r[1])
+    # the dominant kernel
+    dom = max(rows, key=lambda r: r[1])
     name, ms = dom[0], dom[1]
     by, fl, ops = algorithmic(name, T, P, N, chunk, window, s_io, sub_states)
     # per launch: the fused reverse kernel runs once per slab of chunks (equal

@@ -138,8 +138,9 @@ typedef struct {
 /* Library version (major*10000 + minor*100 + patch). */
 int32_t ssm_version(void);
 
-/* Human-readable name of a status code (static string, never NULL). */
-const char *ssm_status_str(ssm_status status);
+/* Human-readable name of a status code (static string, never NULL; any
+ * value, including ones outside ssm_status, is accepted). */
+const char *ssm_status_str(int32_t status);
 
 /* Bytes of the five required ssm_saved buffers together (informational; the
  * caller may allocate them separately; h_sub not included).  0 if dims are

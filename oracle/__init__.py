@@ -97,13 +97,25 @@ def _f64(a) -> np.ndarray:
 
 
 def project(x: np.ndarray, W: np.ndarray, bias: np.ndarray | None = None,
-            block: int = 1 << 14) -> np.ndarray:
-    """out[t][m] = sum_q W[m][q] x[t][q] (+ bias[m]), float64 (row blocks of x)."""
+            block: int = 1 << 14, blas: bool = False) -> np.ndarray:
+    """out[t][m] = sum_q W[m][q] x[t][q] (+ bias[m]), float64 (row blocks of x).
+
+    blas: each row block's product by numpy's float64 matmul (a library
+    routine for the same sum, in its own summation order) instead of the
+    plain C loops -- for the million-token workloads."""
     W = _f64(W)
     T, P = x.shape
     M = W.shape[0]
     out = np.empty((T, M), dtype=np.float64)
     bias64 = _f64(bias) if bias is not None else None
+    if blas:
+        Wt = np.ascontiguousarray(W.T)
+        for t0 in range(0, T, block):
+            t1 = min(T, t0 + block)
+            np.matmul(_f64(x[t0:t1]), Wt, out=out[t0:t1])
+            if bias64 is not None:
+                out[t0:t1] += bias64
+        return out
     bptr = _pd(bias64) if bias64 is not None else ctypes.cast(None, _d)
     for t0 in range(0, T, block):
         t1 = min(T, t0 + block)
@@ -114,7 +126,7 @@ def project(x: np.ndarray, W: np.ndarray, bias: np.ndarray | None = None,
     return out
 
 
-def projections(inp: dict, x: np.ndarray | None = None, chans=None) -> dict:
+def projections(inp: dict, x: np.ndarray | None = None, chans=None, blas: bool = False) -> dict:
     """Delta (for `chans`, default all), b and c of one layer."""
     x = inp["x"] if x is None else x
     Wd = np.asarray(inp["W_delta"])
@@ -124,9 +136,9 @@ def projections(inp: dict, x: np.ndarray | None = None, chans=None) -> dict:
         Wd = Wd[chans]
         bias = bias[chans]
     return {
-        "delta": project(x, Wd, bias),
-        "b": project(x, inp["W_B"]),
-        "c": project(x, inp["W_C"]),
+        "delta": project(x, Wd, bias, blas=blas),
+        "b": project(x, inp["W_B"], blas=blas),
+        "c": project(x, inp["W_C"], blas=blas),
     }
 
 
@@ -214,7 +226,7 @@ def layer_grad(inp: dict, window: int | None = None, method: str = "auto",
 
 
 def channel_grad(inp: dict, chans, window: int | None = None, method: str = "auto",
-                 g_cols: np.ndarray | None = None) -> dict:
+                 g_cols: np.ndarray | None = None, blas: bool = False, bc: dict | None = None) -> dict:
     """Per-channel results for a subset of channels (large workloads).
 
     Channels are independent once b and c (which need every channel of x) are
@@ -222,6 +234,9 @@ def channel_grad(inp: dict, chans, window: int | None = None, method: str = "aut
     the listed channels are exact; db and dc returned here are only the
     contributions of these channels.  g_cols, if given, is g restricted to
     the listed channels ([T][len(chans)]); otherwise inp["g"] is sliced.
+    blas: projections and the dW_delta row sums by numpy's float64 matmul
+    (see project).  bc: b and c of the layer when already known (they do
+    not depend on the channel subset).
     """
     chans = np.asarray(chans, dtype=np.int64)
     x = inp["x"]
@@ -229,7 +244,11 @@ def channel_grad(inp: dict, chans, window: int | None = None, method: str = "aut
     N = inp["W_B"].shape[0]
     W = T if window is None else int(window)
     mode = _mode_for(W, T, method)
-    pr = projections(inp, x=x, chans=chans)
+    if bc is None:
+        pr = projections(inp, x=x, chans=chans, blas=blas)
+    else:
+        pr = {"delta": project(x, np.asarray(inp["W_delta"])[chans], np.asarray(inp["delta_bias"])[chans],
+                               blas=blas), "b": bc["b"], "c": bc["c"]}
     nc = len(chans)
     xc = _f64(x[:, chans])
     gc = _f64(np.asarray(inp["g"])[:, chans] if g_cols is None else g_cols)
@@ -250,6 +269,9 @@ def channel_grad(inp: dict, chans, window: int | None = None, method: str = "aut
     block = 1 << 14
     for t0 in range(0, T, block):
         t1 = min(T, t0 + block)
+        if blas:
+            dWd_rows += np.matmul(dD[t0:t1].T, _f64(x[t0:t1]))
+            continue
         part = np.empty((nc, P))
         _load().orc_weight_grad(t1 - t0, P, nc, _pd(_f64(dD[t0:t1])), _pd(_f64(x[t0:t1])), _pd(part))
         dWd_rows += part

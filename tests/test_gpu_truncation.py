@@ -7,20 +7,21 @@ the products of A; "Referee Report", Section 4.3 leaves T-bar's effect open).
 Layers with W_delta = 0, so softplus(Delta) = u exactly in every channel and
 state n decays at rate u (n + 1) per token; T = 32768, P = 16, N = 16, fp32.
 
-Tolerance.  At u >= 1e-3 the fp32 path meets the fp32 bound 1e-4.  At
-u = 1e-4 the decay factor a = e^{-u (n+1)} lies within 2e-3 of 1, where
-float32 values are spaced 2^-24 apart: the stored a carries a relative error
-of up to 2^-25 / (u (n+1)) (3e-4 for n = 0) in its decay rate, the same at
-every token because s is constant, so the state and the adjoint sums of any
-float32 recurrence -- exact or windowed, forward or reverse -- drift by that
-order over the ~1/u tokens of memory.  The bound used there is
-2^-24 / u = 6e-4 (the decay-rate error at one ulp, the hardware exp's
-accuracy).  Separately, the windowed result must be no less accurate than the
-exact recurrence's on the same inputs (error <= 1.5 x the exact error +
-1e-5): the subtraction of the token leaving the window adds no error of its
-own.  W = 4096 is a whole number of 256-token chunks (window aggregates
-composed from exact chunk aggregates), W = 4000 is not (the window term walked
-inside the local pass).
+Tolerance: the fp32 bound 1e-4 at both decay rates.  The float32 format
+sets a floor that grows as the decay slows: at u = 1e-4 the decay factor
+a = e^{-u (n+1)} lies within 2e-3 of 1, where float32 values are 2^-24
+apart, so the stored a can carry a relative error up to 2^-25 / (u (n+1))
+(3e-4 for n = 0) in its decay rate, the same at every token because s is
+constant, and any float32 recurrence -- exact or windowed, forward or
+reverse -- drifts by that order over the ~1/u tokens of memory.  On this
+hardware's exp the cases below stay within 2e-5 (a CPU simulation with
+other roundings reached 2.4e-4 in dalpha): a failure at u = 1e-4 alone points
+at that floor, not at the window.  Separately, the windowed result must be no
+less accurate than the exact recurrence's on the same inputs (error
+<= 1.5 x the exact error + 1e-5): the subtraction of the token leaving the
+window adds no error of its own.  W = 4096 is a whole number of 256-token
+chunks (window aggregates composed from exact chunk aggregates), W = 4000 is
+not (the window term walked inside the local pass).
 """
 import math
 
@@ -62,7 +63,7 @@ def _case(u, seed=61):
 
 
 def _tol(u):
-    return 1e-4 if u >= 1e-3 else 2.0 ** -24 / u
+    return 1e-4
 
 
 @pytest.mark.parametrize("u", [1e-3, 1e-4])
@@ -90,9 +91,8 @@ def test_truncation_study(orc):
     """The truncation study on a reduced layer: for each decay rate u and
     window W, the relative gradient change ||grad^(W) - grad|| / ||grad||
     (Frobenius norms, exact gradient grad) computed from the GPU's windowed
-    and exact results equals the oracle's within 1e-4 (2^-24 / u below
-    u = 1e-3, see the module notes), and tracks exp(-u W), the weight of the
-    slowest state's tail beyond the window."""
+    and exact results equals the oracle's within 1e-4, and tracks exp(-u W),
+    the weight of the slowest state's tail beyond the window."""
     rows = []
     for u in (1e-4, 1e-3, 1e-2, 1e-1):
         inp = make_layer(_case(u, seed=62))

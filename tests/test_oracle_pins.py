@@ -33,6 +33,21 @@ def test_projection_matches_library_matmul(orc):
     assert rel_err(pr["c"], inp["x"] @ inp["W_C"].T) < 1e-14
 
 
+def test_blas_projection_and_channel_sums_match_loops(orc):
+    # the matmul path used for the million-token workloads equals the loops
+    inp = _tiny(T=300, P=24, N=4)
+    chans = np.array([0, 5, 23])
+    a = orc.channel_grad(inp, chans, window=37)
+    b = orc.channel_grad(inp, chans, window=37, blas=True)
+    pr = orc.projections(inp, blas=True)
+    c = orc.channel_grad(inp, chans, window=37, blas=True, bc={"b": pr["b"], "c": pr["c"]})
+    for k in ("y", "dDelta", "dalpha", "dbias", "db_part", "dc_part", "dW_delta_rows"):
+        assert rel_err(b[k], a[k]) < 1e-12, k
+        assert rel_err(c[k], a[k]) < 1e-12, k
+    assert rel_err(orc.project(inp["x"], inp["W_delta"], inp["delta_bias"], block=64, blas=True),
+                   orc.project(inp["x"], inp["W_delta"], inp["delta_bias"])) < 1e-14
+
+
 def test_time_sums_match_library_matmul(orc):
     rng = np.random.default_rng(3)
     T, P, M = 53, 7, 6

@@ -35,6 +35,7 @@ EXPORTED = (
     "ssm_status_str",
     "ssm_saved_bytes",
     "ssm_sub_state_bytes",
+    "ssm_all_state_bytes",
     "ssm_grad_workspace_bytes_sub",
     "ssm_grad_slab_count",
     "ssm_workspace_bytes",
@@ -66,7 +67,8 @@ class Layer(ctypes.Structure):
 
 class Saved(ctypes.Structure):
     _fields_ = [("s", ctypes.c_void_p), ("b", ctypes.c_void_p), ("c", ctypes.c_void_p),
-                ("h_ckpt", ctypes.c_void_p), ("s_sum", ctypes.c_void_p), ("h_sub", ctypes.c_void_p)]
+                ("h_ckpt", ctypes.c_void_p), ("s_sum", ctypes.c_void_p), ("h_sub", ctypes.c_void_p),
+                ("h_all", ctypes.c_void_p)]
 
 
 class Grads(ctypes.Structure):
@@ -89,6 +91,8 @@ def _load():
     lib.ssm_saved_bytes.restype = ctypes.c_size_t
     lib.ssm_sub_state_bytes.argtypes = [P(Dims)]
     lib.ssm_sub_state_bytes.restype = ctypes.c_size_t
+    lib.ssm_all_state_bytes.argtypes = [P(Dims)]
+    lib.ssm_all_state_bytes.restype = ctypes.c_size_t
     lib.ssm_grad_workspace_bytes_sub.argtypes = [P(Dims), ctypes.c_int64]
     lib.ssm_grad_workspace_bytes_sub.restype = ctypes.c_size_t
     lib.ssm_workspace_bytes.argtypes = [P(Dims), ctypes.c_int64, ctypes.c_int32]
@@ -138,6 +142,10 @@ def ssm_saved_bytes(dims: Dims) -> int:
 
 def ssm_sub_state_bytes(dims: Dims) -> int:
     return int(lib.ssm_sub_state_bytes(ctypes.byref(dims)))
+
+
+def ssm_all_state_bytes(dims: Dims) -> int:
+    return int(lib.ssm_all_state_bytes(ctypes.byref(dims)))
 
 
 def ssm_grad_workspace_bytes_sub(dims: Dims, window: int) -> int:
@@ -240,8 +248,10 @@ def saved_struct(saved: dict, dims: Dims) -> Saved:
     _need(saved.get("s_sum"), "saved s_sum", K * P, torch.float64)
     if saved.get("h_sub") is not None:
         _need(saved["h_sub"], "saved h_sub", ssm_sub_state_bytes(dims) // 4, f32, at_least=True)
+    if saved.get("h_all") is not None:
+        _need(saved["h_all"], "saved h_all", ssm_all_state_bytes(dims) // 4, f32, at_least=True)
     return Saved(_ptr(saved["s"]), _ptr(saved["b"]), _ptr(saved["c"]), _ptr(saved["h_ckpt"]),
-                 _ptr(saved["s_sum"]), _ptr(saved.get("h_sub")))
+                 _ptr(saved["s_sum"]), _ptr(saved.get("h_sub")), _ptr(saved.get("h_all")))
 
 
 def grads_struct(grads: dict, dims: Dims) -> Grads:
@@ -377,9 +387,11 @@ def io_dtype(io: str):
     return torch.bfloat16 if io == "bf16" else torch.float32
 
 
-def alloc_saved(dims: Dims, device="cuda", sub_states=False) -> dict:
+def alloc_saved(dims: Dims, device="cuda", sub_states=False, all_states=False) -> dict:
     """Saved-state buffers; with sub_states, also the optional h_sub buffer
-    (the forward then keeps the state of every 8th token for the gradient)."""
+    (the forward then keeps the state of every 8th token for the gradient);
+    with all_states, the h_all buffer of the store-everything baseline (the
+    forward keeps every state)."""
     import torch
 
     K = (dims.T + dims.chunk - 1) // dims.chunk
@@ -396,6 +408,11 @@ def alloc_saved(dims: Dims, device="cuda", sub_states=False) -> dict:
         if nbytes == 0:
             raise SsmError(4, "ssm_sub_state_bytes")
         out["h_sub"] = torch.empty(nbytes // 4, **f)
+    if all_states:
+        nbytes = ssm_all_state_bytes(dims)
+        if nbytes == 0:
+            raise SsmError(4, "ssm_all_state_bytes")
+        out["h_all"] = torch.empty(nbytes // 4, **f)
     return out
 
 
@@ -405,16 +422,17 @@ def alloc_workspace(nbytes: int, device="cuda"):
     return torch.empty(max(int(nbytes), 1), device=device, dtype=torch.uint8)
 
 
-def forward(dims: Dims, layer: LayerTensors, x, ws=None, saved=None, y=None, stream=None, sub_states=False):
-    """Runs ssm_forward; returns (y, saved dict).  sub_states: keep h_sub (when
-    saved is not given)."""
+def forward(dims: Dims, layer: LayerTensors, x, ws=None, saved=None, y=None, stream=None, sub_states=False,
+            all_states=False):
+    """Runs ssm_forward; returns (y, saved dict).  sub_states: keep h_sub;
+    all_states: keep h_all, every state (when saved is not given)."""
     import torch
 
     nbytes = ssm_workspace_bytes(dims, 0, 0)
     if nbytes == 0:
         raise SsmError(4, "ssm_workspace_bytes")
     ws = alloc_workspace(nbytes, x.device) if ws is None else ws
-    saved = alloc_saved(dims, x.device, sub_states) if saved is None else saved
+    saved = alloc_saved(dims, x.device, sub_states, all_states) if saved is None else saved
     y = torch.empty(dims.T, dims.P, device=x.device, dtype=torch.float32) if y is None else y
     ssm_forward(dims, layer.struct(dims), x, y, saved_struct(saved, dims), ws, ws.numel(), stream)
     return y, saved
@@ -438,7 +456,7 @@ def alloc_grads(dims: Dims, want_dx=False, want_dalpha=True, want_dbias=True, de
 def adjoint_grad(dims: Dims, layer: LayerTensors, x, saved: dict, g, window: int, want_dx=False, ws=None,
                  grads=None, stream=None) -> dict:
     """Runs ssm_adjoint_grad; returns the gradient dict."""
-    if saved.get("h_sub") is not None:
+    if saved.get("h_sub") is not None or saved.get("h_all") is not None:
         nbytes = ssm_grad_workspace_bytes_sub(dims, window)
     else:
         nbytes = ssm_workspace_bytes(dims, window, 0)

@@ -77,6 +77,8 @@ ssm_status check_saved(const ssm_saved* s) {
   if (!aligned16(s->s) || !aligned16(s->b) || !aligned16(s->c) || !aligned16(s->h_ckpt) || !aligned16(s->s_sum))
     return SSM_ERR_ARG;
   if (s->h_sub && !aligned16(s->h_sub)) return SSM_ERR_ARG;
+  if (s->h_all && !aligned16(s->h_all)) return SSM_ERR_ARG;
+  if (s->h_sub && s->h_all) return SSM_ERR_ARG;  // one kind of kept states at most
   return SSM_OK;
 }
 
@@ -199,6 +201,7 @@ ssm_saved carve_saved(Carver& cv, const ssm_dims* d) {
   s.h_ckpt = cv.take<float>(static_cast<size_t>(K * P * N));
   s.s_sum = cv.take<double>(static_cast<size_t>(K * P));
   s.h_sub = nullptr;  // the stack keeps only the chunk checkpoints
+  s.h_all = nullptr;
   return s;
 }
 
@@ -284,6 +287,7 @@ hipError_t run_forward(const ssm_dims* d, const ssm_layer* L, const void* x, flo
   mk.rec(1, st);
   FwdArgs fa{d->T, d->P, d->N, d->chunk, sv->s, x, sv->b, sv->c, L->alpha, w.hloc, sv->s_sum, sv->h_ckpt, y};
   fa.hsub = sv->h_sub;
+  fa.hall = sv->h_all;
   fa.marks = mk;
   return ssm::launch_forward_scan(fa, bf, st);
 }
@@ -306,6 +310,7 @@ hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, co
   a.dal_part = w.dal_part; a.dbias_part = w.dbias_part;
   a.hsub = sv->h_sub ? sv->h_sub : w.hsub;
   a.hsub_given = sv->h_sub ? 1 : 0;
+  a.hall = sv->h_all;
   a.hsub_chunks = w.hsub_chunks;
   a.dY = w.dY; a.ldy = M;
   // the direct input cotangent: the stack's own buffer (its cotangent stream
@@ -374,7 +379,7 @@ static ssm_status scratch_address(void** out) {
 
 extern "C" {
 
-int32_t ssm_version(void) { return 300; }
+int32_t ssm_version(void) { return 301; }
 
 const char* ssm_status_str(int32_t s) {
   switch (s) {
@@ -410,6 +415,11 @@ int32_t ssm_grad_slab_count(const ssm_dims* d, int64_t window, int32_t sub_state
   const int64_t K = nchunks(d);
   const int64_t slab = ssm::bwd_hsub_slab_chunks(d->T, d->P, d->N, d->chunk);
   return static_cast<int32_t>((K + slab - 1) / slab);
+}
+
+size_t ssm_all_state_bytes(const ssm_dims* d) {
+  if (check_dims(d) != SSM_OK) return 0;
+  return ssm::bwd_hall_floats(d->T, d->P, d->N, d->chunk) * sizeof(float);
 }
 
 size_t ssm_grad_workspace_bytes_sub(const ssm_dims* d, int64_t window) {
@@ -466,7 +476,7 @@ static ssm_status adjoint_impl(const ssm_dims* d, const ssm_layer* L, const void
   if (mk.n < 0 || (mk.n > 0 && !mk.ev)) return SSM_ERR_ARG;
   const int64_t W = window < d->T ? window : d->T;
   const bool need_dx = gr->dx != nullptr;
-  const bool own_hsub = sv->h_sub == nullptr;
+  const bool own_hsub = sv->h_sub == nullptr && sv->h_all == nullptr;
   if ((s = check_ws(ws, ws_bytes, bwd_ws_bytes(d, W, need_dx, own_hsub, false, slab_chunks))) != SSM_OK) return s;
   Carver cv(ws);
   BwdWs w = carve_bwd(cv, d, W, need_dx, own_hsub, false, slab_chunks);
@@ -481,7 +491,7 @@ ssm_status ssm_adjoint_grad_noalloc(const ssm_dims* d, const ssm_layer* L, const
   if (s != SSM_OK) return s;
   const int64_t W = window < d->T ? window : d->T;
   const bool need_dx = gr->dx != nullptr;
-  const bool own_hsub = sv->h_sub == nullptr;
+  const bool own_hsub = sv->h_sub == nullptr && sv->h_all == nullptr;
   // everything but the sub-chunk-state slab must fit; the rest of the array
   // holds as large a slab as fits (at most the default one)
   const size_t fixed = bwd_ws_bytes(d, W, need_dx, false);

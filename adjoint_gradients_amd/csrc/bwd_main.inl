@@ -268,7 +268,9 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
 
 }  // namespace
 
-template <typename IO, int NL, int G, bool WIN>
+// ST: every state was kept by the forward (a.hall; the store-everything
+// baseline): each sub-chunk's states are loaded instead of recomputed.
+template <typename IO, int NL, int G, bool WIN, bool ST>
 __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int64_t NBW) {
   constexpr int CH = 64 / G;
   constexpr int NN = NL * G;
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   float* const dxb = a.dxdir ? a.dxdir : static_cast<float*>(a.dY);
   const int64_t ldy_b = a.ldy * static_cast<int64_t>(sizeof(IO)), ldx_b = P * 4;
   float* xw = lds + 2 * STG + kWpb * RED;  // [kWpb][S][OUT]
-  float* hsg = a.hsub + hsub_offset(k - a.hsub_k0, wave_live ? cb : 0, 0, NB, nsub_max, NL);
+  float* hsg = ST ? nullptr : a.hsub + hsub_offset(k - a.hsub_k0, wave_live ? cb : 0, 0, NB, nsub_max, NL);
   const IO* xp = static_cast<const IO*>(a.x);
   const int64_t t0 = k * C;
   const int64_t t1 = (t0 + C < T) ? t0 + C : T;
@@ -419,7 +421,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
 
   // ---------------- phase 1: forward walk, sub-chunk start states to scratch
   // (skipped when the separate sub-chunk pass already wrote them)
-  if (!a.hsub_ready) {
+  if (!ST && !a.hsub_ready) {
     float h[NL];
 #pragma unroll
     for (int j = 0; j < NL; j++) h[j] = a.h_ckpt[(k * P + pc) * NN + n0 + j];
@@ -463,8 +465,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   // the last sub-chunk's start state, loaded as the walk's prefetches load
   // the others (one code path at the loop head: a load on one path only
   // would make the compiler drain every load in flight where the paths meet)
+  if constexpr (!ST) {
 #pragma unroll
-  for (int j = 0; j < NL; j++) hn[j] = hsg[((nsub - 1) * NL + j) * 64 + lane];
+    for (int j = 0; j < NL; j++) hn[j] = hsg[((nsub - 1) * NL + j) * 64 + lane];
+  }
+  // stored states of this wavefront's channels (any wavefront may read them)
+  const float* hag = ST ? a.hall + hsub_offset(k, wave_live ? cb : NB - 1, 0, NB, C, NL) + lane : nullptr;
+  const int clen = static_cast<int>(t1 - t0);
   for (int u = nsub - 1; u >= 0; u--) {
     const int buf = u & 1;
     const float* sb = lds + buf * STG;  // b rows [S][NN], then c rows, then partner c rows
@@ -474,19 +481,23 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
     // A wavefront past the last channel block has no states of its own; it
     // starts from zero (it must not read another wavefront's, which a
     // different workgroup may still be writing) and contributes zeros.
+    if constexpr (!ST) {
 #pragma unroll
-    for (int j = 0; j < NL; j++) hs[j] = wave_live ? hn[j] : 0.0f;
+      for (int j = 0; j < NL; j++) hs[j] = wave_live ? hn[j] : 0.0f;
+    }
     auto prefetch = [&]() {
       if (u > 0) {
         dma_rows(u - 1);
         dma_scal(u - 1);
+        if constexpr (!ST) {
 #pragma unroll
-        for (int j = 0; j < NL; j++) {
-          // loaded by every wavefront (hsg is a valid address for all) and
-          // kept only by live ones, where the next sub-chunk starts: an
-          // unconditional load issued here, ahead of the walk, with nothing
-          // waiting for it until then
-          hn[j] = hsg[((u - 1) * NL + j) * 64 + lane];
+          for (int j = 0; j < NL; j++) {
+            // loaded by every wavefront (hsg is a valid address for all) and
+            // kept only by live ones, where the next sub-chunk starts: an
+            // unconditional load issued here, ahead of the walk, with nothing
+            // waiting for it until then
+            hn[j] = hsg[((u - 1) * NL + j) * 64 + lane];
+          }
         }
       }
     };
@@ -495,12 +506,27 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
     // no partner), so they leave the states and the adjoint unchanged, add
     // nothing to any sum, and their stores are dropped.
     float hr[S][NL];
+    if constexpr (ST) {
+      // the stored states: the chunk's checkpoint or the state after the
+      // previous token, then the state after each token of the sub-chunk
+      // (tokens past the chunk end repeat its last one; they add nothing)
+      const float* src = u == 0 ? a.h_ckpt + (k * P + pc) * NN + n0 : hag + (u * S - 1) * NL * 64;
+      const int stride = u == 0 ? 1 : 64;
+#pragma unroll
+      for (int j = 0; j < NL; j++) hs[j] = src[j * stride];
+#pragma unroll
+      for (int tau = 0; tau < S; tau++) {
+        const int tc = (u * S + tau < clen) ? u * S + tau : clen - 1;
+#pragma unroll
+        for (int j = 0; j < NL; j++) hr[tau][j] = hag[(tc * NL + j) * 64];
+      }
+    }
     // bring sub-chunk u - 1's data and start state now: the buffers it
     // fills were last read before the previous sub-chunk's end barrier, and
     // the loads get the whole sub-chunk to land
     prefetch();
     // recompute the sub-chunk's states
-    {
+    if constexpr (!ST) {
       float hh[NL];
 #pragma unroll
       for (int j = 0; j < NL; j++) hh[j] = hs[j];

@@ -705,6 +705,12 @@ size_t bwd_hsub_floats(int64_t T, int64_t P, int64_t N, int C) {
   return bwd_hsub_floats_chunks((T + C - 1) / C, P, N, C);
 }
 
+size_t bwd_hall_floats(int64_t T, int64_t P, int64_t N, int C) {
+  BwdPlan pl;
+  if (!bwd_plan(P, N, C, &pl)) return 0;
+  return static_cast<size_t>((T + C - 1) / C * pl.NB * C) * pl.NL * 64;
+}
+
 int64_t bwd_hsub_slab_chunks(int64_t T, int64_t P, int64_t N, int C) {
   const int64_t K = (T + C - 1) / C;
   const size_t per = bwd_hsub_floats_chunks(1, P, N, C) * sizeof(float);
@@ -740,7 +746,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   // right (the carry enters each chunk from its right, so a slab needs only
   // the aggregates of itself and of the slabs already done).
   const size_t rows_f = static_cast<size_t>(2) * a.C * NNc * 4;
-  const bool fused = !a.hsub_given && !wl && NNc % 4 == 0 && rows_f <= kHsubRowLds;
+  // (every state kept by the forward, a.hall: nothing is rebuilt)
+  const bool given = a.hsub_given || a.hall != nullptr;
+  const bool fused = !given && !wl && NNc % 4 == 0 && rows_f <= kHsubRowLds;
   if (!fused) {
     const size_t rows_b = static_cast<size_t>(wl ? 2 : 1) * a.C * NNc * 4;
     const dim3 gs(static_cast<unsigned>(K), static_cast<unsigned>((NB + kBwdLocWpb - 1) / kBwdLocWpb));
@@ -785,12 +793,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   // them slab by slab into a region that holds a.hsub_chunks chunks, each
   // slab's rebuild followed by the reverse walk over the same chunks, so the
   // region's size does not grow with T.
-  auto kern = k_bwd_main<IO, NL, G, WIN>;
+  auto kern = a.hall ? k_bwd_main<IO, NL, G, WIN, true> : k_bwd_main<IO, NL, G, WIN, false>;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(pl.lds_bytes));
   if (e != hipSuccess) return e;
   const size_t rows_h = static_cast<size_t>(a.C) * NNc * 4;
-  const bool hpass = !a.hsub_given && !fused && NNc % 4 == 0 && rows_h <= kHsubRowLds;
+  const bool hpass = !given && !fused && NNc % 4 == 0 && rows_h <= kHsubRowLds;
   if (hpass) {
     auto hk = k_bwd_hsub<IO, NL, G>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(hk), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -803,7 +811,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
                             static_cast<int>(rows_f));
     if (e != hipSuccess) return e;
   }
-  const int64_t slab = a.hsub_given ? K : a.hsub_chunks;
+  const int64_t slab = given ? K : a.hsub_chunks;
   if (slab < 1) return hipErrorInvalidValue;
   const int64_t nslab = (K + slab - 1) / slab;
   for (int64_t q = 0; q < nslab; q++) {
@@ -813,8 +821,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const int64_t nk = (K - k_lo < slab) ? K - k_lo : slab;
     BwdArgs am = a;  // arguments of this slab's launches
     am.k_lo = k_lo;
-    am.hsub_k0 = a.hsub_given ? 0 : k_lo;
-    am.hsub_ready = a.hsub_given ? 1 : 0;
+    am.hsub_k0 = given ? 0 : k_lo;
+    am.hsub_ready = given ? 1 : 0;
     const dim3 grid(static_cast<unsigned>(nk), static_cast<unsigned>(pl.NBW));
     if (fused) {
       k_bwd_local_hsub<IO, NL, G><<<grid, 64 * kWpb, rows_f, st>>>(am, NB);

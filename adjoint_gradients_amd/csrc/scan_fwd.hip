@@ -103,7 +103,7 @@ __global__ __launch_bounds__(64) void k_fwd_final(int64_t T, int64_t P, int64_t 
                                                   const float* __restrict__ b, const float* __restrict__ c,
                                                   const float* __restrict__ alpha,
                                                   const float* __restrict__ h_ckpt, float* __restrict__ y,
-                                                  float* __restrict__ hsub) {
+                                                  float* __restrict__ hsub, float* __restrict__ hall) {
   constexpr int CH = 64 / G;
   const int lane = threadIdx.x;
   const int grp = lane / CH, pl = lane % CH;
@@ -123,6 +123,8 @@ __global__ __launch_bounds__(64) void k_fwd_final(int64_t T, int64_t P, int64_t 
   // sub-chunk start states for the gradient, when kept
   const int64_t NB = (P + CH - 1) / CH, nsub_max = (C + kSub - 1) / kSub;
   float* hsg = hsub ? hsub + hsub_offset(k, blockIdx.y, 0, NB, nsub_max, NL) + lane : nullptr;
+  // every state, when kept (the store-everything baseline): h_t after token t
+  float* hag = hall ? hall + hsub_offset(k, blockIdx.y, 0, NB, C, NL) + lane : nullptr;
   for (int64_t t = t0; t < t1; t++) {
     if (hsg && (t - t0) % kSub == 0) {
 #pragma unroll
@@ -139,6 +141,10 @@ __global__ __launch_bounds__(64) void k_fwd_final(int64_t T, int64_t P, int64_t 
       const float a = fast_exp2(ns * al2[j]);
       h[j] = fmaf(a, h[j], bt[j] * xv);
       acc = fmaf(ct[j], h[j], acc);
+    }
+    if (hag) {
+#pragma unroll
+      for (int j = 0; j < NL; j++) hag[((t - t0) * NL + j) * 64] = h[j];
     }
     acc = group_sum<G, CH>(acc);
     if (valid && grp == 0) y[t * P + p] = acc;
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
                                                     const float* __restrict__ alpha,
                                                     const float* __restrict__ h_ckpt, float* __restrict__ y,
                                                     float* __restrict__ hloc, double* __restrict__ ssum,
-                                                    float* __restrict__ hsub) {
+                                                    float* __restrict__ hsub, float* __restrict__ hall) {
   constexpr int CH = 64 / G;
   constexpr int NN = NL * G;
   constexpr int D = kFwdRing;
@@ -220,6 +226,8 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
   // sub-chunk start states for the gradient, when kept (final pass only)
   const int64_t nsub_max = (C + kSub - 1) / kSub;
   float* hsg = (FINAL && hsub && cb < NB) ? hsub + hsub_offset(k, cb, 0, NB, nsub_max, NL) + lane : nullptr;
+  // every state, when kept (the store-everything baseline): h_t after token t
+  float* hag = (FINAL && hall && cb < NB) ? hall + hsub_offset(k, cb, 0, NB, C, NL) + lane : nullptr;
   static_assert(D % kSub == 0, "ring length a multiple of the sub-chunk");
   double ss = 0.0;
   // One token of the walk; `ahead` is the token whose s and x the ring
@@ -252,6 +260,10 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
           h[j + jj] = fmaf(a, h[j + jj], bt[j + jj] * xv);
           acc = fmaf(cq[jj], h[j + jj], acc);
         }
+      }
+      if (hag) {
+#pragma unroll
+        for (int j = 0; j < NL; j++) hag[(tau * NL + j) * 64] = h[j];
       }
       acc = group_sum<G, CH>(acc);
       if (valid && grp == 0)
@@ -314,7 +326,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   if (staged) {
     k_fwd_staged<IO, NL, G, false><<<grid_s, 64 * kFwdWpb, rows_local, st>>>(
         a.T, a.P, a.N, a.C, NB, a.s, static_cast<const IO*>(a.x), a.b, a.c, a.alpha, a.h_ckpt, a.y, a.hloc, a.ssum,
-        nullptr);
+        nullptr, nullptr);
   } else {
     k_fwd_local<IO, NL, G><<<grid, 64, 0, st>>>(a.T, a.P, a.N, a.C, a.s, static_cast<const IO*>(a.x), a.b,
                                                 a.alpha, a.hloc, a.ssum);
@@ -329,10 +341,10 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   if (staged) {
     k_fwd_staged<IO, NL, G, true><<<grid_s, 64 * kFwdWpb, rows_final, st>>>(
         a.T, a.P, a.N, a.C, NB, a.s, static_cast<const IO*>(a.x), a.b, a.c, a.alpha, a.h_ckpt, a.y, a.hloc, a.ssum,
-        a.hsub);
+        a.hsub, a.hall);
   } else {
     k_fwd_final<IO, NL, G><<<grid, 64, 0, st>>>(a.T, a.P, a.N, a.C, a.s, static_cast<const IO*>(a.x), a.b, a.c,
-                                                a.alpha, a.h_ckpt, a.y, a.hsub);
+                                                a.alpha, a.h_ckpt, a.y, a.hsub, a.hall);
   }
   e = hipGetLastError();
   a.marks.rec(4, st);

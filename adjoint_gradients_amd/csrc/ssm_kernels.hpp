@@ -51,6 +51,8 @@ struct FwdArgs {
   float* h_ckpt;        // [K][P][N] saved
   float* y;             // [T][P]
   float* hsub = nullptr;  // optional: sub-chunk start states (bwd_hsub_floats floats)
+  float* hall = nullptr;  // optional: every state, h_t after token t (hsub_offset layout with
+                          // one-token sub-chunks: hsub_offset(k, cb, t - kC, NB, C, NL))
   Marks marks{};        // phases 2..4: after local scan, carry, final scan
 };
 
@@ -80,6 +82,7 @@ struct BwdArgs {
   int64_t hsub_chunks;  // chunks the hsub region holds (the slab; all chunks when given)
   int64_t k_lo;         // first chunk of a launch over a slab (set by the launcher)
   int64_t hsub_k0;      // chunk held by the region's first slot (set by the launcher)
+  const float* hall;    // every state kept by the forward (store-everything baseline), or nullptr
   // outputs of the scan
   void* dY;             // [T][ldy] io: columns [0,P) = dDelta, [P,P+N) = db, [P+N,P+2N) = dc
   int64_t ldy;
@@ -102,6 +105,9 @@ bool bwd_plan(int64_t P, int64_t N, int C, BwdPlan* plan);
 size_t bwd_hsub_floats_chunks(int64_t chunks, int64_t P, int64_t N, int C);
 // Floats of sub-chunk states for every chunk of T tokens (the forward's h_sub).
 size_t bwd_hsub_floats(int64_t T, int64_t P, int64_t N, int C);
+// Floats of every state of T tokens in the one-token-sub-chunk layout (the
+// store-everything baseline's buffer).
+size_t bwd_hall_floats(int64_t T, int64_t P, int64_t N, int C);
 // Chunks per slab of the gradient's own sub-chunk-state region: at most
 // kHsubSlabBytes of states, a multiple of 32 chunks when that many fit, never
 // more than the chunk count.

@@ -21,15 +21,21 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 WORKLOADS = {
-    # name: (index in ssm_inputs.CASES, window, chunk, sub-chunk states kept by the forward)
-    "layer1m": (3, 4096, 256, False),        # 1M tokens, P = 2048, N = 16, bf16, chunk checkpoints only
-    "layer1m_substates": (3, 4096, 256, True),  # the same, the forward also keeps every 8th token's state
-    "layer128k": (2, 8192, 256, False),      # 128K tokens, P = 2048, N = 16, bf16
-    "layer128k_w1k": (2, 1024, 256, False),
-    "layer16k": (1, 2048, 256, False),       # 16K tokens, P = 1024, N = 16, fp32
-    "layer16k_exact": (1, 16384, 256, False),
-    "stack4": (4, 4096, 256, False),  # the 4-layer residual stack (ssm_stack_grad), timed whole
-    "stack4_norm": (4, 4096, 256, False),  # the same stack, every layer reading the RMS-normalised stream
+    # name: (index in ssm_inputs.CASES, window, chunk, states the forward keeps besides the chunk
+    # checkpoints: None, "sub" (every 8th token's) or "all" (every token's: the store-everything
+    # backpropagation baseline))
+    "layer1m": (3, 4096, 256, None),         # 1M tokens, P = 2048, N = 16, bf16, chunk checkpoints only
+    "layer1m_substates": (3, 4096, 256, "sub"),
+    "layer1m_bptt": (3, 4096, 256, "all"),   # store-everything baseline: 128 GiB of states
+    "layer1m_exact": (3, 1048576, 256, None),
+    "layer1m_bptt_exact": (3, 1048576, 256, "all"),
+    "layer128k": (2, 8192, 256, None),       # 128K tokens, P = 2048, N = 16, bf16
+    "layer128k_w1k": (2, 1024, 256, None),
+    "layer128k_bptt": (2, 8192, 256, "all"),
+    "layer16k": (1, 2048, 256, None),        # 16K tokens, P = 1024, N = 16, fp32
+    "layer16k_exact": (1, 16384, 256, None),
+    "stack4": (4, 4096, 256, None),  # the 4-layer residual stack (ssm_stack_grad), timed whole
+    "stack4_norm": (4, 4096, 256, None),  # the same stack, every layer reading the RMS-normalised stream
 }
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -46,12 +52,14 @@ FWD_PHASES = ["proj_gemm", "fwd_local", "fwd_carry", "fwd_final"]
 BWD_PHASES = ["bwd_local", "bwd_carry", "bwd_slab_prep", "bwd_main", "bwd_reduce", "wgrad_gemm", "dx_gemm"]
 
 
-def algorithmic(name, T, P, N, C, W, s_io, sub_states=False, _prep=False):
+def algorithmic(name, T, P, N, C, W, s_io, kept=None, _prep=False):
     """Per-launch algorithmic work of a phase: (bytes, flops, valu_ops).
 
-    Bytes count each compulsory HBM stream once.  With sub_states the forward
-    keeps the state entering every 8th token (T/8 x P x N fp32): the final
-    forward scan writes it and the fused gradient kernel reads it.  valu_ops counts the VALU
+    Bytes count each compulsory HBM stream once.  With kept == "sub" the
+    forward keeps the state entering every 8th token (T/8 x P x N fp32), with
+    kept == "all" every state (T x P x N fp32, the store-everything
+    baseline): the final forward scan writes them and the fused gradient
+    kernel reads them.  valu_ops counts the VALU
     issue slots of the method's own arithmetic per (t, p, n) element, a
     hardware exp2 counting 2 (it issues at half rate on gfx950):
       a_t = exp(-alpha s_t)                          mul + exp        3
@@ -74,7 +82,7 @@ def algorithmic(name, T, P, N, C, W, s_io, sub_states=False, _prep=False):
         return (T * (P * s_io + 4 * P + 4 * N) + K * P * N * 12, 0, 5 * E)
     if name == "fwd_carry":
         return (K * P * N * 8 + K * P * 8, 0, 4 * K * P * N)
-    sub = (T + 7) // 8 * P * N * 4 if sub_states else 0
+    sub = {"sub": (T + 7) // 8 * P * N * 4, "all": T * P * N * 4}.get(kept, 0)
     if name == "fwd_final":
         return (T * (P * s_io + 8 * P + 8 * N) + K * P * N * 4 + sub, 0, 6 * E)
     # a window of whole chunks is composed from exact chunk aggregates in the
@@ -83,7 +91,7 @@ def algorithmic(name, T, P, N, C, W, s_io, sub_states=False, _prep=False):
     # without states kept by the forward, exact local aggregates whose chunk
     # rows (b and c) fit the 64 KB staging area are formed slab by slab in
     # the rebuild walk (phase bwd_slab_prep), with the composition and carry
-    fused = not sub_states and (not win or compose) and 2 * C * N * 4 <= 65536
+    fused = kept is None and (not win or compose) and 2 * C * N * 4 <= 65536
     if name in ("bwd_local", "bwd_carry") and fused and not _prep:
         return (0, 0, 0)
     if name == "bwd_local":
@@ -91,7 +99,7 @@ def algorithmic(name, T, P, N, C, W, s_io, sub_states=False, _prep=False):
     if name == "bwd_carry":
         return (K * P * N * 8 + K * P * 8, 0, (9 if compose else 4) * K * P * N)
     if name == "bwd_slab_prep":
-        if sub_states:
+        if kept is not None:
             return (0, 0, 0)
         # the local aggregates (bytes and slots as bwd_local) formed in the
         # forward walk that rebuilds the states -- the rebuild itself is
@@ -99,8 +107,8 @@ def algorithmic(name, T, P, N, C, W, s_io, sub_states=False, _prep=False):
         # composition and the carry
         if not fused:
             return (0, 0, 0)
-        lb, _, lo = algorithmic("bwd_local", T, P, N, C, W, s_io, False, True)
-        cb, _, co = algorithmic("bwd_carry", T, P, N, C, W, s_io, False, True)
+        lb, _, lo = algorithmic("bwd_local", T, P, N, C, W, s_io, None, True)
+        cb, _, co = algorithmic("bwd_carry", T, P, N, C, W, s_io, None, True)
         return (lb + cb, 0, lo + co)
     if name == "bwd_main":
         # per token: x, s, g, b, c, dDelta (io) and db/dc, plus h_ckpt once per chunk
@@ -266,13 +274,14 @@ def study_truncation():
 
 
 def study_memory():
-    """Device memory of one layer's forward + gradient at the 128K and 1M-token
-    workloads: the buffers the caller allocates (the library allocates
-    nothing), measured as torch's peak of allocated bytes, beside two
-    references -- the per-token storage of the reviewed paper's memory
-    analysis ({A_t, C_t, h_t, y_t} for every token) applied to this layer in
-    fp16, T (2 P N + N + P) x 2 bytes, and a store-everything backpropagation
-    through time that keeps at least every h_t, T P N x 4 bytes."""
+    """Device memory and time of one layer's forward + gradient at the 128K and
+    1M-token workloads, for the three kinds of kept state: chunk checkpoints
+    only (the adjoint path as benchmarked), also every 8th token's state, and
+    every state (the store-everything backpropagation baseline).  The library
+    allocates nothing, so the memory is the caller's buffers: torch's peak of
+    allocated bytes over both calls.  Beside them, the per-token storage of
+    the reviewed paper's memory analysis ({A_t, C_t, h_t, y_t} for every token)
+    applied to this layer in fp16, T (2 P N + N + P) x 2 bytes."""
     import torch
 
     import adjoint_gradients_amd as agm
@@ -283,7 +292,7 @@ def study_memory():
         case = CASES[case_idx]
         T, P, N, io = case.T, case.P, case.N, case.io
         dims = agm.make_dims(T, P, N, 256, io)
-        for sub in (False, True):
+        for kept in (None, "sub", "all"):
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
             torch.cuda.reset_peak_memory_stats()
@@ -293,23 +302,31 @@ def study_memory():
             lay = agm.LayerTensors(dv(inp["W_delta"], dt), dv(inp["W_B"], dt), dv(inp["W_C"], dt),
                                    dv(inp["alpha"]), dv(inp["delta_bias"]))
             x, g = inp["x_dev"], inp["g_dev"]
-            base = torch.cuda.memory_allocated()
-            y, saved = agm.forward(dims, lay, x, sub_states=sub)
-            grads = agm.adjoint_grad(dims, lay, x, saved, g, window)
             torch.cuda.synchronize()
+            base = torch.cuda.memory_allocated()
+            times = []
+            for rep in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                y, saved = agm.forward(dims, lay, x, sub_states=kept == "sub", all_states=kept == "all")
+                grads = agm.adjoint_grad(dims, lay, x, saved, g, window)
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+                if rep < 2:
+                    del y, saved, grads
             peak = torch.cuda.max_memory_allocated()
             row = {
                 "study": "memory", "workload": case.name, "T": T, "P": P, "N": N, "window": window,
-                "sub_states_saved": sub,
+                "states_kept": {None: "chunk checkpoints", "sub": "every 8th token", "all": "every token"}[kept],
                 "inputs_gib": round(base / gib, 3),
-                "saved_gib": round((agm.ssm_saved_bytes(dims) + (agm.ssm_sub_state_bytes(dims) if sub else 0))
-                                   / gib, 3),
+                "saved_gib": round(sum(v.numel() * v.element_size() for v in saved.values()) / gib, 3),
                 "workspace_fwd_gib": round(agm.ssm_workspace_bytes(dims, 0, 0) / gib, 3),
-                "workspace_grad_gib": round((agm.ssm_grad_workspace_bytes_sub(dims, window) if sub
+                "workspace_grad_gib": round((agm.ssm_grad_workspace_bytes_sub(dims, window) if kept
                                              else agm.ssm_workspace_bytes(dims, window, 0)) / gib, 3),
                 "peak_allocated_gib": round(peak / gib, 3),
+                "ms_fwd_plus_grad_incl_allocation": round(min(times), 2),
                 "paper_sec45_per_token_fp16_gib": round(T * (2 * P * N + N + P) * 2 / gib, 3),
-                "bptt_all_h_fp32_gib": round(T * P * N * 4 / gib, 3),
             }
             print(json.dumps(row), flush=True)
             del y, saved, grads, inp, x, g, lay
@@ -420,19 +437,29 @@ def main():
         study_memory()
         return
     if args.calibrate_copy:
+        # a plain device-to-device copy of known size: its FETCH_SIZE and
+        # WRITE_SIZE counter readings calibrate the traffic figures, and its
+        # event-timed rate is the copy bandwidth the HBM-bound kernels are
+        # compared with (read + written bytes / time)
         n = args.calibrate_copy * (1 << 20) // 4
         src = torch.ones(n, device="cuda:0", dtype=torch.float32)
         dst = torch.empty_like(src)
+        ms = []
         for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3}), flush=True)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3, "ms": [round(v, 4) for v in ms],
+                          "copy_gbs_read_plus_write": round(2 * n * 4 / (min(ms) * 1e-3) / 1e9, 1)}), flush=True)
         return
 
     import adjoint_gradients_amd as agm
     from ssm_inputs import CASES, make_layer_device
 
-    case_idx, window, chunk, sub_states = WORKLOADS[args.workload]
+    case_idx, window, chunk, kept = WORKLOADS[args.workload]
     if CASES[case_idx].K > 1:
         bench_stack(args, case_idx, window, chunk, norm=args.workload.endswith("norm"))
         return
@@ -452,15 +479,16 @@ def main():
     x, g = inp["x_dev"], inp["g_dev"]
     dims = agm.make_dims(T, P, N, chunk, io)
     ws_f = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, 0, 0), dev)
-    saved = agm.alloc_saved(dims, dev, sub_states=sub_states)
-    ws_b = agm.alloc_workspace(agm.ssm_grad_workspace_bytes_sub(dims, window) if sub_states
+    saved = agm.alloc_saved(dims, dev, sub_states=kept == "sub", all_states=kept == "all")
+    ws_b = agm.alloc_workspace(agm.ssm_grad_workspace_bytes_sub(dims, window) if kept
                                else agm.ssm_workspace_bytes(dims, window, 0), dev)
     grads = agm.alloc_grads(dims, device=dev)
     y = torch.empty(T, P, device=dev, dtype=torch.float32)
+    mem_total = torch.cuda.memory_allocated()  # everything the step uses, allocated before it runs
     L = lay.struct(dims)
     S = agm.saved_struct(saved, dims)
     G = agm.grads_struct(grads, dims)
-    nslab = agm.ssm_grad_slab_count(dims, window, sub_states)
+    nslab = agm.ssm_grad_slab_count(dims, window, kept is not None)
     stream = torch.cuda.current_stream()
 
     hev = HipEvents()
@@ -512,7 +540,7 @@ def main():
 
     rows = []
     for k, ms in phase_ms.items():
-        by, fl, ops = algorithmic(k, T, P, N, chunk, window, s_io, sub_states)
+        by, fl, ops = algorithmic(k, T, P, N, chunk, window, s_io, kept)
         rows.append((k, ms, by / (ms * 1e-3) / 1e9 if ms > 0 else 0.0, fl / (ms * 1e-3) / 1e12 if ms > 0 else 0.0,
                      ops / (ms * 1e-3) / 1e9 if ms > 0 else 0.0))
     if args.phases:
@@ -524,7 +552,7 @@ def main():
     # the dominant kernel
     dom = max(rows, key=lambda r: r[1])
     name, ms = dom[0], dom[1]
-    by, fl, ops = algorithmic(name, T, P, N, chunk, window, s_io, sub_states)
+    by, fl, ops = algorithmic(name, T, P, N, chunk, window, s_io, kept)
     # per launch: the fused reverse kernel runs once per slab of chunks (equal
     # slabs at this workload), every other phase once per step
     nl = nslab if name == "bwd_main" else 1
@@ -559,11 +587,20 @@ def main():
         "dtype": "bf16" if io == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": f"{case.name}: one selective SSM layer, T={T}, P={P}, N={N}, io={io}, "
-                               f"fp32 state, window={window}, h stored only at {chunk}-token chunk boundaries"
-                               + (" and before every 8th token (the forward keeps the sub-chunk states)"
-                                  if sub_states else " (the gradient rebuilds the states inside each chunk)"),
+                               f"fp32 state, window={window}, "
+                               + {None: f"h stored only at {chunk}-token chunk boundaries (the gradient rebuilds "
+                                        "the states inside each chunk)",
+                                  "sub": f"h stored at {chunk}-token chunk boundaries and before every 8th token "
+                                         "(the forward keeps the sub-chunk states)",
+                                  "all": "every h_t stored by the forward and read by the gradient "
+                                         "(the store-everything backpropagation baseline)"}[kept],
                    "T": T, "P": P, "N": N, "window": window, "chunk": chunk,
-                   "sub_states_saved": sub_states, "fused_kernel_launches": nslab},
+                   "states_kept": kept or "chunk checkpoints", "fused_kernel_launches": nslab,
+                   "device_memory_gib": {
+                       "saved_state": round(sum(v.numel() * v.element_size() for v in saved.values()) / 2**30, 3),
+                       "gradient_workspace": round(ws_b.numel() / 2**30, 3),
+                       "forward_workspace": round(ws_f.numel() / 2**30, 3),
+                       "total_with_inputs_and_outputs": round(mem_total / 2**30, 3)}},
         "roofline": roof,
         "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
     }

@@ -113,7 +113,16 @@ typedef struct {
  * whose workspace then drops the region in which it would rebuild them
  * (ssm_grad_workspace_bytes_sub).
  * h_sub must be NULL in both calls or, in the gradient call, hold what
- * ssm_forward wrote for the same dims, x and layer. */
+ * ssm_forward wrote for the same dims, x and layer.
+ *
+ * h_all is optional too (NULL: not kept) and is the store-everything
+ * baseline of backpropagation through time, kept for comparison: when set,
+ * ssm_forward stores the state after every token (ssm_all_state_bytes(dims)
+ * bytes, T*P*N floats in a private layout: 128 GiB at T = 2^20, P = 2048,
+ * N = 16) and ssm_adjoint_grad reads those states instead of rebuilding any,
+ * with the same reverse kernel otherwise.  At most one of h_sub and h_all may
+ * be set (SSM_ERR_ARG otherwise); with either set, the gradient's workspace
+ * is ssm_grad_workspace_bytes_sub(dims, window). */
 typedef struct {
   float *s;        /* [T][P]  softplus(Delta) */
   float *b;        /* [T][N] */
@@ -121,6 +130,7 @@ typedef struct {
   float *h_ckpt;   /* [ceil(T/C)][P][N]  h_{kC-1}; entry 0 is the zero state */
   double *s_sum;   /* [ceil(T/C)][P]  sum of s over each chunk, in fp64 */
   float *h_sub;    /* optional sub-chunk states (see above), or NULL */
+  float *h_all;    /* optional: every state, the store-everything baseline (see above), or NULL */
 } ssm_saved;
 
 /* Gradient outputs of one layer.  The three weight gradients are required;
@@ -150,6 +160,10 @@ size_t ssm_saved_bytes(const ssm_dims *dims);
 /* Bytes of the optional ssm_saved.h_sub buffer.  0 if dims are invalid. */
 size_t ssm_sub_state_bytes(const ssm_dims *dims);
 
+/* Bytes of the optional ssm_saved.h_all buffer (every state, the
+ * store-everything baseline).  0 if dims are invalid. */
+size_t ssm_all_state_bytes(const ssm_dims *dims);
+
 /* Workspace bytes needed by ssm_forward (window = 0, K = 0), by
  * ssm_adjoint_grad (window >= 1, K = 0) or by ssm_stack_grad (K >= 1) for a
  * stack in which no layer normalises its input (for other stacks see
@@ -171,15 +185,15 @@ size_t ssm_workspace_bytes(const ssm_dims *dims, int64_t window, int32_t K);
  * and row scratch.  0 if the arguments are invalid. */
 size_t ssm_stack_workspace_bytes(int32_t K, const ssm_dims *dims, const ssm_layer *layers, int64_t window);
 
-/* Workspace bytes of ssm_adjoint_grad (window >= 1) when saved->h_sub is set:
+/* Workspace bytes of ssm_adjoint_grad (window >= 1) when saved->h_sub or saved->h_all is set:
  * smaller than ssm_workspace_bytes(dims, window, 0) by the region that would
  * otherwise hold a slab of sub-chunk states.  0 if the arguments are invalid. */
 size_t ssm_grad_workspace_bytes_sub(const ssm_dims *dims, int64_t window);
 
 /* Number of slabs of chunks ssm_adjoint_grad processes (each slab: the
  * rebuild of its sub-chunk states, then the fused reverse adjoint + VJP
- * kernel over it): 1 when the forward kept the sub-chunk states
- * (sub_states_given != 0).  Instrumentation (see ssm_adjoint_grad_timed);
+ * kernel over it): 1 when the forward kept sub-chunk states or every state
+ * (sub_states_given != 0: saved->h_sub or saved->h_all set).  Instrumentation (see ssm_adjoint_grad_timed);
  * 0 if the arguments are invalid. */
 int32_t ssm_grad_slab_count(const ssm_dims *dims, int64_t window, int32_t sub_states_given);
 

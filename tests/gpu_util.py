@@ -40,9 +40,10 @@ def layer_tensors(inp, io):
                             None if ns is None else to_dev(np.asarray(ns, dtype=np.float32)))
 
 
-def gpu_layer(inp, window, chunk, want_dx=True, io=None, g=None, sub_states=False):
+def gpu_layer(inp, window, chunk, want_dx=True, io=None, g=None, sub_states=False, all_states=False):
     """Forward + adjoint gradient of one layer on the GPU; returns numpy float64 dict.
-    sub_states: the forward keeps the sub-chunk states (saved h_sub) for the gradient."""
+    sub_states: the forward keeps the sub-chunk states (saved h_sub) for the gradient;
+    all_states: it keeps every state (saved h_all, the store-everything baseline)."""
     import torch
 
     import adjoint_gradients_amd as agm
@@ -54,13 +55,13 @@ def gpu_layer(inp, window, chunk, want_dx=True, io=None, g=None, sub_states=Fals
     lay = layer_tensors(inp, io)
     x = to_dev(inp["x"], io)
     gg = to_dev(inp["g"] if g is None else g)
-    y, saved = agm.forward(dims, lay, x, sub_states=sub_states)
+    y, saved = agm.forward(dims, lay, x, sub_states=sub_states, all_states=all_states)
     grads = agm.adjoint_grad(dims, lay, x, saved, gg, window, want_dx=want_dx)
     torch.cuda.synchronize()
     out = {k: v.double().cpu().numpy() for k, v in grads.items()}
     out["y"] = y.double().cpu().numpy()
     for k, v in saved.items():
-        if k != "h_sub":  # private layout
+        if k not in ("h_sub", "h_all"):  # private layouts
             out["saved_" + k] = v.double().cpu().numpy()
     return out
 

@@ -30,11 +30,11 @@ def orc():
     return oracle
 
 
-def _run_case(orc, inp, window, chunk, label, tol=None, sub_states=False):
+def _run_case(orc, inp, window, chunk, label, tol=None, sub_states=False, all_states=False):
     say(f"case {label}: T={inp['x'].shape[0]} P={inp['x'].shape[1]} N={inp['W_B'].shape[0]} "
-        f"io={inp['io']} W={window} C={chunk} sub_states={sub_states}")
+        f"io={inp['io']} W={window} C={chunk} sub_states={sub_states} all_states={all_states}")
     tol = tol if tol is not None else TOL[inp["io"]]
-    got = gpu_layer(inp, window, chunk, sub_states=sub_states)
+    got = gpu_layer(inp, window, chunk, sub_states=sub_states, all_states=all_states)
     o = oracle_inputs(inp)
     T = inp["x"].shape[0]
     ref = orc.layer_grad(o, window=None if window >= T else window)
@@ -139,7 +139,27 @@ def test_sub_states(orc, label, T, P, N, io, window, chunk):
         assert rel_err(got[gk], ref[gk]) <= 1e-5, gk
 
 
-@pytest.mark.parametrize("sub_states", [False, True])
+@pytest.mark.parametrize("label,T,P,N,io,window,chunk", [
+    ("exact", 256, 64, 16, "f32", 256, 256),
+    ("ragged C", 300, 40, 8, "f32", 300, 100),
+    ("window", 1024, 96, 16, "f32", 255, 256),
+    ("window of whole chunks, ragged T", 700, 70, 32, "f32", 256, 128),
+    ("N=1", 300, 40, 1, "f32", 120, 64),
+    ("N=64, one-wavefront forward", 512, 48, 64, "f32", 200, 256),
+    ("bf16", 1024, 96, 16, "bf16", 200, 256),
+])
+def test_store_everything_baseline(orc, label, T, P, N, io, window, chunk):
+    # the forward keeps every state (h_all) and the gradient reads them
+    # instead of rebuilding any: the oracle's tolerance, and the same result
+    # as the path that keeps only the chunk checkpoints
+    inp = make_layer(small_case(T, P, N, 22, io=io))
+    got, _ = _run_case(orc, inp, window, chunk, f"store-everything {label}", all_states=True)
+    ref = gpu_layer(inp, window, chunk)
+    for gk, _ in GRAD_KEYS:
+        assert rel_err(got[gk], ref[gk]) <= 1e-6, gk
+
+
+@pytest.mark.parametrize("mode", ["checkpoints", "sub_states", "all_states"])
 @pytest.mark.parametrize("T,P,N,io,window,chunk", [
     (512, 48, 64, "f32", 200, 256),    # 6 channel blocks: idle wavefronts in the last workgroup
     (300, 40, 8, "f32", 120, 100),
@@ -148,7 +168,7 @@ def test_sub_states(orc, label, T, P, N, io, window, chunk):
     (1000, 96, 16, "bf16", 256, 128),  # window of whole chunks, ragged last chunk, an idle wavefront
     (700, 40, 8, "f32", 200, 100),     # window of whole chunks, one lane group
 ])
-def test_poisoned_buffers(orc, T, P, N, io, window, chunk, sub_states):
+def test_poisoned_buffers(orc, T, P, N, io, window, chunk, mode):
     # workspaces and saved buffers filled with NaN bytes beforehand: a read of
     # anything the library did not write shows up in the outputs
     import torch
@@ -157,15 +177,17 @@ def test_poisoned_buffers(orc, T, P, N, io, window, chunk, sub_states):
     from gpu_util import layer_tensors, to_dev
 
     inp = make_layer(small_case(T, P, N, 31, io=io))
-    say(f"case poisoned T={T} P={P} N={N} io={io} W={window} C={chunk} sub_states={sub_states}")
+    sub_states, all_states = mode == "sub_states", mode == "all_states"
+    say(f"case poisoned T={T} P={P} N={N} io={io} W={window} C={chunk} kept={mode}")
     dims = agm.make_dims(T, P, N, chunk, io)
     lay = layer_tensors(inp, io)
     x = to_dev(inp["x"], io)
     g = to_dev(inp["g"])
     ws_f = agm.alloc_workspace(agm.ssm_workspace_bytes(dims, 0, 0), x.device).fill_(255)
-    nb = agm.ssm_grad_workspace_bytes_sub(dims, window) if sub_states else agm.ssm_workspace_bytes(dims, window, 0)
+    nb = (agm.ssm_grad_workspace_bytes_sub(dims, window) if mode != "checkpoints"
+          else agm.ssm_workspace_bytes(dims, window, 0))
     ws_b = agm.alloc_workspace(nb, x.device).fill_(255)
-    saved = agm.alloc_saved(dims, x.device, sub_states=sub_states)
+    saved = agm.alloc_saved(dims, x.device, sub_states=sub_states, all_states=all_states)
     for v in saved.values():
         v.view(torch.uint8).fill_(255)
     y, saved = agm.forward(dims, lay, x, ws=ws_f, saved=saved)
@@ -174,7 +196,7 @@ def test_poisoned_buffers(orc, T, P, N, io, window, chunk, sub_states):
     got = {k: v.double().cpu().numpy() for k, v in grads.items()}
     got["y"] = y.double().cpu().numpy()
     ref = orc.layer_grad(oracle_inputs(inp), window=None if window >= T else window)
-    compare(got, ref, GRAD_KEYS, TOL[io], f"poisoned N={N} P={P} sub_states={sub_states}")
+    compare(got, ref, GRAD_KEYS, TOL[io], f"poisoned N={N} P={P} kept={mode}")
 
 
 @pytest.mark.parametrize("io,window,mask", [("f32", 256, (1, 1, 1)), ("f32", 50, (1, 0, 1)),

@@ -42,6 +42,9 @@ struct EpiProj {
   // its last tile column holds the 2N projection columns past the P of Delta:
   // the direct-to-LDS kernel skips the blocks past them
   static constexpr bool kSkipTail = true;
+  // eight wavefronts per workgroup in the direct-to-LDS kernel (measured at
+  // 1M x 2080 x 2048: 10.65 -> 10.20 ms)
+  static constexpr int kWaveCols = 4;
   EpiProjArgs e;
   __device__ __forceinline__ void operator()(int64_t row, int64_t col, float v, int) const {
     if (col < e.P) {
@@ -96,6 +99,7 @@ struct EpiPart {
 };
 
 struct EpiAdd {
+  static constexpr int kWaveCols = 4;
   EpiAddArgs e;
   int64_t Nc;
   __device__ __forceinline__ void operator()(int64_t row, int64_t col, float v, int) const {

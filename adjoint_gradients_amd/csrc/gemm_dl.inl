@@ -4,10 +4,10 @@
 // C[m][n] = sum_k A[m][k] B[n][k], fp32 accumulation, each element handed to
 // an epilogue.  Operands may be K-contiguous (X[r][k]) or K-outer (X[k][r]).
 //
-// Macro tile 256 x 256 per 256-thread workgroup, one wavefront per SIMD, each
-// owning 128 x 128 = 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 (256 fp32
-// accumulators per lane).  K advances in stages of 32: every operand tile of a
-// stage (256 x 32 bf16, 16 KB) is fetched by 16 wave-wide
+// Macro tile 256 x 256 per workgroup of four or eight wavefronts, each owning
+// 128 x 128 (4 x 4) or 128 x 64 (4 x 2) tiles of v_mfma_f32_32x32x16_bf16
+// (256 or 128 fp32 accumulators per lane).  K advances in stages of 32: every
+// operand tile of a stage (256 x 32 bf16, 16 KB) is fetched by 16 wave-wide
 // global_load_lds_dwordx4 instructions straight into LDS, so no register
 // holds operands in flight and no VALU work moves them.  Four LDS stages
 // (128 KB) let the loads run three stages ahead of the MFMAs; each stage is
@@ -31,12 +31,32 @@
 
 namespace gdl {
 
-constexpr int NT = 256;
+// Wavefronts of a workgroup: 2 along M (128 rows each, kBI = 4 blocks of 32)
+// by WN along N (256 / WN columns, kBJ = 8 / WN blocks of 32).  WN = 2 gives
+// four waves, one per SIMD with 256 accumulators per lane; WN = 4 gives
+// eight, two per SIMD with 128 each, whose second wave can issue while the
+// first waits on LDS.  An epilogue picks WN with kWaveCols (default 2).
+template <int WN>
+struct Waves {
+  static constexpr int kWM = 2;
+  static constexpr int kWN = WN;
+  static constexpr int kBI = 4;
+  static constexpr int kBJ = 8 / WN;
+  static constexpr int kWaves = kWM * kWN;
+  static constexpr int NT = 64 * kWaves;
+  static constexpr int kLPW = kInstrPerTile / kWaves;  // load instructions per operand, wave and stage
+  static constexpr int kLoadsPerWave = 2 * kLPW;       // both operands, per stage
+  // Per sub-step of 16 k a wave runs kBI kBJ MFMAs; a stage's refill loads are
+  // spread over the second sub-step's, one every kEvery MFMAs, A and B alternating.
+  static constexpr int kEvery = kBI * kBJ / (2 * kLPW);
+  static_assert(kWM * kBI * 32 == kRows && kWN * kBJ * 32 == kRows, "wave layout covers the tile");
+  static_assert(kLPW * kWaves == kInstrPerTile, "loads divide over the waves");
+  static_assert(kEvery >= 1 && kEvery * 2 * kLPW == kBI * kBJ, "refill spacing");
+};
 constexpr int NS = 4;                          // LDS stages (wait_stages covers NS <= 5)
 static_assert(NS >= 3 && NS <= 5, "stage count");
 constexpr int kStageBytes = 2 * kTileBytes;    // A tile, then B tile
 constexpr size_t kLdsBytes = static_cast<size_t>(NS) * kStageBytes;
-constexpr int kLoadsPerWave = 2 * kInstrPerTile / 4;  // both operands, per stage
 constexpr int kXcds = 8;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -87,20 +107,20 @@ __device__ __forceinline__ void wait_stages(int64_t n) {
   else wait_vm<0>();
 }
 
-template <bool KC>
+template <bool KC, int NBLK, int kLPW>
 struct Operand {
   const bf16_t* base;  // wave-uniform: the tile corner at k = 0
   int64_t ld;
-  uint32_t off[4];     // per-lane element offsets of this wave's 4 load instructions
-  int rd[KC ? 2 : 4];  // per-lane byte offsets of the operand fetches (see read())
+  uint32_t off[kLPW];  // per-lane element offsets of this wave's load instructions
+  int rd[KC ? 2 : NBLK];  // per-lane byte offsets of the operand fetches (see read())
 
   __device__ __forceinline__ void init(const bf16_t* X, int64_t ldx, int64_t R, int64_t r0, int wave, int lane,
                                        int rb) {
     ld = ldx;
     base = X + (KC ? r0 * ldx : r0);
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int gi = wave * 4 + j;
+    for (int j = 0; j < kLPW; j++) {
+      const int gi = wave * kLPW + j;
       if constexpr (KC) {
         const int64_t row = r0 + kc_load_row(gi, lane);
         const int64_t rr = (row < R ? row : R - 1) - r0;
@@ -116,19 +136,19 @@ struct Operand {
       rd[1] = kc_read_off(lane, rb, 1);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; i++) rd[i] = ko_read_off(lane, rb + 32 * i, 0, 0);  // + 8192 q, + 2048 h
+      for (int i = 0; i < NBLK; i++) rd[i] = ko_read_off(lane, rb + 32 * i, 0, 0);  // + 8192 q, + 2048 h
     }
   }
 
   // Stage loads for K offset k0 into the tile at LDS address `tile`: this
-  // wave's 4 load instructions (issue) or its j-th one (issue_one).
+  // wave's kLPW load instructions (issue) or its j-th one (issue_one).
   __device__ __forceinline__ void issue_one(uint32_t tile, int64_t k0, int wave, int j) const {
     const bf16_t* src = base + (KC ? k0 : k0 * ld);
-    dma16(src + off[j], tile + static_cast<uint32_t>((wave * 4 + j) * 1024));
+    dma16(src + off[j], tile + static_cast<uint32_t>((wave * kLPW + j) * 1024));
   }
   __device__ __forceinline__ void issue(uint32_t tile, int64_t k0, int wave) const {
 #pragma unroll
-    for (int j = 0; j < 4; j++) issue_one(tile, k0, wave, j);
+    for (int j = 0; j < kLPW; j++) issue_one(tile, k0, wave, j);
   }
 
   // MFMA operand (8 bf16) of 32-row block i of this wave, k sub-step q.
@@ -161,15 +181,28 @@ constexpr bool kSkipTailImpl = false;
 template <class E>
 constexpr bool kSkipTailImpl<E, std::void_t<decltype(E::kSkipTail)>> = E::kSkipTail;
 
+// Wave count of an epilogue's GEMM (kWaveCols wavefronts along N).
+template <class E, class = void>
+constexpr int kWaveColsImpl = 2;
+template <class E>
+constexpr int kWaveColsImpl<E, std::void_t<decltype(E::kWaveCols)>> = E::kWaveCols;
+template <class Epi>
+using WavesOf = Waves<kWaveColsImpl<Epi>>;
+
 template <class Epi, bool a_kc, bool b_kc>
-__global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_t K, const bf16_t* __restrict__ A,
-                                                   int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
-                                                   int64_t k_per_split, int64_t tilesM, int64_t tilesN, Epi epi) {
+__global__ __launch_bounds__(WavesOf<Epi>::NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_t K,
+                                                                const bf16_t* __restrict__ A, int64_t lda,
+                                                                const bf16_t* __restrict__ B, int64_t ldb,
+                                                                int64_t k_per_split, int64_t tilesM, int64_t tilesN,
+                                                                Epi epi) {
   extern __shared__ __attribute__((aligned(1024))) char smem_dl[];
   lds_char* const lds = (lds_char*)(smem_dl);  // generic -> LDS address space
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  using W = WavesOf<Epi>;
+  constexpr int kWN = W::kWN, kBI = W::kBI, kBJ = W::kBJ, kLPW = W::kLPW;
+  constexpr int kLoadsPerWave = W::kLoadsPerWave, kEvery = W::kEvery;
+  const int wm = wave / kWN, wn = wave % kWN;
 
   // XCD-aware bijection of the workgroup id onto (split, tile row, tile column)
   const int64_t nwg = gridDim.x;
@@ -185,16 +218,16 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_
   const int64_t kend = (kbeg + k_per_split < K) ? kbeg + k_per_split : K;
   const int64_t nsteps = kbeg < kend ? (kend - kbeg) / kBK : 0;
 
-  Operand<a_kc> oa;
-  Operand<b_kc> ob;
-  oa.init(A, lda, M, m0, wave, l, wm * 128);
-  ob.init(B, ldb, Nc, n0, wave, l, wn * 128);
+  Operand<a_kc, kBI, kLPW> oa;
+  Operand<b_kc, kBJ, kLPW> ob;
+  oa.init(A, lda, M, m0, wave, l, wm * (32 * kBI));
+  ob.init(B, ldb, Nc, n0, wave, l, wn * (32 * kBJ));
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[kBI][kBJ];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < kBI; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < kBJ; j++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
@@ -212,16 +245,16 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_
   if constexpr (!kSkipTailImpl<Epi>) {
     // every wave runs the whole loop (the tail variants below cost the
     // weight-gradient split-K kernel more in its schedule than they save)
-    // Operand fragments of one k sub-step: A blocks 0..3, B blocks 0..3.
+    // Operand fragments of one k sub-step: A blocks 0..kBI-1, B blocks 0..kBJ-1.
     struct Frags {
-      bf16x8_t a[4], b[4];
+      bf16x8_t a[kBI], b[kBJ];
     };
     auto read_frags = [&](Frags& f, int64_t s, int q) {
       const lds_char* st = lds + (s % NS) * kStageBytes;
 #pragma unroll
-      for (int i = 0; i < 4; i++) f.a[i] = oa.read(st, i, q);
+      for (int i = 0; i < kBI; i++) f.a[i] = oa.read(st, i, q);
 #pragma unroll
-      for (int j = 0; j < 4; j++) f.b[j] = ob.read(st + kTileBytes, j, q);
+      for (int j = 0; j < kBJ; j++) f.b[j] = ob.read(st + kTileBytes, j, q);
     };
 
     // Stage s: multiply sub-step 0 (read one sub-step earlier) with the reads
@@ -242,12 +275,12 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_
       constexpr bool NEXT = decltype(next_tag)::value;      // stage s + 1 exists
       const lds_char* st0 = lds + (s % NS) * kStageBytes;
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
+      for (int i = 0; i < kBI; i++) {
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < kBJ; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.a[i], f0.b[j], acc[i][j], 0, 0, 0);
         f1.a[i] = oa.read(st0, i, 1);
-        f1.b[i] = ob.read(st0 + kTileBytes, i, 1);
+        if (i < kBJ) f1.b[i < kBJ ? i : 0] = ob.read(st0 + kTileBytes, i, 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (NEXT) {
@@ -260,18 +293,22 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_
       const uint32_t stn = lds_base + static_cast<uint32_t>(((s + NS - 1) % NS) * kStageBytes);
       const lds_char* st1 = lds + ((s + 1) % NS) * kStageBytes;
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
+      for (int i = 0; i < kBI; i++) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
+        for (int j = 0; j < kBJ; j++) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.a[i], f1.b[j], acc[i][j], 0, 0, 0);
           if constexpr (REFILL) {
-            if (j == 0) oa.issue_one(stn, kn, wave, i);
-            if (j == 2) ob.issue_one(stn + kTileBytes, kn, wave, i);
+            const int m = i * kBJ + j;
+            if (m % kEvery == 0) {
+              const int q = m / kEvery;
+              if (q % 2 == 0) oa.issue_one(stn, kn, wave, q / 2);
+              else ob.issue_one(stn + kTileBytes, kn, wave, q / 2);
+            }
           }
         }
         if constexpr (NEXT) {
           f0.a[i] = oa.read(st1, i, 0);
-          f0.b[i] = ob.read(st1 + kTileBytes, i, 0);
+          if (i < kBJ) f0.b[i < kBJ ? i : 0] = ob.read(st1 + kTileBytes, i, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -300,9 +337,9 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_
     auto kloop = [&](auto ni_tag, auto nj_tag) {
       constexpr int NI = decltype(ni_tag)::value;
       constexpr int NJ = decltype(nj_tag)::value;
-      // Operand fragments of one k sub-step: A blocks 0..3, B blocks 0..3.
+      // Operand fragments of one k sub-step: A blocks 0..kBI-1, B blocks 0..kBJ-1.
       struct Frags {
-        bf16x8_t a[4], b[4];
+        bf16x8_t a[kBI], b[kBJ];
       };
       auto read_frags = [&](Frags& f, int64_t s, int q) {
         const lds_char* st = lds + (s % NS) * kStageBytes;
@@ -329,13 +366,13 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_
         constexpr bool NEXT = decltype(next_tag)::value;      // stage s + 1 exists
         const lds_char* st0 = lds + (s % NS) * kStageBytes;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < kBI; i++) {
 #pragma unroll
-          for (int j = 0; j < 4; j++)
+          for (int j = 0; j < kBJ; j++)
             if (i < NI && j < NJ)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.a[i], f0.b[j], acc[i][j], 0, 0, 0);
           if (i < NI) f1.a[i] = oa.read(st0, i, 1);
-          if (i < NJ) f1.b[i] = ob.read(st0 + kTileBytes, i, 1);
+          if (i < NJ) f1.b[i < kBJ ? i : 0] = ob.read(st0 + kTileBytes, i, 1);
           __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (NEXT) {
@@ -348,19 +385,23 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_
         const uint32_t stn = lds_base + static_cast<uint32_t>(((s + NS - 1) % NS) * kStageBytes);
         const lds_char* st1 = lds + ((s + 1) % NS) * kStageBytes;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < kBI; i++) {
 #pragma unroll
-          for (int j = 0; j < 4; j++) {
+          for (int j = 0; j < kBJ; j++) {
             if (i < NI && j < NJ)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.a[i], f1.b[j], acc[i][j], 0, 0, 0);
             if constexpr (REFILL) {
-              if (j == 0) oa.issue_one(stn, kn, wave, i);
-              if (j == 2) ob.issue_one(stn + kTileBytes, kn, wave, i);
+              const int m = i * kBJ + j;
+              if (m % kEvery == 0) {
+                const int q = m / kEvery;
+                if (q % 2 == 0) oa.issue_one(stn, kn, wave, q / 2);
+                else ob.issue_one(stn + kTileBytes, kn, wave, q / 2);
+              }
             }
           }
           if constexpr (NEXT) {
             if (i < NI) f0.a[i] = oa.read(st1, i, 0);
-            if (i < NJ) f0.b[i] = ob.read(st1 + kTileBytes, i, 0);
+            if (i < NJ) f0.b[i < kBJ ? i : 0] = ob.read(st1 + kTileBytes, i, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -382,39 +423,43 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_
       if (s < nsteps) stage(s, std::false_type{}, std::false_type{});
     };
     // Blocks of 32 rows (A) and columns (B) of this wave that hold output:
-    // 4 inside the matrix, 0 .. 3 at a tail; 2 and 3 run the full loop.
-    auto nblk = [](int64_t left) -> int { return left >= 128 ? 4 : left <= 0 ? 0 : left <= 32 ? 1 : 4; };
-    const int bi = nblk(M - (m0 + wm * 128)), bj = nblk(Nc - (n0 + wn * 128));
+    // all inside the matrix, 0 .. all - 1 at a tail; 1 and 0 take their own
+    // loop variants, the others run the full loop.
+    auto nblk = [](int64_t left, int all) -> int {
+      return left >= 32 * all ? all : left <= 0 ? 0 : left <= 32 ? 1 : all;
+    };
+    const int bi = nblk(M - (m0 + wm * (32 * kBI)), kBI), bj = nblk(Nc - (n0 + wn * (32 * kBJ)), kBJ);
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    using I4 = std::integral_constant<int, 4>;
-    if (bi == 4) {
-      if (bj == 4) kloop(I4{}, I4{});
-      else if (bj == 1) kloop(I4{}, I1{});
-      else kloop(I4{}, I0{});
+    using IA = std::integral_constant<int, kBI>;
+    using IB = std::integral_constant<int, kBJ>;
+    if (bi == kBI) {
+      if (bj == kBJ) kloop(IA{}, IB{});
+      else if (bj == 1) kloop(IA{}, I1{});
+      else kloop(IA{}, I0{});
     } else if (bi == 1) {
-      kloop(I1{}, I4{});
+      kloop(I1{}, IB{});
     } else {
-      kloop(I0{}, I4{});
+      kloop(I0{}, IB{});
     }
   }
 
-  // Epilogue.  Lane l holds, in acc[i][j][r], row m0 + 128 wm + 32 i +
-  // 8 (r / 4) + 4 (l / 32) + r % 4 of column n0 + 128 wn + 32 j + l % 32.  The
-  // element offsets (row * ld) are stepped by additions; interior tiles skip
-  // the row bound.
+  // Epilogue.  Lane l holds, in acc[i][j][r], row m0 + 32 kBI wm + 32 i +
+  // 8 (r / 4) + 4 (l / 32) + r % 4 of column n0 + 32 kBJ wn + 32 j + l % 32.
+  // The element offsets (row * ld) are stepped by additions; interior tiles
+  // skip the row bound.
   const bool full_rows = m0 + kRows <= M;
-  const int64_t row0 = m0 + wm * 128 + (l >> 5) * 4;
+  const int64_t row0 = m0 + wm * (32 * kBI) + (l >> 5) * 4;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int64_t col = n0 + wn * 128 + j * 32 + (l & 31);
+  for (int j = 0; j < kBJ; j++) {
+    const int64_t col = n0 + wn * (32 * kBJ) + j * 32 + (l & 31);
     if (col >= Nc) continue;
     const auto q = epi.prep(col, z);
     const int64_t ld = q.ld;
     int64_t oi = row0 * ld;
     if (full_rows) {
 #pragma unroll
-      for (int i = 0; i < 4; i++, oi += 32 * ld) {
+      for (int i = 0; i < kBI; i++, oi += 32 * ld) {
         if constexpr (kHasBatch<Epi>) {
           int64_t offs[16];
           float vals[16];
@@ -441,7 +486,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_dl(int64_t M, int64_t Nc, int64_
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; i++, oi += 32 * ld) {
+      for (int i = 0; i < kBI; i++, oi += 32 * ld) {
         int64_t orr = oi;
 #pragma unroll
         for (int rr = 0; rr < 4; rr++, orr += 8 * ld) {
@@ -472,6 +517,7 @@ template <class Epi, bool AKC, bool BKC>
 hipError_t run_t(const GemmOperands& op, int splits, int64_t kps, Epi epi, hipStream_t st) {
   const int64_t tilesM = (op.M + kRows - 1) / kRows, tilesN = (op.Nc + kRows - 1) / kRows;
   const int64_t nwg = tilesM * tilesN * splits;
+  constexpr int NT = WavesOf<Epi>::NT;
   auto kern = k_gemm_dl<Epi, AKC, BKC>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));

@@ -505,6 +505,8 @@ ssm_status ssm_adjoint_grad_noalloc(const ssm_dims* d, const ssm_layer* L, const
     if (slab < 1) return SSM_ERR_WORKSPACE;
     const int64_t dflt = ssm::bwd_hsub_slab_chunks(d->T, d->P, d->N, d->chunk);
     if (slab > dflt) slab = dflt;
+    // slabs at multiples of the carry's segments give the default path's values bit for bit
+    if (slab < dflt && slab >= ssm::kSegLen) slab -= slab % ssm::kSegLen;
   }
   void* ws = nullptr;
   if ((s = scratch_address(&ws)) != SSM_OK) return s;

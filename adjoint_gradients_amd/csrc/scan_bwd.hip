@@ -524,95 +524,112 @@ __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
 }
 
 // Carry of the adjoint sums between chunks, right to left:
-//   carry[K-1] = 0,  carry[k-1] = A_k carry[k] + umu[k],  A_k = exp(-alpha sum_{t in k} s_t).
-// carry[k] is a_{e+1} mu_{e+1} for the last token e of chunk k.  umu may be
-// carry itself (windowed aggregates composed in place): each element is read
-// before it is overwritten, by the same thread.  One launch walks chunks
-// k_hi - 1 down to k_lo: the carry entering chunk k_hi - 1 comes from `edge`
-// (written by the launch over the chunks to the right; zero when k_hi = K),
-// and the carry the walk hands on to chunk k_lo - 1 is left in `edge`.
-__global__ __launch_bounds__(256) void k_bwd_carry(int64_t K, int64_t P, int64_t N, int64_t k_lo, int64_t k_hi,
-                                                   const float* __restrict__ alpha,
-                                                   const double* __restrict__ ssum,
-                                                   const float* umu,
-                                                   float* carry, float* __restrict__ edge) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t PN = P * N;
-  if (e >= PN) return;
-  const int64_t p = e / N;
-  const float al2 = alpha[e] * kLog2e;
-  float cin = k_hi < K ? edge[e] : 0.0f;
-  // Blocks of 32 chunks: all loads of a block are issued before its stores
-  // (umu may alias carry, so the compiler would not move a load above an
-  // earlier store by itself); the walk is latency-bound with one thread per
-  // (channel, state), so the deeper the block, the more loads in flight.
-  constexpr int B = 32;
-  int64_t k = k_hi - 1;
-  for (; k - k_lo >= B - 1; k -= B) {
-    float u[B], sk[B];
-#pragma unroll
-    for (int r = 0; r < B; r++) {
-      u[r] = umu[(k - r) * PN + e];
-      sk[r] = static_cast<float>(ssum[(k - r) * P + p]);
-    }
-#pragma unroll
-    for (int r = 0; r < B; r++) {
-      carry[(k - r) * PN + e] = cin;
-      cin = fmaf(fast_exp2(-sk[r] * al2), cin, u[r]);
-    }
-  }
-  for (; k >= k_lo; k--) {
-    const float u = umu[k * PN + e];
-    carry[k * PN + e] = cin;
-    cin = fmaf(fast_exp2(-static_cast<float>(ssum[k * P + p]) * al2), cin, u);
-  }
-  if (k_lo > 0) edge[e] = cin;
-}
-
-// Windows of a whole number q = W / C of chunks.  The window term of chunk
-// k's aggregate is then the exact aggregate of chunk k + q scaled by the
-// decay across the W tokens in between:
+//   carry[K-1] = 0,  carry[k-1] = A_k carry[k] + u_k,  A_k = exp(-alpha sum_{t in k} s_t),
+// with u_k the aggregate of chunk k.  carry[k] is a_{e+1} mu_{e+1} for the
+// last token e of chunk k.
+//
+// Windows of a whole number q = W / C of chunks: the window term of chunk k's
+// aggregate is then the exact aggregate of chunk k + q scaled by the decay
+// across the W tokens in between,
 //   sum_{i in k} g_{i+W} c_{i+W} prod_{j=t0}^{i+W} a_j
 //     = exp(-alpha sum_{t=t0}^{t0+W-1} s_t) * umu_exact[k+q],
 // because the tokens i + W of a full chunk k are exactly chunk k + q (a
 // partial chunk is the last one, and has no partner inside the sequence).
-// The local pass therefore runs without window terms (one exp per state
-// element instead of two, no partner reads), and this fully parallel pass
-// writes each windowed aggregate into `out` (the carry array, which
-// k_bwd_carry then turns into carries in place).  Lanes of state 0 also write
-// the fp64 sum of s over the W tokens that follow each chunk, for the main
-// kernel.
-constexpr int64_t kComposeSpan = 32;  // chunks per thread of k_bwd_window_compose (at least)
+// The local pass then runs without window terms, and with q > 0 this kernel
+// forms each windowed aggregate from the exact ones as it reads them; lanes
+// of state 0 also write the fp64 sum of s over the W tokens that follow each
+// chunk, for the main kernel.  With q = 0 umu holds the aggregates as they
+// are.
+//
+// The walk is a segmented scan.  Chunks are grouped in segments of kSegLen at
+// fixed positions (segment j: chunks [j kSegLen, (j + 1) kSegLen)).  A
+// segment maps the carry entering it from the right to the carry leaving it
+// by x -> A_seg x + B_seg (A_seg the product of its A_k, B_seg its walk from
+// a zero carry).  A workgroup of kSegs wavefronts takes 64 (channel, state)
+// pairs and kSegs segments at a time: each wavefront loads its segment and
+// forms the segment's map; the maps meet in LDS; each wavefront passes the
+// group's entry carry through the maps of the segments to its right and
+// walks its own segment from there, storing the carries.  The dependent
+// chain is kSegLen + kSegs steps per group instead of one per chunk, and all
+// of a segment's loads are in flight together.  A launch over [k_lo, k_hi)
+// starts from `edge` (zero at the right end of the sequence) and leaves the
+// carry entering chunk k_lo - 1 in `edge`.  Launches that split the chunks
+// at multiples of kSegLen compute the same values as one launch over all of
+// them (empty segment slots are the identity map, applied exactly).
+constexpr int kSegs = 16;
 
-__global__ __launch_bounds__(256) void k_bwd_window_compose(int64_t K, int64_t P, int64_t N, int64_t q,
-                                                            int64_t k_lo, int64_t k_hi, int64_t span,
-                                                            const float* __restrict__ alpha,
-                                                            const double* __restrict__ ps64,
-                                                            const float* __restrict__ umu,
-                                                            float* __restrict__ out,
-                                                            double* __restrict__ hwin) {
+__global__ __launch_bounds__(64 * kSegs) void k_bwd_carry_seg(int64_t K, int64_t P, int64_t N, int64_t q,
+                                                              int64_t k_lo, int64_t k_hi,
+                                                              const float* __restrict__ alpha,
+                                                              const double* __restrict__ ssum,
+                                                              const double* __restrict__ ps64,
+                                                              const float* __restrict__ umu,
+                                                              float* __restrict__ carry, float* __restrict__ edge,
+                                                              double* __restrict__ hwin) {
+  constexpr int L = kSegLen;
+  __shared__ float sA[kSegs][64], sB[kSegs][64];
   const int64_t PN = P * N;
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (e >= PN) return;
-  const int64_t p = e / N;
-  const bool first_state = (e - p * N) == 0;
-  const float al2 = alpha[e] * kLog2e;
-  const int64_t k0 = k_lo + static_cast<int64_t>(blockIdx.y) * span;
-  const int64_t k1 = (k0 + span < k_hi) ? k0 + span : k_hi;
-#pragma unroll 4
-  for (int64_t k = k0; k < k1; k++) {
-    float u = umu[k * PN + e];
-    if (k + q < K) {
-      const float Ew = static_cast<float>(ps64[(k + q) * P + p] - ps64[k * P + p]);
-      u = fmaf(-fast_exp2(-Ew * al2), umu[(k + q) * PN + e], u);
+  const int lane = threadIdx.x & 63;
+  const int sg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+  const bool live = e < PN;
+  const int64_t ee = live ? e : PN - 1;  // clamped for reads
+  const int64_t p = ee / N;
+  const bool first_state = live && ee - p * N == 0;
+  const float al2 = alpha[ee] * kLog2e;
+  float cin = k_hi < K ? edge[ee] : 0.0f;
+  constexpr int64_t GL = static_cast<int64_t>(kSegs) * L;
+  for (int64_t g = (k_hi - 1) / GL; g >= 0 && (g + 1) * GL > k_lo; g--) {
+    int64_t s0 = g * GL + static_cast<int64_t>(sg) * L;
+    int64_t s1 = s0 + L;
+    s0 = s0 > k_lo ? s0 : k_lo;
+    s1 = s1 < k_hi ? s1 : k_hi;
+    // this segment's chunks [s0, s1), right to left (slots past it: u = 0, A = 1)
+    float u[L], d[L];
+#pragma unroll
+    for (int r = 0; r < L; r++) {
+      const int64_t k = s1 - 1 - r;
+      const bool valid = k >= s0;
+      const int64_t kk = valid ? k : k_lo;
+      float v = umu[kk * PN + ee];
+      if (q > 0 && kk + q < K) {
+        const float Ew = static_cast<float>(ps64[(kk + q) * P + p] - ps64[kk * P + p]);
+        v = fmaf(-fast_exp2(-Ew * al2), umu[(kk + q) * PN + ee], v);
+      }
+      const float dk = fast_exp2(-static_cast<float>(ssum[kk * P + p]) * al2);
+      u[r] = valid ? v : 0.0f;
+      d[r] = valid ? dk : 1.0f;
     }
-    out[k * PN + e] = u;
-    if (first_state) {
-      const int64_t kb = (k + q + 1 < K) ? k + q + 1 : K;
-      const int64_t ka = (k + 1 < K) ? k + 1 : K;
-      hwin[k * P + p] = ps64[kb * P + p] - ps64[ka * P + p];
+    float A = 1.0f, B = 0.0f;
+#pragma unroll
+    for (int r = 0; r < L; r++) {
+      B = fmaf(d[r], B, u[r]);
+      A *= d[r];
     }
+    sA[sg][lane] = A;
+    sB[sg][lane] = B;
+    __syncthreads();
+    float x = cin;
+    for (int j = kSegs - 1; j > sg; j--) x = fmaf(sA[j][lane], x, sB[j][lane]);
+#pragma unroll
+    for (int r = 0; r < L; r++) {
+      const int64_t k = s1 - 1 - r;
+      if (live && k >= s0) carry[k * PN + e] = x;
+      x = fmaf(d[r], x, u[r]);
+    }
+    if (q > 0 && first_state) {
+      for (int64_t k = s0; k < s1; k++) {
+        const int64_t kb = (k + q + 1 < K) ? k + q + 1 : K;
+        const int64_t ka = (k + 1 < K) ? k + 1 : K;
+        hwin[k * P + p] = ps64[kb * P + p] - ps64[ka * P + p];
+      }
+    }
+    float xn = cin;
+    for (int j = kSegs - 1; j >= 0; j--) xn = fmaf(sA[j][lane], xn, sB[j][lane]);
+    cin = xn;
+    __syncthreads();  // the next group overwrites the maps
   }
+  if (k_lo > 0 && live && sg == 0) edge[e] = cin;
 }
 
 #include "bwd_main.inl"
@@ -717,6 +734,7 @@ int64_t bwd_hsub_slab_chunks(int64_t T, int64_t P, int64_t N, int C) {
   if (per == 0) return K;
   int64_t n = static_cast<int64_t>(kHsubSlabBytes / per);
   if (n >= 32) n -= n % 32;  // whole rounds of resident workgroups when the channel blocks allow
+  else if (n >= kSegLen) n -= n % kSegLen;
   if (n < 1) n = 1;
   return n < K ? n : K;
 }
@@ -768,25 +786,13 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   }
   a.marks.rec(1, st);
   const int64_t PN = a.P * a.N;
-  // windowed aggregates of chunks [lo, hi) from exact ones (into the carry array)
-  auto compose_range = [&](int64_t lo, int64_t hi) -> hipError_t {
-    int64_t span = (hi - lo + 65534) / 65535;  // grid y stays within its limit
-    if (span < kComposeSpan) span = kComposeSpan;
-    k_bwd_window_compose<<<dim3(static_cast<unsigned>((PN + 255) / 256),
-                                static_cast<unsigned>((hi - lo + span - 1) / span)),
-                           256, 0, st>>>(K, a.P, a.N, a.W / a.C, lo, hi, span, a.alpha, a.ps64, a.umu, a.carry,
-                                         a.hwin);
-    return hipGetLastError();
-  };
+  // carries of chunks [lo, hi) (windowed aggregates composed on the way)
   auto carry_range = [&](int64_t lo, int64_t hi) -> hipError_t {
-    k_bwd_carry<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, lo, hi, a.alpha, a.ssum,
-                                                                        compose ? a.carry : a.umu, a.carry, a.edge);
+    k_bwd_carry_seg<<<static_cast<unsigned>((PN + 63) / 64), 64 * kSegs, 0, st>>>(
+        K, a.P, a.N, compose ? a.W / a.C : 0, lo, hi, a.alpha, a.ssum, a.ps64, a.umu, a.carry, a.edge, a.hwin);
     return hipGetLastError();
   };
-  if (!fused) {
-    if (compose && (e = compose_range(0, K)) != hipSuccess) return e;
-    if ((e = carry_range(0, K)) != hipSuccess) return e;
-  }
+  if (!fused && (e = carry_range(0, K)) != hipSuccess) return e;
   a.marks.rec(2, st);
   // Sub-chunk start states and the fused reverse walk.  States kept by the
   // forward cover every chunk: one launch.  Otherwise the gradient rebuilds
@@ -827,7 +833,6 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     if (fused) {
       k_bwd_local_hsub<IO, NL, G><<<grid, 64 * kWpb, rows_f, st>>>(am, NB);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      if (compose && (e = compose_range(k_lo, k_lo + nk)) != hipSuccess) return e;
       if ((e = carry_range(k_lo, k_lo + nk)) != hipSuccess) return e;
       am.hsub_ready = 1;
     } else if (hpass) {

@@ -108,9 +108,12 @@ size_t bwd_hsub_floats(int64_t T, int64_t P, int64_t N, int C);
 // Floats of every state of T tokens in the one-token-sub-chunk layout (the
 // store-everything baseline's buffer).
 size_t bwd_hall_floats(int64_t T, int64_t P, int64_t N, int C);
+// Chunks per segment of the carry's segmented scan.  Slabs that start at
+// multiples of it give the same carries, bit for bit, whatever their size.
+constexpr int kSegLen = 16;
 // Chunks per slab of the gradient's own sub-chunk-state region: at most
-// kHsubSlabBytes of states, a multiple of 32 chunks when that many fit, never
-// more than the chunk count.
+// kHsubSlabBytes of states, a multiple of 32 chunks when that many fit (else
+// of kSegLen when that many fit), never more than the chunk count.
 constexpr size_t kHsubSlabBytes = size_t(1) << 30;
 int64_t bwd_hsub_slab_chunks(int64_t T, int64_t P, int64_t N, int C);
 

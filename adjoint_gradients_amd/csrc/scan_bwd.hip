@@ -541,21 +541,12 @@ __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
 // chunk, for the main kernel.  With q = 0 umu holds the aggregates as they
 // are.
 //
-// The walk is a segmented scan.  Chunks are grouped in segments of kSegLen at
-// fixed positions (segment j: chunks [j kSegLen, (j + 1) kSegLen)).  A
-// segment maps the carry entering it from the right to the carry leaving it
-// by x -> A_seg x + B_seg (A_seg the product of its A_k, B_seg its walk from
-// a zero carry).  A workgroup of kSegs wavefronts takes 64 (channel, state)
-// pairs and kSegs segments at a time: each wavefront loads its segment and
-// forms the segment's map; the maps meet in LDS; each wavefront passes the
-// group's entry carry through the maps of the segments to its right and
-// walks its own segment from there, storing the carries.  The dependent
-// chain is kSegLen + kSegs steps per group instead of one per chunk, and all
-// of a segment's loads are in flight together.  A launch over [k_lo, k_hi)
-// starts from `edge` (zero at the right end of the sequence) and leaves the
-// carry entering chunk k_lo - 1 in `edge`.  Launches that split the chunks
-// at multiples of kSegLen compute the same values as one launch over all of
-// them (empty segment slots are the identity map, applied exactly).
+// The walk is a segmented scan (seg_affine_scan): segments of kSegLen chunks
+// at fixed positions, kSegs wavefronts per workgroup, 64 (channel, state)
+// pairs per wavefront.  A launch over [k_lo, k_hi) starts from `edge` (zero
+// at the right end of the sequence) and leaves the carry entering chunk
+// k_lo - 1 in `edge`.  Slabs that start at multiples of kSegLen give the
+// same carries, bit for bit, as one launch over all chunks.
 constexpr int kSegs = 16;
 
 __global__ __launch_bounds__(64 * kSegs) void k_bwd_carry_seg(int64_t K, int64_t P, int64_t N, int64_t q,
@@ -566,7 +557,6 @@ __global__ __launch_bounds__(64 * kSegs) void k_bwd_carry_seg(int64_t K, int64_t
                                                               const float* __restrict__ umu,
                                                               float* __restrict__ carry, float* __restrict__ edge,
                                                               double* __restrict__ hwin) {
-  constexpr int L = kSegLen;
   __shared__ float sA[kSegs][64], sB[kSegs][64];
   const int64_t PN = P * N;
   const int lane = threadIdx.x & 63;
@@ -575,61 +565,29 @@ __global__ __launch_bounds__(64 * kSegs) void k_bwd_carry_seg(int64_t K, int64_t
   const bool live = e < PN;
   const int64_t ee = live ? e : PN - 1;  // clamped for reads
   const int64_t p = ee / N;
-  const bool first_state = live && ee - p * N == 0;
   const float al2 = alpha[ee] * kLog2e;
-  float cin = k_hi < K ? edge[ee] : 0.0f;
-  constexpr int64_t GL = static_cast<int64_t>(kSegs) * L;
-  for (int64_t g = (k_hi - 1) / GL; g >= 0 && (g + 1) * GL > k_lo; g--) {
-    int64_t s0 = g * GL + static_cast<int64_t>(sg) * L;
-    int64_t s1 = s0 + L;
-    s0 = s0 > k_lo ? s0 : k_lo;
-    s1 = s1 < k_hi ? s1 : k_hi;
-    // this segment's chunks [s0, s1), right to left (slots past it: u = 0, A = 1)
-    float u[L], d[L];
-#pragma unroll
-    for (int r = 0; r < L; r++) {
-      const int64_t k = s1 - 1 - r;
-      const bool valid = k >= s0;
-      const int64_t kk = valid ? k : k_lo;
-      float v = umu[kk * PN + ee];
-      if (q > 0 && kk + q < K) {
-        const float Ew = static_cast<float>(ps64[(kk + q) * P + p] - ps64[kk * P + p]);
-        v = fmaf(-fast_exp2(-Ew * al2), umu[(kk + q) * PN + ee], v);
-      }
-      const float dk = fast_exp2(-static_cast<float>(ssum[kk * P + p]) * al2);
-      u[r] = valid ? v : 0.0f;
-      d[r] = valid ? dk : 1.0f;
+  const float cin = k_hi < K ? edge[ee] : 0.0f;
+  auto load = [&](int64_t k, float* u, float* d) {
+    float v = umu[k * PN + ee];
+    if (q > 0 && k + q < K) {
+      const float Ew = static_cast<float>(ps64[(k + q) * P + p] - ps64[k * P + p]);
+      v = fmaf(-fast_exp2(-Ew * al2), umu[(k + q) * PN + ee], v);
     }
-    float A = 1.0f, B = 0.0f;
-#pragma unroll
-    for (int r = 0; r < L; r++) {
-      B = fmaf(d[r], B, u[r]);
-      A *= d[r];
+    *u = v;
+    *d = fast_exp2(-static_cast<float>(ssum[k * P + p]) * al2);
+  };
+  auto store = [&](int64_t k, float x) {
+    if (live) carry[k * PN + e] = x;
+  };
+  const float out = seg_affine_scan<kSegLen, kSegs, true>(k_lo, k_hi, cin, sA, sB, sg, lane, load, store);
+  if (k_lo > 0 && live && sg == 0) edge[e] = out;
+  if (q > 0 && live && ee - p * N == 0) {
+    for (int64_t k = k_lo + sg; k < k_hi; k += kSegs) {
+      const int64_t kb = (k + q + 1 < K) ? k + q + 1 : K;
+      const int64_t ka = (k + 1 < K) ? k + 1 : K;
+      hwin[k * P + p] = ps64[kb * P + p] - ps64[ka * P + p];
     }
-    sA[sg][lane] = A;
-    sB[sg][lane] = B;
-    __syncthreads();
-    float x = cin;
-    for (int j = kSegs - 1; j > sg; j--) x = fmaf(sA[j][lane], x, sB[j][lane]);
-#pragma unroll
-    for (int r = 0; r < L; r++) {
-      const int64_t k = s1 - 1 - r;
-      if (live && k >= s0) carry[k * PN + e] = x;
-      x = fmaf(d[r], x, u[r]);
-    }
-    if (q > 0 && first_state) {
-      for (int64_t k = s0; k < s1; k++) {
-        const int64_t kb = (k + q + 1 < K) ? k + q + 1 : K;
-        const int64_t ka = (k + 1 < K) ? k + 1 : K;
-        hwin[k * P + p] = ps64[kb * P + p] - ps64[ka * P + p];
-      }
-    }
-    float xn = cin;
-    for (int j = kSegs - 1; j >= 0; j--) xn = fmaf(sA[j][lane], xn, sB[j][lane]);
-    cin = xn;
-    __syncthreads();  // the next group overwrites the maps
   }
-  if (k_lo > 0 && live && sg == 0) edge[e] = cin;
 }
 
 #include "bwd_main.inl"

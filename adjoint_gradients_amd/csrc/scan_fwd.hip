@@ -9,7 +9,7 @@
 // Time is cut into chunks of C tokens.  Three launches:
 //   1. k_fwd_local : every (chunk, channel block) scans its chunk from h = 0
 //                    and records the end state and sum_t s_t (fp64).
-//   2. k_fwd_carry : one thread per (p, n) walks the chunks in order and
+//   2. k_fwd_carry : per (p, n), a segmented scan over the chunks in order
 //                    composes the affine chunk maps h -> A_k h + hloc_k with
 //                    A_k = exp(-alpha sum_{t in k} s_t); it writes the state
 //                    entering every chunk, h_{kC-1}, which is also the saved
@@ -78,23 +78,34 @@ __global__ __launch_bounds__(64) void k_fwd_local(int64_t T, int64_t P, int64_t 
   }
 }
 
-__global__ __launch_bounds__(256) void k_fwd_carry(int64_t K, int64_t P, int64_t N,
-                                                   const float* __restrict__ alpha,
-                                                   const double* __restrict__ ssum,
-                                                   const float* __restrict__ hloc,
-                                                   float* __restrict__ h_ckpt) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+// The carry as a segmented scan (seg_affine_scan): segments of kSegLen chunks,
+// kFwdSegs wavefronts per workgroup, 64 (channel, state) pairs per wavefront,
+// so the dependent chain is kSegLen + kFwdSegs steps per kSegLen kFwdSegs
+// chunks instead of one per chunk.
+constexpr int kFwdSegs = 16;
+
+__global__ __launch_bounds__(64 * kFwdSegs) void k_fwd_carry(int64_t K, int64_t P, int64_t N,
+                                                            const float* __restrict__ alpha,
+                                                            const double* __restrict__ ssum,
+                                                            const float* __restrict__ hloc,
+                                                            float* __restrict__ h_ckpt) {
+  __shared__ float sA[kFwdSegs][64], sB[kFwdSegs][64];
   const int64_t PN = P * N;
-  if (e >= PN) return;
-  const int64_t p = e / N;
-  const float al2 = alpha[e] * kLog2e;
-  float hin = 0.0f;
-#pragma unroll 8
-  for (int64_t k = 0; k < K; k++) {
-    h_ckpt[k * PN + e] = hin;
-    const float A = fast_exp2(-static_cast<float>(ssum[k * P + p]) * al2);
-    hin = fmaf(A, hin, hloc[k * PN + e]);
-  }
+  const int lane = threadIdx.x & 63;
+  const int sg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+  const bool live = e < PN;
+  const int64_t ee = live ? e : PN - 1;  // clamped for reads
+  const int64_t p = ee / N;
+  const float al2 = alpha[ee] * kLog2e;
+  auto load = [&](int64_t k, float* u, float* d) {
+    *u = hloc[k * PN + ee];
+    *d = fast_exp2(-static_cast<float>(ssum[k * P + p]) * al2);
+  };
+  auto store = [&](int64_t k, float x) {
+    if (live) h_ckpt[k * PN + e] = x;
+  };
+  seg_affine_scan<kSegLen, kFwdSegs, false>(0, K, 0.0f, sA, sB, sg, lane, load, store);
 }
 
 template <typename IO, int NL, int G>
@@ -334,8 +345,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.marks.rec(2, st);
   const int64_t PN = a.P * a.N;
-  k_fwd_carry<<<static_cast<unsigned>((PN + 255) / 256), 256, 0, st>>>(K, a.P, a.N, a.alpha, a.ssum, a.hloc,
-                                                                      a.h_ckpt);
+  k_fwd_carry<<<static_cast<unsigned>((PN + 63) / 64), 64 * kFwdSegs, 0, st>>>(K, a.P, a.N, a.alpha, a.ssum,
+                                                                              a.hloc, a.h_ckpt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.marks.rec(3, st);
   if (staged) {

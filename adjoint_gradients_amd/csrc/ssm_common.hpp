@@ -129,4 +129,76 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Segmented scan of an affine recurrence over chunks, x <- d_k x + u_k, one
+// value per lane: chunks k_lo .. k_hi - 1 in order (REV: k_hi - 1 down to
+// k_lo), entering with x = cin; store(k, x) receives the value entering chunk
+// k and the return value is the one leaving the range.
+//
+// Chunks are grouped in segments of L at fixed positions (segment j: chunks
+// [j L, (j + 1) L)).  A segment maps the value entering it to the value
+// leaving it by x -> A x + B (A the product of its d_k, B its walk from zero).
+// A workgroup of S wavefronts (its lanes the same 64 independent recurrences
+// in every wavefront) takes S segments at a time: each wavefront loads its
+// segment through load(k, &u, &d) (all L loads in flight together) and forms
+// the segment's map; the maps meet in LDS; each wavefront passes the group's
+// entry value through the maps of the segments before its own and walks its
+// segment from there, calling store.  The dependent chain is L + S steps per
+// group instead of one per chunk.  Empty slots of a partial segment are the
+// identity map (d = 1, u = 0), applied exactly, so launches that split a
+// range at multiples of L give the same values, bit for bit, as one launch.
+// Every wavefront of the workgroup must call this (it holds barriers).
+template <int L, int S, bool REV, class Load, class Store>
+__device__ __forceinline__ float seg_affine_scan(int64_t k_lo, int64_t k_hi, float cin, float (&sA)[S][64],
+                                                 float (&sB)[S][64], int sg, int lane, Load load, Store store) {
+  constexpr int64_t GL = static_cast<int64_t>(S) * L;
+  const int64_t g_first = REV ? (k_hi - 1) / GL : k_lo / GL;
+  const int64_t g_last = REV ? k_lo / GL : (k_hi - 1) / GL;
+  for (int64_t g = g_first; REV ? g >= g_last : g <= g_last; g += REV ? -1 : 1) {
+    int64_t s0 = g * GL + static_cast<int64_t>(sg) * L;
+    int64_t s1 = s0 + L;
+    s0 = s0 > k_lo ? s0 : k_lo;
+    s1 = s1 < k_hi ? s1 : k_hi;
+    float u[L], d[L];
+#pragma unroll
+    for (int r = 0; r < L; r++) {
+      const int64_t k = REV ? s1 - 1 - r : s0 + r;
+      const bool valid = REV ? k >= s0 : k < s1;
+      float uk, dk;
+      load(valid ? k : k_lo, &uk, &dk);
+      u[r] = valid ? uk : 0.0f;
+      d[r] = valid ? dk : 1.0f;
+    }
+    float A = 1.0f, B = 0.0f;
+#pragma unroll
+    for (int r = 0; r < L; r++) {
+      B = fmaf(d[r], B, u[r]);
+      A *= d[r];
+    }
+    sA[sg][lane] = A;
+    sB[sg][lane] = B;
+    __syncthreads();
+    float x = cin;
+    if (REV) {
+      for (int j = S - 1; j > sg; j--) x = fmaf(sA[j][lane], x, sB[j][lane]);
+    } else {
+      for (int j = 0; j < sg; j++) x = fmaf(sA[j][lane], x, sB[j][lane]);
+    }
+#pragma unroll
+    for (int r = 0; r < L; r++) {
+      const int64_t k = REV ? s1 - 1 - r : s0 + r;
+      if (REV ? k >= s0 : k < s1) store(k, x);
+      x = fmaf(d[r], x, u[r]);
+    }
+    float xn = cin;
+    if (REV) {
+      for (int j = S - 1; j >= 0; j--) xn = fmaf(sA[j][lane], xn, sB[j][lane]);
+    } else {
+      for (int j = 0; j < S; j++) xn = fmaf(sA[j][lane], xn, sB[j][lane]);
+    }
+    cin = xn;
+    __syncthreads();  // the next group overwrites the maps
+  }
+  return cin;
+}
+
 }  // namespace ssm

@@ -74,17 +74,37 @@ constexpr size_t bwd_main_lds_floats(int NL, int G) {
 
 }  // namespace
 
-// Exclusive prefix over chunks of the per-chunk sums of s, in fp64.
-__global__ __launch_bounds__(256) void k_bwd_prefix(int64_t K, int64_t P, const double* __restrict__ ssum,
-                                                    double* __restrict__ ps64) {
-  const int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (p >= P) return;
+// Exclusive prefix over chunks of the per-chunk sums of s, in fp64:
+// ps64[0] = 0, ps64[k + 1] = ps64[k] + ssum[k].  A workgroup of kPrefixRanges
+// wavefronts takes 64 channels; wavefront w owns the w-th of kPrefixRanges
+// contiguous ranges of chunks.  Each wavefront sums its range, the range
+// totals meet in LDS, and each wavefront then writes its range's prefix
+// starting from the sum of the totals before it (in range order), so the
+// dependent chain is K / kPrefixRanges additions instead of K.
+constexpr int kPrefixRanges = 16;
+
+__global__ __launch_bounds__(64 * kPrefixRanges) void k_bwd_prefix(int64_t K, int64_t P,
+                                                                   const double* __restrict__ ssum,
+                                                                   double* __restrict__ ps64) {
+  __shared__ double tot[kPrefixRanges][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+  const bool live = p < P;
+  const int64_t pc = live ? p : P - 1;  // clamped for reads
+  const int64_t k0 = K * w / kPrefixRanges, k1 = K * (w + 1) / kPrefixRanges;
   double acc = 0.0;
-  ps64[p] = 0.0;
 #pragma unroll 8
-  for (int64_t k = 0; k < K; k++) {
-    acc += ssum[k * P + p];
-    ps64[(k + 1) * P + p] = acc;
+  for (int64_t k = k0; k < k1; k++) acc += ssum[k * P + pc];
+  tot[w][lane] = acc;
+  __syncthreads();
+  double run = 0.0;
+  for (int j = 0; j < w; j++) run += tot[j][lane];
+  if (live && w == 0) ps64[p] = 0.0;
+#pragma unroll 8
+  for (int64_t k = k0; k < k1; k++) {
+    run += ssum[k * P + pc];
+    if (live) ps64[(k + 1) * P + p] = run;
   }
 }
 
@@ -608,6 +628,48 @@ __global__ __launch_bounds__(256) void k_bwd_reduce_dbdc(int64_t T, int64_t P, i
   store_io(dY + t * ldy + P + o, v);
 }
 
+// The same sums, four outputs per thread (OUT a multiple of 4): the NBW
+// partials of a token come as 16-byte loads, all in flight together, and
+// each output is summed over the workgroups in the same order as above.
+template <typename IO>
+__global__ __launch_bounds__(256) void k_bwd_reduce_dbdc4(int64_t T, int64_t P, int OUT, int64_t NBW,
+                                                          const float* __restrict__ part, IO* __restrict__ dY,
+                                                          int64_t ldy) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int Q = OUT / 4;
+  if (e >= T * Q) return;
+  const int64_t t = e / Q;
+  const int o = static_cast<int>(e % Q) * 4;
+  const float4* src = reinterpret_cast<const float4*>(part + t * NBW * OUT + o);
+  const int64_t step = OUT / 4;
+  float4 v = src[0];
+  int64_t wb = 1;
+  for (; wb + 4 <= NBW; wb += 4) {
+    float4 r[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) r[i] = src[(wb + i) * step];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v.x += r[i].x;
+      v.y += r[i].y;
+      v.z += r[i].z;
+      v.w += r[i].w;
+    }
+  }
+  for (; wb < NBW; wb++) {
+    const float4 r = src[wb * step];
+    v.x += r.x;
+    v.y += r.y;
+    v.z += r.z;
+    v.w += r.w;
+  }
+  IO* dst = dY + t * ldy + P + o;
+  store_io(dst, v.x);
+  store_io(dst + 1, v.y);
+  store_io(dst + 2, v.z);
+  store_io(dst + 3, v.w);
+}
+
 // dalpha and dbias: sums over chunks in a fixed order, in two stages so the
 // loads are spread over many threads: stage 1 sums KS slices of the chunk
 // range into tmp[KS][P*N + P], stage 2 adds the KS slice sums.
@@ -708,7 +770,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   const int64_t NB = pl.NB;
   hipError_t e;
   if constexpr (WIN) {
-    k_bwd_prefix<<<static_cast<unsigned>((a.P + 255) / 256), 256, 0, st>>>(K, a.P, a.ssum, a.ps64);
+    k_bwd_prefix<<<static_cast<unsigned>((a.P + 63) / 64), 64 * kPrefixRanges, 0, st>>>(K, a.P, a.ssum, a.ps64);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // A window of whole chunks is composed from exact chunk aggregates in the
@@ -805,8 +867,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   }
   a.marks.rec(3, st);
   const int OUT = 2 * static_cast<int>(a.N);
-  k_bwd_reduce_dbdc<IO><<<static_cast<unsigned>((a.T * OUT + 255) / 256), 256, 0, st>>>(
-      a.T, a.P, OUT, pl.NBW, a.part, static_cast<IO*>(a.dY), a.ldy);
+  if (OUT % 4 == 0)
+    k_bwd_reduce_dbdc4<IO><<<static_cast<unsigned>((a.T * (OUT / 4) + 255) / 256), 256, 0, st>>>(
+        a.T, a.P, OUT, pl.NBW, a.part, static_cast<IO*>(a.dY), a.ldy);
+  else
+    k_bwd_reduce_dbdc<IO><<<static_cast<unsigned>((a.T * OUT + 255) / 256), 256, 0, st>>>(
+        a.T, a.P, OUT, pl.NBW, a.part, static_cast<IO*>(a.dY), a.ldy);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.dalpha || a.dbias) {
     // the chunk aggregates (umu) are dead after the carry pass: reuse them as scratch

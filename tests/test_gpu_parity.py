@@ -75,7 +75,11 @@ def test_window_pinning(orc, W):
     if W < 512:
         exact = orc.layer_grad(oracle_inputs(inp), window=None)
         gap = rel_err(ref["dx"], exact["dx"])
+        err = rel_err(got["dx"], ref["dx"])
         say(f"  window-vs-exact gap (dx) = {gap:.2e}")
+        # a kernel that ran another window (W - 1, W + 1, or none) would miss
+        # the oracle by about this gap: it must be far above the error
+        assert err < gap / 100, (W, err, gap)
 
 
 @pytest.mark.parametrize("chunk", [7, 64, 200])
@@ -93,7 +97,9 @@ def test_window_whole_chunks(orc, chunk, W):
     inp = make_layer(window_pin_case(seed=102, T=700, P=8, N=4))
     got, ref = _run_case(orc, inp, W, chunk, f"winpin whole chunks C={chunk} W={W}")
     exact = orc.layer_grad(oracle_inputs(inp), window=None)
-    say(f"  window-vs-exact gap (dx) = {rel_err(ref['dx'], exact['dx']):.2e}")
+    gap = rel_err(ref["dx"], exact["dx"])
+    say(f"  window-vs-exact gap (dx) = {gap:.2e}")
+    assert rel_err(got["dx"], ref["dx"]) < gap / 100, (chunk, W, gap)
 
 
 def test_window_whole_chunks_bf16_n16(orc):

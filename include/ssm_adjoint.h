@@ -227,8 +227,11 @@ ssm_status ssm_adjoint_grad(const ssm_dims *dims, const ssm_layer *layer, const 
  * ssm_adjoint_grad without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving or
  * training loops, harnesses that forbid hipMalloc).  It computes the same
- * gradient with the same kernels (bitwise equal to ssm_adjoint_grad) and
- * calls no hipMalloc, hipFree or other allocating routine: its workspace is a
+ * gradient with the same kernels and calls no hipMalloc, hipFree or other
+ * allocating routine.  The result is bitwise equal to ssm_adjoint_grad's
+ * whenever its slab (below) holds at least 16 chunks, since the carry between
+ * chunks is then grouped the same way; a smaller slab rounds the carries
+ * differently, within fp32 rounding.  Its workspace is a
  * device array of SSM_NOALLOC_SCRATCH_BYTES bytes inside the library, one per
  * device, held until the process ends.  Whatever the gradient's fixed buffers
  * leave of it holds the slab of rebuilt sub-chunk states, so a larger problem

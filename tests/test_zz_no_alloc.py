@@ -46,10 +46,15 @@ def test_noalloc_matches_workspace_entry_point():
     cases = [
         # (T, P, N, io, window, chunk, sub-chunk states kept, seed): the first
         # needs several slabs of rebuilt states in the array, the second is
-        # smaller and reuses the array the first left behind
+        # smaller and reuses the array the first left behind.  The fourth (a
+        # window of whole chunks, so the chunk aggregates and the carries are
+        # formed slab by slab) runs 2 slabs of 80 and 48 chunks in the array
+        # against 1 slab of 128 in the workspace entry point: the segmented
+        # carry must give the same bits either way.
         (32768, 512, 16, "f32", 1000, 256, False, 71),
         (4096, 256, 16, "bf16", 4096, 256, False, 72),
         (3000, 96, 32, "f32", 512, 128, True, 73),
+        (32768, 512, 16, "f32", 4096, 256, False, 74),
     ]
     for T, P, N, io, W, C, sub, seed in cases:
         d = agm.make_dims(T, P, N, C, io)

@@ -183,6 +183,27 @@ def test_gradient_workspace_is_bounded(agm):
     assert agm.ssm_grad_slab_count(d3, 100, False) == 1
 
 
+def test_slabs_start_at_carry_segment_multiples(agm):
+    # A slab holds at most 1 GiB of sub-chunk states (C / 8 state vectors of
+    # P N floats per chunk), rounded down to a multiple of 32 chunks when that
+    # many fit, else of 16 (the carry between chunks is scanned in segments of
+    # 16 at fixed positions, so slab starts at multiples of 16 keep every
+    # carry independent of the slab size).
+    def slabs(T, P, N):
+        return agm.ssm_grad_slab_count(agm.make_dims(T, P, N, 256, "bf16"), 4096, False)
+
+    per = lambda P, N: 32 * P * N * 4  # bytes of one chunk's sub-chunk states
+    # 1 GiB holds 21 chunks at P = 6144, N = 64: rounded down to 16
+    assert (1 << 30) // per(6144, 64) == 21
+    assert slabs(256 * 100, 6144, 64) == 7  # ceil(100 / 16)
+    # 1 GiB holds 39 chunks at P = 3328, N = 64: rounded down to 32
+    assert (1 << 30) // per(3328, 64) == 39
+    assert slabs(256 * 100, 3328, 64) == 4  # ceil(100 / 32)
+    # fewer than 16 fit: no rounding (12 chunks at P = 10240, N = 64)
+    assert (1 << 30) // per(10240, 64) == 12
+    assert slabs(256 * 100, 10240, 64) == 9  # ceil(100 / 12)
+
+
 def test_stack_workspace_counts_normalising_layers(agm):
     d = agm.make_dims(1000, 48, 16, 64, "f32")
     plain = (agm.Layer * 3)(_layer(agm), _layer(agm), _layer(agm))

@@ -439,7 +439,12 @@ __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
   constexpr int NN = NL * G;
   constexpr int D = kBwdLocRing;
   constexpr int S = kSub;
-  extern __shared__ float rows[];  // [C][NN] b rows, then [C][NN] c rows
+  // The chunk's b and c rows are staged in parts of TP tokens (the whole
+  // chunk when its rows fit the staging area): [TP][NN] b rows, then [TP][NN]
+  // c rows.
+  constexpr int TP = static_cast<int>(kHsubRowLds / (2 * NN * 4)) / D * D;
+  static_assert(TP >= D, "a ring turn of rows fits the staging area");
+  extern __shared__ float rows[];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int grp = lane / CH, pl = lane % CH;
@@ -457,18 +462,21 @@ __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
   const int len = static_cast<int>(t1 - t0);
   const int nsub_max = (C + S - 1) / S;
   float* hsg = a.hsub + hsub_offset(k - a.hsub_k0, wave_live ? cb : 0, 0, NB, nsub_max, NL);
-  float* crow = rows + static_cast<size_t>(C) * NN;
-  {
-    const int per = len * NN / 4;
-    const float4* b4 = reinterpret_cast<const float4*>(a.b + t0 * NN);
-    const float4* c4 = reinterpret_cast<const float4*>(a.c + t0 * NN);
+  const int tp = len < TP ? len : TP;  // tokens per staged part
+  float* crow = rows + static_cast<size_t>(tp) * NN;
+  // rows of tokens [lo, lo + n) -> the staging area (the caller synchronises)
+  auto stage = [&](int lo, int n) {
+    const int per = n * NN / 4;
+    const float4* b4 = reinterpret_cast<const float4*>(a.b + (t0 + lo) * NN);
+    const float4* c4 = reinterpret_cast<const float4*>(a.c + (t0 + lo) * NN);
     float4* db4 = reinterpret_cast<float4*>(rows);
     float4* dc4 = reinterpret_cast<float4*>(crow);
     for (int e = tid; e < per; e += 64 * kWpb) {
       db4[e] = b4[e];
       dc4[e] = c4[e];
     }
-  }
+  };
+  stage(0, tp);
   float al2[NL], h[NL], Q[NL], U[NL];
 #pragma unroll
   for (int j = 0; j < NL; j++) {
@@ -492,6 +500,7 @@ __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
     if (q < len) ld(q, t0 + q);
   __syncthreads();  // staged rows visible
   static_assert(D % S == 0 || S % D == 0, "ring and sub-chunk sizes");
+  int plo = 0;  // first token of the staged part
   auto tok = [&](int r, int tau, bool fetch, int ahead) {
     if (tau % S == 0 && wave_live) {
 #pragma unroll
@@ -501,8 +510,8 @@ __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
     const float ns = -rs[r];
     const float xv = raw_to_f32(rx[r]);
     const float gv = rg[r];
-    const float* rb = rows + tau * NN + n0;
-    const float* rc = crow + tau * NN + n0;
+    const float* rb = rows + (tau - plo) * NN + n0;
+    const float* rc = crow + (tau - plo) * NN + n0;
 #pragma unroll
     for (int j = 0; j < NL; j += 4) {
       const float4 vb = *reinterpret_cast<const float4*>(rb + j);
@@ -518,10 +527,21 @@ __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
       }
     }
   };
+  // the next part's rows, once every wavefront is done with this part's
+  // (parts are whole ring turns)
+  auto next_part = [&](int q8) {
+    if (q8 > plo && q8 - plo == tp) {
+      __syncthreads();
+      plo = q8;
+      stage(plo, len - plo < tp ? len - plo : tp);
+      __syncthreads();
+    }
+  };
   if (len % D == 0) {
     // whole ring turns: fetches past the chunk end re-read its last token,
     // so the ring body has no per-token branch
     for (int q8 = 0; q8 < len; q8 += D) {
+      next_part(q8);
 #pragma unroll
       for (int r = 0; r < D; r++) {
         const int tau = q8 + r;
@@ -530,6 +550,7 @@ __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
     }
   } else {
     for (int q8 = 0; q8 < len; q8 += D) {
+      next_part(q8);
 #pragma unroll
       for (int r = 0; r < D; r++) {
         const int tau = q8 + r;
@@ -783,10 +804,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   // forward walk that rebuilds the sub-chunk states, slab by slab from the
   // right (the carry enters each chunk from its right, so a slab needs only
   // the aggregates of itself and of the slabs already done).
-  const size_t rows_f = static_cast<size_t>(2) * a.C * NNc * 4;
+  // (b and c rows in LDS, in parts of at most kHsubRowLds bytes)
+  const size_t rows_f = std::min(static_cast<size_t>(2) * a.C * NNc * 4, kHsubRowLds / (2 * NNc * 4) / kBwdLocRing *
+                                                                           kBwdLocRing * 2 * NNc * 4);
   // (every state kept by the forward, a.hall: nothing is rebuilt)
   const bool given = a.hsub_given || a.hall != nullptr;
-  const bool fused = !given && !wl && NNc % 4 == 0 && rows_f <= kHsubRowLds;
+  const bool fused = !given && !wl && NNc % 4 == 0;
   if (!fused) {
     const size_t rows_b = static_cast<size_t>(wl ? 2 : 1) * a.C * NNc * 4;
     const dim3 gs(static_cast<unsigned>(K), static_cast<unsigned>((NB + kBwdLocWpb - 1) / kBwdLocWpb));

@@ -30,6 +30,8 @@
 // Sums over channels (db, dc) go through an LDS transpose per wavefront, an
 // LDS sum over the wavefronts of the workgroup, and a deterministic final sum
 // over workgroups in a separate kernel.
+#include <type_traits>
+
 #include "ssm_common.hpp"
 #include "ssm_kernels.hpp"
 #include "red_layout.hpp"
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(256) void k_bwd_hsub(BwdArgs a, int64_t NB) {
 // token goes to the sub-chunk-state slab (layout of k_bwd_hsub).  A 4-wavefront
 // workgroup takes 4 channel blocks of one chunk; the chunk's b and c rows are
 // staged once into LDS, s, x and g come through an 8-token register ring.
-template <typename IO, int NL, int G>
+template <typename IO, int NL, int G, bool PARTS>
 __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
   constexpr int CH = 64 / G;
   constexpr int NN = NL * G;
@@ -501,60 +503,63 @@ __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
   __syncthreads();  // staged rows visible
   static_assert(D % S == 0 || S % D == 0, "ring and sub-chunk sizes");
   int plo = 0;  // first token of the staged part
-  auto tok = [&](int r, int tau, bool fetch, int ahead) {
-    if (tau % S == 0 && wave_live) {
+  {
+    constexpr bool MULTI = PARTS;
+    auto tok = [&](int r, int tau, bool fetch, int ahead) {
+      if (tau % S == 0 && wave_live) {
 #pragma unroll
-      for (int j = 0; j < NL; j++) hsg[((tau / S) * NL + j) * 64 + lane] = h[j];
-    }
-    if (fetch) ld((r + D - 1) % D, t0 + ahead);
-    const float ns = -rs[r];
-    const float xv = raw_to_f32(rx[r]);
-    const float gv = rg[r];
-    const float* rb = rows + (tau - plo) * NN + n0;
-    const float* rc = crow + (tau - plo) * NN + n0;
-#pragma unroll
-    for (int j = 0; j < NL; j += 4) {
-      const float4 vb = *reinterpret_cast<const float4*>(rb + j);
-      const float4 vc = *reinterpret_cast<const float4*>(rc + j);
-      const float bq[4] = {vb.x, vb.y, vb.z, vb.w};
-      const float cq[4] = {vc.x, vc.y, vc.z, vc.w};
-#pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const float av = fast_exp2(ns * al2[j + jj]);
-        h[j + jj] = fmaf(av, h[j + jj], bq[jj] * xv);
-        Q[j + jj] *= av;
-        U[j + jj] = fmaf(gv * cq[jj], Q[j + jj], U[j + jj]);
+        for (int j = 0; j < NL; j++) hsg[((tau / S) * NL + j) * 64 + lane] = h[j];
       }
-    }
-  };
-  // the next part's rows, once every wavefront is done with this part's
-  // (parts are whole ring turns)
-  auto next_part = [&](int q8) {
-    if (q8 > plo && q8 - plo == tp) {
-      __syncthreads();
-      plo = q8;
-      stage(plo, len - plo < tp ? len - plo : tp);
-      __syncthreads();
-    }
-  };
-  if (len % D == 0) {
-    // whole ring turns: fetches past the chunk end re-read its last token,
-    // so the ring body has no per-token branch
-    for (int q8 = 0; q8 < len; q8 += D) {
-      next_part(q8);
+      if (fetch) ld((r + D - 1) % D, t0 + ahead);
+      const float ns = -rs[r];
+      const float xv = raw_to_f32(rx[r]);
+      const float gv = rg[r];
+      const float* rb = rows + (MULTI ? tau - plo : tau) * NN + n0;
+      const float* rc = crow + (MULTI ? tau - plo : tau) * NN + n0;
 #pragma unroll
-      for (int r = 0; r < D; r++) {
-        const int tau = q8 + r;
-        tok(r, tau, true, (tau + D - 1 < len) ? tau + D - 1 : len - 1);
+      for (int j = 0; j < NL; j += 4) {
+        const float4 vb = *reinterpret_cast<const float4*>(rb + j);
+        const float4 vc = *reinterpret_cast<const float4*>(rc + j);
+        const float bq[4] = {vb.x, vb.y, vb.z, vb.w};
+        const float cq[4] = {vc.x, vc.y, vc.z, vc.w};
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const float av = fast_exp2(ns * al2[j + jj]);
+          h[j + jj] = fmaf(av, h[j + jj], bq[jj] * xv);
+          Q[j + jj] *= av;
+          U[j + jj] = fmaf(gv * cq[jj], Q[j + jj], U[j + jj]);
+        }
       }
-    }
-  } else {
-    for (int q8 = 0; q8 < len; q8 += D) {
-      next_part(q8);
+    };
+    // the next part's rows, once every wavefront is done with this part's
+    // (parts are whole ring turns)
+    auto next_part = [&](int q8) {
+      if (MULTI && q8 > plo && q8 - plo == tp) {
+        __syncthreads();
+        plo = q8;
+        stage(plo, len - plo < tp ? len - plo : tp);
+        __syncthreads();
+      }
+    };
+    if (len % D == 0) {
+      // whole ring turns: fetches past the chunk end re-read its last token,
+      // so the ring body has no per-token branch
+      for (int q8 = 0; q8 < len; q8 += D) {
+        next_part(q8);
 #pragma unroll
-      for (int r = 0; r < D; r++) {
-        const int tau = q8 + r;
-        if (tau < len) tok(r, tau, tau + D - 1 < len, tau + D - 1);
+        for (int r = 0; r < D; r++) {
+          const int tau = q8 + r;
+          tok(r, tau, true, (tau + D - 1 < len) ? tau + D - 1 : len - 1);
+        }
+      }
+    } else {
+      for (int q8 = 0; q8 < len; q8 += D) {
+        next_part(q8);
+#pragma unroll
+        for (int r = 0; r < D; r++) {
+          const int tau = q8 + r;
+          if (tau < len) tok(r, tau, tau + D - 1 < len, tau + D - 1);
+        }
       }
     }
   }
@@ -854,8 +859,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
                             static_cast<int>(rows_h));
     if (e != hipSuccess) return e;
   }
+  // rows staged in parts when a chunk's do not fit the staging area at once
+  const bool parts = static_cast<size_t>(2) * a.C * NNc * 4 > kHsubRowLds;
+  auto fk = parts ? k_bwd_local_hsub<IO, NL, G, true> : k_bwd_local_hsub<IO, NL, G, false>;
   if (fused) {
-    auto fk = k_bwd_local_hsub<IO, NL, G>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(fk), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(rows_f));
     if (e != hipSuccess) return e;
@@ -874,7 +881,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     am.hsub_ready = given ? 1 : 0;
     const dim3 grid(static_cast<unsigned>(nk), static_cast<unsigned>(pl.NBW));
     if (fused) {
-      k_bwd_local_hsub<IO, NL, G><<<grid, 64 * kWpb, rows_f, st>>>(am, NB);
+      fk<<<grid, 64 * kWpb, rows_f, st>>>(am, NB);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if ((e = carry_range(k_lo, k_lo + nk)) != hipSuccess) return e;
       am.hsub_ready = 1;

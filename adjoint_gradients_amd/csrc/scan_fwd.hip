@@ -18,6 +18,8 @@
 //                    What carries the argument).
 //   3. k_fwd_final : every (chunk, channel block) rescans its chunk from the
 //                    exact entering state and writes y.
+#include <type_traits>
+
 #include "ssm_common.hpp"
 #include "ssm_kernels.hpp"
 
@@ -174,18 +176,22 @@ constexpr size_t kFwdRowLds = 32 * 1024;  // LDS bytes for staged rows
 
 template <int NQ>
 __device__ __forceinline__ void stage_rows(float* rows, const float* __restrict__ const (&src)[NQ], int64_t t0,
-                                          int len, int NN, int C, int tid) {
-  // rows[q][tau][n] = src[q][(t0 + tau) * NN + n], tau < len; float4 granularity
+                                          int len, int NN, int stride, int tid) {
+  // rows[q][tau][n] = src[q][(t0 + tau) * NN + n], tau < len, with `stride`
+  // tokens per row kind; float4 granularity
   const int per = len * NN / 4;
 #pragma unroll
   for (int q = 0; q < NQ; q++) {
     const float4* s4 = reinterpret_cast<const float4*>(src[q] + t0 * NN);
-    float4* d4 = reinterpret_cast<float4*>(rows + static_cast<size_t>(q) * C * NN);
+    float4* d4 = reinterpret_cast<float4*>(rows + static_cast<size_t>(q) * stride * NN);
     for (int e = tid; e < per; e += 64 * kFwdWpb) d4[e] = s4[e];
   }
 }
 
-template <typename IO, int NL, int G, bool FINAL>
+// The staged forward walk.  PARTS: the chunk's rows are staged in parts (the
+// launcher picks this instantiation when a chunk's rows exceed the staging
+// area); otherwise the whole chunk is staged at once.
+template <typename IO, int NL, int G, bool FINAL, bool PARTS>
 __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_t N, int C, int64_t NB,
                                                     const float* __restrict__ sp, const IO* __restrict__ x,
                                                     const float* __restrict__ b, const float* __restrict__ c,
@@ -196,7 +202,12 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
   constexpr int CH = 64 / G;
   constexpr int NN = NL * G;
   constexpr int D = kFwdRing;
-  extern __shared__ float rows[];  // [FINAL ? 2 : 1][C][NN]
+  constexpr int NQ = FINAL ? 2 : 1;  // staged row kinds: b (, c)
+  // The chunk's rows are staged in parts of TP tokens (the whole chunk when
+  // its rows fit the staging area): [NQ][TP][NN].
+  constexpr int TP = static_cast<int>(kFwdRowLds / (NQ * NN * 4)) / D * D;
+  static_assert(TP >= D, "a ring turn of rows fits the staging area");
+  extern __shared__ float rows[];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int grp = lane / CH, pl = lane % CH;
@@ -209,13 +220,17 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
   const int64_t t0 = k * C;
   const int64_t t1 = (t0 + C < T) ? t0 + C : T;
   const int len = static_cast<int>(t1 - t0);
-  if constexpr (FINAL) {
-    const float* __restrict__ srcs[2] = {b, c};
-    stage_rows<2>(rows, srcs, t0, len, NN, C, tid);
-  } else {
-    const float* __restrict__ srcs[1] = {b};
-    stage_rows<1>(rows, srcs, t0, len, NN, C, tid);
-  }
+  const int tp = len < TP ? len : TP;  // tokens per staged part
+  auto stage = [&](int lo, int n) {
+    if constexpr (FINAL) {
+      const float* __restrict__ srcs[2] = {b, c};
+      stage_rows<2>(rows, srcs, t0 + lo, n, NN, tp, tid);
+    } else {
+      const float* __restrict__ srcs[1] = {b};
+      stage_rows<1>(rows, srcs, t0 + lo, n, NN, tp, tid);
+    }
+  };
+  stage(0, tp);
   float al2[NL], h[NL];
 #pragma unroll
   for (int j = 0; j < NL; j++) {
@@ -241,73 +256,89 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
   float* hag = (FINAL && hall && cb < NB) ? hall + hsub_offset(k, cb, 0, NB, C, NL) + lane : nullptr;
   static_assert(D % kSub == 0, "ring length a multiple of the sub-chunk");
   double ss = 0.0;
-  // One token of the walk; `ahead` is the token whose s and x the ring
-  // fetches now (D - 1 tokens on).
-  auto token = [&](int r, int tau, bool fetch, int64_t ahead) {
-    if (FINAL && r % kSub == 0 && hsg) {
+  int plo = 0;  // first token of the staged part
+  {
+    constexpr bool MULTI = PARTS;
+    // One token of the walk; `ahead` is the token whose s and x the ring
+    // fetches now (D - 1 tokens on).
+    auto token = [&](int r, int tau, bool fetch, int64_t ahead) {
+      if (FINAL && r % kSub == 0 && hsg) {
 #pragma unroll
-      for (int j = 0; j < NL; j++) hsg[(tau / kSub * NL + j) * 64] = h[j];
-    }
-    if (fetch) ld((r + D - 1) % D, ahead);
-    const float ns = -rs[r];
-    const float xv = raw_to_f32(rx[r]);
-    const float* rb = rows + tau * NN + n0;
-    float bt[NL];
-#pragma unroll
-    for (int j = 0; j < NL; j += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(rb + j);
-      bt[j] = v.x; bt[j + 1] = v.y; bt[j + 2] = v.z; bt[j + 3] = v.w;
-    }
-    if constexpr (FINAL) {
-      const float* rc = rows + static_cast<size_t>(C) * NN + tau * NN + n0;
-      float acc = 0.0f;
+        for (int j = 0; j < NL; j++) hsg[(tau / kSub * NL + j) * 64] = h[j];
+      }
+      if (fetch) ld((r + D - 1) % D, ahead);
+      const float ns = -rs[r];
+      const float xv = raw_to_f32(rx[r]);
+      const float* rb = rows + (MULTI ? tau - plo : tau) * NN + n0;
+      float bt[NL];
 #pragma unroll
       for (int j = 0; j < NL; j += 4) {
-        const float4 cv = *reinterpret_cast<const float4*>(rc + j);
-        const float cq[4] = {cv.x, cv.y, cv.z, cv.w};
+        const float4 v = *reinterpret_cast<const float4*>(rb + j);
+        bt[j] = v.x; bt[j + 1] = v.y; bt[j + 2] = v.z; bt[j + 3] = v.w;
+      }
+      if constexpr (FINAL) {
+        const float* rc = rows + static_cast<size_t>(tp) * NN + (MULTI ? tau - plo : tau) * NN + n0;
+        float acc = 0.0f;
 #pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const float a = fast_exp2(ns * al2[j + jj]);
-          h[j + jj] = fmaf(a, h[j + jj], bt[j + jj] * xv);
-          acc = fmaf(cq[jj], h[j + jj], acc);
+        for (int j = 0; j < NL; j += 4) {
+          const float4 cv = *reinterpret_cast<const float4*>(rc + j);
+          const float cq[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) {
+            const float a = fast_exp2(ns * al2[j + jj]);
+            h[j + jj] = fmaf(a, h[j + jj], bt[j + jj] * xv);
+            acc = fmaf(cq[jj], h[j + jj], acc);
+          }
+        }
+        if (hag) {
+#pragma unroll
+          for (int j = 0; j < NL; j++) hag[(tau * NL + j) * 64] = h[j];
+        }
+        acc = group_sum<G, CH>(acc);
+        if (valid && grp == 0)
+          *reinterpret_cast<float*>(reinterpret_cast<char*>(y + (t0 + tau) * P) + ob4) = acc;
+      } else {
+#pragma unroll
+        for (int j = 0; j < NL; j++) {
+          const float a = fast_exp2(ns * al2[j]);
+          h[j] = fmaf(a, h[j], bt[j] * xv);
+        }
+        ss -= static_cast<double>(ns);
+      }
+    };
+    // the next part's rows, once every wavefront is done with this part's
+    // (parts are whole ring turns)
+    auto next_part = [&](int q8) {
+      if (MULTI && q8 > plo && q8 - plo == tp) {
+        __syncthreads();
+        plo = q8;
+        stage(plo, len - plo < tp ? len - plo : tp);
+        __syncthreads();
+      }
+    };
+    if (!FINAL && len % D == 0) {
+      // whole ring turns: no per-token bounds branches (the fetches past the
+      // chunk end re-read its last token), so the state stays in place rather
+      // than being copied back at every token.  (The final pass keeps the
+      // checked loop: its per-token branches remain for the y and sub-chunk
+      // state stores, and there the checked form addresses its loads better.)
+      for (int q8 = 0; q8 < len; q8 += D) {
+        next_part(q8);
+#pragma unroll
+        for (int r = 0; r < D; r++) {
+          const int tau = q8 + r;
+          const int ahead = (tau + D - 1 < len) ? tau + D - 1 : len - 1;
+          token(r, tau, true, t0 + ahead);
         }
       }
-      if (hag) {
-#pragma unroll
-        for (int j = 0; j < NL; j++) hag[(tau * NL + j) * 64] = h[j];
-      }
-      acc = group_sum<G, CH>(acc);
-      if (valid && grp == 0)
-        *reinterpret_cast<float*>(reinterpret_cast<char*>(y + (t0 + tau) * P) + ob4) = acc;
     } else {
+      for (int q8 = 0; q8 < len; q8 += D) {
+        next_part(q8);
 #pragma unroll
-      for (int j = 0; j < NL; j++) {
-        const float a = fast_exp2(ns * al2[j]);
-        h[j] = fmaf(a, h[j], bt[j] * xv);
-      }
-      ss -= static_cast<double>(ns);
-    }
-  };
-  if (!FINAL && len % D == 0) {
-    // whole ring turns: no per-token bounds branches (the fetches past the
-    // chunk end re-read its last token), so the state stays in place rather
-    // than being copied back at every token.  (The final pass keeps the
-    // checked loop: its per-token branches remain for the y and sub-chunk
-    // state stores, and there the checked form addresses its loads better.)
-    for (int q8 = 0; q8 < len; q8 += D) {
-#pragma unroll
-      for (int r = 0; r < D; r++) {
-        const int tau = q8 + r;
-        const int ahead = (tau + D - 1 < len) ? tau + D - 1 : len - 1;
-        token(r, tau, true, t0 + ahead);
-      }
-    }
-  } else {
-    for (int q8 = 0; q8 < len; q8 += D) {
-#pragma unroll
-      for (int r = 0; r < D; r++) {
-        const int tau = q8 + r;
-        if (tau < len) token(r, tau, tau + D - 1 < len, t0 + tau + D - 1);
+        for (int r = 0; r < D; r++) {
+          const int tau = q8 + r;
+          if (tau < len) token(r, tau, tau + D - 1 < len, t0 + tau + D - 1);
+        }
       }
     }
   }
@@ -328,16 +359,24 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   constexpr int NN = NL * G;
   const int64_t NB = (a.P + CH - 1) / CH;
   const int64_t K = (a.T + a.C - 1) / a.C;
-  // staged kernels: rows of a chunk (b, c) in LDS, 4 channel blocks per workgroup
-  const size_t rows_local = static_cast<size_t>(a.C) * NN * 4, rows_final = 2 * rows_local;
-  const bool staged = (NN % 4 == 0) && rows_final <= kFwdRowLds;
+  // staged kernels: rows of a chunk (b, c) in LDS, in parts of at most
+  // kFwdRowLds bytes, 4 channel blocks per workgroup
+  auto part_bytes = [&](int nq) {
+    const size_t tp = kFwdRowLds / (nq * NN * 4) / kFwdRing * kFwdRing;
+    return static_cast<size_t>(nq) * std::min<size_t>(a.C, tp) * NN * 4;
+  };
+  const size_t rows_local = part_bytes(1), rows_final = part_bytes(2);
+  const bool staged = NN % 4 == 0;
+  // rows staged in parts when a chunk's do not fit at once
+  const bool parts_local = static_cast<size_t>(a.C) * NN * 4 > kFwdRowLds;
+  const bool parts_final = static_cast<size_t>(2) * a.C * NN * 4 > kFwdRowLds;
   const dim3 grid(static_cast<unsigned>(K), static_cast<unsigned>(NB));
   const dim3 grid_s(static_cast<unsigned>(K), static_cast<unsigned>((NB + kFwdWpb - 1) / kFwdWpb));
   hipError_t e;
   if (staged) {
-    k_fwd_staged<IO, NL, G, false><<<grid_s, 64 * kFwdWpb, rows_local, st>>>(
-        a.T, a.P, a.N, a.C, NB, a.s, static_cast<const IO*>(a.x), a.b, a.c, a.alpha, a.h_ckpt, a.y, a.hloc, a.ssum,
-        nullptr, nullptr);
+    auto kl = parts_local ? k_fwd_staged<IO, NL, G, false, true> : k_fwd_staged<IO, NL, G, false, false>;
+    kl<<<grid_s, 64 * kFwdWpb, rows_local, st>>>(a.T, a.P, a.N, a.C, NB, a.s, static_cast<const IO*>(a.x), a.b, a.c,
+                                                 a.alpha, a.h_ckpt, a.y, a.hloc, a.ssum, nullptr, nullptr);
   } else {
     k_fwd_local<IO, NL, G><<<grid, 64, 0, st>>>(a.T, a.P, a.N, a.C, a.s, static_cast<const IO*>(a.x), a.b,
                                                 a.alpha, a.hloc, a.ssum);
@@ -350,9 +389,9 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.marks.rec(3, st);
   if (staged) {
-    k_fwd_staged<IO, NL, G, true><<<grid_s, 64 * kFwdWpb, rows_final, st>>>(
-        a.T, a.P, a.N, a.C, NB, a.s, static_cast<const IO*>(a.x), a.b, a.c, a.alpha, a.h_ckpt, a.y, a.hloc, a.ssum,
-        a.hsub, a.hall);
+    auto kf = parts_final ? k_fwd_staged<IO, NL, G, true, true> : k_fwd_staged<IO, NL, G, true, false>;
+    kf<<<grid_s, 64 * kFwdWpb, rows_final, st>>>(a.T, a.P, a.N, a.C, NB, a.s, static_cast<const IO*>(a.x), a.b, a.c,
+                                                 a.alpha, a.h_ckpt, a.y, a.hloc, a.ssum, a.hsub, a.hall);
   } else {
     k_fwd_final<IO, NL, G><<<grid, 64, 0, st>>>(a.T, a.P, a.N, a.C, a.s, static_cast<const IO*>(a.x), a.b, a.c,
                                                 a.alpha, a.h_ckpt, a.y, a.hsub, a.hall);

@@ -88,10 +88,11 @@ def algorithmic(name, T, P, N, C, W, s_io, kept=None, _prep=False):
     # a window of whole chunks is composed from exact chunk aggregates in the
     # carry pass, so the local pass then walks no window term
     compose = win and W % C == 0
-    # without states kept by the forward, exact local aggregates whose chunk
-    # rows (b and c) fit the 64 KB staging area are formed slab by slab in
-    # the rebuild walk (phase bwd_slab_prep), with the composition and carry
-    fused = kept is None and (not win or compose) and 2 * C * N * 4 <= 65536
+    # without states kept by the forward, exact local aggregates (N a
+    # multiple of 4: the rebuild stages the chunk rows, in parts if need be)
+    # are formed slab by slab in the rebuild walk (phase bwd_slab_prep), with
+    # the composition and carry
+    fused = kept is None and (not win or compose) and N % 4 == 0
     if name in ("bwd_local", "bwd_carry") and fused and not _prep:
         return (0, 0, 0)
     if name == "bwd_local":

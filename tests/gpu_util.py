@@ -20,6 +20,19 @@ def rel_err(got, ref):
     return num if den == 0.0 else num / den
 
 
+def p999_err(got, ref):
+    """99.9th percentile of the elementwise |got - ref| / (|ref| + 1e-3 max|ref|),
+    reported beside the per-tensor maximum (where elementwise relative errors
+    near zeros are undefined, the 1e-3 max|ref| floor keeps them finite)."""
+    got = np.asarray(got, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    if ref.size == 0:
+        return 0.0
+    floor = 1e-3 * float(np.max(np.abs(ref)))
+    e = np.abs(got - ref) / (np.abs(ref) + floor) if floor > 0 else np.abs(got - ref)
+    return float(np.percentile(e, 99.9))
+
+
 def say(msg):
     print(msg, flush=True)
 
@@ -75,7 +88,10 @@ def compare(got, ref, keys, tol, label=""):
     errs = {}
     for gk, rk in keys:
         errs[gk] = rel_err(got[gk], ref[rk])
-    say(f"[{label}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    p = {gk: p999_err(got[gk], ref[rk]) for gk, rk in keys}
+    worst = max(p, key=p.get) if p else None
+    say(f"[{label}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items())
+        + (f" | elementwise p99.9 worst {worst}={p[worst]:.2e}" if worst else ""))
     bad = {k: v for k, v in errs.items() if not (v <= tol)}
     assert not bad, f"{label}: over tolerance {tol}: {bad}"
     return errs

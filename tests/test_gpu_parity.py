@@ -60,13 +60,16 @@ def test_chunk_invariance_ragged(orc, chunk):
     _run_case(orc, inp, 300, chunk, f"ragged C={chunk}")
 
 
-@pytest.mark.parametrize("N,chunk", [(64, 256), (32, 512)])
+@pytest.mark.parametrize("N,chunk", [(64, 256), (32, 512), (64, 100)])
 def test_rebuild_rows_in_parts(orc, N, chunk):
-    """Chunks whose b and c rows exceed the rebuild's 64 KB staging area are
-    staged in parts (128 tokens at N = 64, 256 at N = 32): chunk checkpoints
-    only, a window of whole chunks and exact, with a ragged last chunk (T =
-    700) and channel blocks that do not fill the last workgroup."""
-    inp = make_layer(small_case(700 if chunk == 256 else 1100, 40, N, 30 + N))
+    """Chunks whose b and c rows exceed the staging areas are staged in parts
+    (the rebuild: 128 tokens at N = 64, 256 at N = 32; the forward: 64 or 128
+    tokens at N = 64, 128 or 256 at N = 32): chunk checkpoints only, a window
+    of whole chunks and exact, with a ragged last chunk and channel blocks
+    that do not fill the last workgroup.  C = 100 at N = 64 stages the
+    forward in a part of 64 tokens and one of 36 (chunks that are not whole
+    ring turns)."""
+    inp = make_layer(small_case(1100 if chunk == 512 else 700, 40, N, 30 + N))
     T = inp["x"].shape[0]
     _run_case(orc, inp, chunk, chunk, f"rows in parts N={N} C={chunk} W={chunk}")
     _run_case(orc, inp, T, chunk, f"rows in parts N={N} C={chunk} exact")

@@ -33,9 +33,11 @@ struct Tok {
 
 // Tokens at the end of a sub-chunk whose decay factors the recompute keeps
 // for the reverse walk, which starts with them (their exps are not repeated).
-// Four fit in 254 VGPRs at two waves per SIMD without spilling (five spill);
-// measured at the 1M-token layer: 30.4 -> 29.3 ms for this kernel.
-constexpr int kKeepA = 4;
+// Six fit in 250 VGPRs at two waves per SIMD without spilling (seven spill),
+// with each token's b and c rows read from LDS at the token rather than one
+// token ahead (which held 24 more registers).  Measured at the 1M-token
+// layer: none kept 30.4 ms, four (rows read ahead) 29.3, six 28.9.
+constexpr int kKeepA = 6;
 
 // Vector-memory operations the reverse walk issues per token (rev_token's
 // dDelta and dx_dir stores).
@@ -581,8 +583,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         sig[S / 2 + q] = __uint_as_float(r[1]);  // lanes 0..31: group 1's (token S/2 + q)
       }
     }
-    // reverse walk; a token's per-lane values and its b, c (and partner c)
-    // rows are read from LDS one token ahead
+    // reverse walk; a token's per-lane values are read from LDS one token
+    // ahead, its b, c (and partner c) rows at the token
     struct Rows {
       float b[NL], c[NL], m[NL];
     };
@@ -596,8 +598,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
       }
     };
     Tok cur = read_tok(S - 1);
-    Rows rcur;
-    read_rows(S - 1, rcur);
     // rows of the token being walked (dDelta in dY, dx_dir), stepped down by
     // one row per token; tokens tau < npart have their window partner inside
     // the sequence
@@ -609,11 +609,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
     for (int tau = S - 1; tau >= 0; tau--) {
       token_fence();
       Tok nxt = cur;
-      Rows rnxt = rcur;
-      if (tau > 0) {
-        nxt = read_tok(tau - 1);
-        read_rows(tau - 1, rnxt);
-      }
+      if (tau > 0) nxt = read_tok(tau - 1);
+      Rows rcur;
+      read_rows(tau, rcur);
       float bt[NL], ct[NL], cm[NL];
 #pragma unroll
       for (int j = 0; j < NL; j++) {
@@ -632,7 +630,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
       yrow -= ldy_b;
       xrow -= ldx_b;
       cur = nxt;
-      rcur = rnxt;
     }
     // Wait for the prefetch of sub-chunk u - 1 (and the start states): the
     // vector memory counter retires in issue order, and the only operations

@@ -33,11 +33,12 @@ struct Tok {
 
 // Tokens at the end of a sub-chunk whose decay factors the recompute keeps
 // for the reverse walk, which starts with them (their exps are not repeated).
-// Six fit in 250 VGPRs at two waves per SIMD without spilling (seven spill),
-// with each token's b and c rows read from LDS at the token rather than one
-// token ahead (which held 24 more registers).  Measured at the 1M-token
-// layer: none kept 30.4 ms, four (rows read ahead) 29.3, six 28.9.
-constexpr int kKeepA = 6;
+// Seven fit in the 256 VGPRs of two waves per SIMD without spilling (eight
+// spill), with each token's LDS values (b and c rows, per-lane values) read
+// at the token rather than one token ahead, which held 29 more registers.
+// Measured at the 1M-token layer: none kept 30.4 ms, four (values read ahead)
+// 29.3, six 28.9, seven 28.8.
+constexpr int kKeepA = 7;
 
 // Vector-memory operations the reverse walk issues per token (rev_token's
 // dDelta and dx_dir stores).
@@ -583,8 +584,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         sig[S / 2 + q] = __uint_as_float(r[1]);  // lanes 0..31: group 1's (token S/2 + q)
       }
     }
-    // reverse walk; a token's per-lane values are read from LDS one token
-    // ahead, its b, c (and partner c) rows at the token
+    // reverse walk; a token's per-lane values and its b, c (and partner c)
+    // rows are read from LDS at the token
     struct Rows {
       float b[NL], c[NL], m[NL];
     };
@@ -597,7 +598,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         for (int j = 0; j < NL; j++) r.m[j] = 0.0f;
       }
     };
-    Tok cur = read_tok(S - 1);
     // rows of the token being walked (dDelta in dY, dx_dir), stepped down by
     // one row per token; tokens tau < npart have their window partner inside
     // the sequence
@@ -608,8 +608,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
 #pragma unroll
     for (int tau = S - 1; tau >= 0; tau--) {
       token_fence();
-      Tok nxt = cur;
-      if (tau > 0) nxt = read_tok(tau - 1);
+      const Tok cur = read_tok(tau);
       Rows rcur;
       read_rows(tau, rcur);
       float bt[NL], ct[NL], cm[NL];
@@ -629,7 +628,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
                                                            : nullptr);
       yrow -= ldy_b;
       xrow -= ldx_b;
-      cur = nxt;
     }
     // Wait for the prefetch of sub-chunk u - 1 (and the start states): the
     // vector memory counter retires in issue order, and the only operations

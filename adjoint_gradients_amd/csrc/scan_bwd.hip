@@ -424,22 +424,6 @@ __global__ __launch_bounds__(256) void k_bwd_hsub(BwdArgs a, int64_t NB) {
   }
 }
 
-// Workgroup id -> (chunk within the launch, channel group) for a 1-D launch
-// over nk chunks x ng channel groups.  Consecutive workgroup ids go round-robin
-// over the 8 XCDs; when nk is a multiple of 8, chunk c's groups all run on XCD
-// c % 8, one after another, so the chunk's b and c rows reach that XCD's L2
-// once.  (Otherwise chunk-major order.)
-__device__ __forceinline__ void chunk_and_group(uint32_t id, uint32_t nk, uint32_t ng, uint32_t* c, uint32_t* g) {
-  if (nk % 8 == 0) {
-    const uint32_t loc = id / 8;
-    *c = id % 8 + 8 * (loc / ng);
-    *g = loc % ng;
-  } else {
-    *c = id / ng;
-    *g = id % ng;
-  }
-}
-
 // The chunk-local reverse aggregate and the sub-chunk start states in one
 // forward walk over the chunk (exact aggregates: no window term inside the
 // walk), for slabs processed right to left.  The aggregate of chunk k with a
@@ -468,10 +452,9 @@ __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
   const int grp = lane / CH, pl = lane % CH;
   const int64_t T = a.T, P = a.P;
   const int C = a.C;
-  // 1-D launch over the slab's chunks x the channel groups
-  const uint32_t ng = static_cast<uint32_t>((NB + kWpb - 1) / kWpb);
+  // one workgroup per (chunk of the slab, channel group): chunk_group_grid
   uint32_t kc, kg;
-  chunk_and_group(blockIdx.x, gridDim.x / ng, ng, &kc, &kg);
+  chunk_and_group(&kc, &kg);
   const int64_t k = a.k_lo + kc;  // chunk (the launch covers one slab)
   const int64_t cb = static_cast<int64_t>(kg) * kWpb + w;
   const bool wave_live = cb < NB;
@@ -901,8 +884,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     am.hsub_ready = given ? 1 : 0;
     const dim3 grid(static_cast<unsigned>(nk), static_cast<unsigned>(pl.NBW));
     if (fused) {
-      // one workgroup per (chunk, channel group), in the order of chunk_and_group
-      fk<<<static_cast<unsigned>(nk * pl.NBW), 64 * kWpb, rows_f, st>>>(am, NB);
+      fk<<<chunk_group_grid(nk, pl.NBW), 64 * kWpb, rows_f, st>>>(am, NB);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if ((e = carry_range(k_lo, k_lo + nk)) != hipSuccess) return e;
       am.hsub_ready = 1;

@@ -211,8 +211,11 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int grp = lane / CH, pl = lane % CH;
-  const int64_t k = blockIdx.x;
-  const int64_t cb = static_cast<int64_t>(blockIdx.y) * kFwdWpb + w;
+  // one workgroup per (chunk, channel group): chunk_group_grid
+  uint32_t kc, kg;
+  chunk_and_group(&kc, &kg);
+  const int64_t k = kc;
+  const int64_t cb = static_cast<int64_t>(kg) * kFwdWpb + w;
   const int64_t p = cb * CH + pl;
   const bool valid = cb < NB && p < P;
   const int64_t pc = p < P ? p : P - 1;
@@ -371,7 +374,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const bool parts_local = static_cast<size_t>(a.C) * NN * 4 > kFwdRowLds;
   const bool parts_final = static_cast<size_t>(2) * a.C * NN * 4 > kFwdRowLds;
   const dim3 grid(static_cast<unsigned>(K), static_cast<unsigned>(NB));
-  const dim3 grid_s(static_cast<unsigned>(K), static_cast<unsigned>((NB + kFwdWpb - 1) / kFwdWpb));
+  const dim3 grid_s = chunk_group_grid(K, (NB + kFwdWpb - 1) / kFwdWpb);
   hipError_t e;
   if (staged) {
     auto kl = parts_local ? k_fwd_staged<IO, NL, G, false, true> : k_fwd_staged<IO, NL, G, false, false>;

@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "grid_order.hpp"
+
 namespace ssm {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -199,6 +201,17 @@ __device__ __forceinline__ float seg_affine_scan(int64_t k_lo, int64_t k_hi, flo
     __syncthreads();  // the next group overwrites the maps
   }
   return cin;
+}
+
+// Launch grid and workgroup -> (chunk, channel group) of the chunked scans
+// (order in grid_order.hpp).
+inline dim3 chunk_group_grid(int64_t nk, int64_t ng) {
+  uint32_t gx = 0, gy = 0;
+  chunk_group_dims(nk, ng, &gx, &gy);
+  return dim3(gx, gy);
+}
+__device__ __forceinline__ void chunk_and_group(uint32_t* c, uint32_t* g) {
+  chunk_group_of(blockIdx.x, blockIdx.y, gridDim.x, c, g);
 }
 
 }  // namespace ssm

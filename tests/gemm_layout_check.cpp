@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "gemm_dl_index.hpp"
+#include "grid_order.hpp"
 
 using namespace gdl;
 
@@ -97,6 +98,47 @@ int main() {
             CHECK(ko_read_off(l, rb + 32 * i, q, h) == ko_read_off(l, rb + 32 * i, 0, 0) + 8192 * q + 2048 * h,
                   "ko linear l %d rb %d i %d q %d h %d", l, rb, i, q, h);
         }
+  // workgroup order of the chunked scans: a bijection of the grid onto
+  // (chunk, group); with nk a multiple of 8 the ids that the 8 XCDs take
+  // round-robin (x fastest) put all of a chunk's groups on XCD chunk % 8,
+  // consecutively; each grid dimension's work items fit 32 bits at the
+  // largest sizes (2^31 tokens in chunks of 1, 2^20 channels)
+  for (int64_t nk = 1; nk <= 70; nk++)
+    for (int64_t ng = 1; ng <= 20; ng++) {
+      uint32_t gx = 0, gy = 0;
+      ssm::chunk_group_dims(nk, ng, &gx, &gy);
+      CHECK((int64_t)gx * gy == nk * ng, "order nk %ld ng %ld: grid %u x %u", (long)nk, (long)ng, gx, gy);
+      std::vector<int> seen(nk * ng, 0);
+      std::vector<int> last_loc(nk, -1);
+      for (uint32_t by = 0; by < gy; by++)
+        for (uint32_t bx = 0; bx < gx; bx++) {
+          uint32_t c = 0, g = 0;
+          ssm::chunk_group_of(bx, by, gx, &c, &g);
+          CHECK(c < nk && g < ng, "order nk %ld ng %ld: (%u, %u) -> (%u, %u)", (long)nk, (long)ng, bx, by, c, g);
+          if (c >= nk || g >= ng) continue;
+          seen[c * ng + g]++;
+          if (nk % 8 == 0) {
+            const int64_t id = (int64_t)by * gx + bx;
+            CHECK(id % 8 == c % 8, "order nk %ld ng %ld: chunk %u on XCD %ld", (long)nk, (long)ng, c, (long)(id % 8));
+            const int loc = (int)(id / 8);
+            CHECK(last_loc[c] < 0 || loc == last_loc[c] + 1, "order nk %ld ng %ld: chunk %u not consecutive", (long)nk,
+                  (long)ng, c);
+            last_loc[c] = loc;
+          }
+        }
+      for (int64_t v = 0; v < nk * ng; v++)
+        CHECK(seen[v] == 1, "order nk %ld ng %ld: pair %ld taken %d times", (long)nk, (long)ng, (long)v, seen[v]);
+    }
+  {
+    const int64_t T = int64_t(1) << 31, P = int64_t(1) << 20;
+    for (int64_t C : {1, 2, 7, 8, 256}) {
+      const int64_t nk = (T + C - 1) / C, ng = (P / 32 + 3) / 4;  // 4 wavefronts of >= 32 channels
+      uint32_t gx = 0, gy = 0;
+      ssm::chunk_group_dims(nk, ng, &gx, &gy);
+      CHECK((int64_t)gx * 256 < (int64_t(1) << 32) || nk % 8 != 0, "order: x work items overflow at C %ld", (long)C);
+      CHECK((int64_t)gy * 1 < (int64_t(1) << 32), "order: y overflow at C %ld", (long)C);
+    }
+  }
   printf(fails ? "FAILED (%d)\n" : "layout OK\n", fails);
   return fails ? 1 : 0;
 }

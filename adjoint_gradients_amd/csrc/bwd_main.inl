@@ -148,7 +148,7 @@ struct RevState {
 template <typename IO, int NL, int G, bool WIN>
 __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, const Tok& tk, const float (&bt)[NL],
                                           const float (&ct)[NL], const float (&cm)[NL], const float (&hp)[NL],
-                                          const float (&hc)[NL], float sg, char* yrow, char* xrow, bool live, bool part,
+                                          const float (&hc)[NL], float sg, char* yrow, char* xrow, bool live,
                                           bool valid, int grp, int pl, int lane, float* red, int rd_off,
                                           int voff_dy, int voff_dx, float* xw_tau, const float* a_in) {
   constexpr int CH = 64 / G;
@@ -163,18 +163,19 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
   if constexpr (WIN) {
     // drop the token leaving the window: - g_{i+W} c_{i+W} prod_{j=i+1}^{i+W} a_j.
     // Where the partner token i + W lies past the sequence end there is no
-    // such term: its g and s are taken as zero (a select, not a branch, so
-    // the token's code stays one block).
-    const float gm = part ? tk.gm : 0.0f;
-    const float sm = part ? tk.sm : 0.0f;
+    // such term: its g and s arrive as zeros.
+    const float gm = tk.gm;
+    const float sm = tk.sm;
     const float E = static_cast<float>(st.E64);
 #pragma unroll
     for (int j = 0; j < NL; j++) {
       const float D = fast_exp2(-E * st.al2[j]);
       mu[j] = fmaf(-gm * cm[j], D, mu[j]);
     }
-    // token i + W leaves the window of token i - 1, token i enters it
-    st.E64 += static_cast<double>(tk.s) - static_cast<double>(sm);
+    // token i + W leaves the window of token i - 1, token i enters it (the
+    // difference rounded to fp32 adds at most 2^-24 of it per token, far
+    // below the fp32 rounding of E itself)
+    st.E64 += static_cast<double>(tk.s - sm);
   }
   float ds = 0.0f, dxd = 0.0f;
 #pragma unroll
@@ -350,8 +351,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   // tokens grp, grp + G, ... of channel pc, so each instruction covers G token
   // rows.  x arrives raw (bf16 zero-extended to 4 bytes, or the float).  Only
   // this wavefront reads the area.  Partner values of tokens whose partner
-  // lies past the sequence end are whatever the clamped row holds; the walk
-  // does not use them.
+  // lies past the sequence end are zeros (written here), so the walk drops no
+  // window term for them.
   constexpr int NQS = WIN ? 5 : 3;
   constexpr int SPL = S / G;       // tokens fetched per lane
   constexpr int SQ = S * CH + 32;  // floats per quantity block
@@ -388,9 +389,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
           dma_v(a.g + t * P + pc, d + 8u * SQ);
           if constexpr (WIN) {
             const int64_t m = t + a.W;
-            const int64_t mm = m < T ? m : t;
-            dma_v(a.s + mm * P + pc, d + 12u * SQ);
-            dma_v(a.g + mm * P + pc, d + 16u * SQ);
+            if (m < T) {
+              dma_v(a.s + m * P + pc, d + 12u * SQ);
+              dma_v(a.g + m * P + pc, d + 16u * SQ);
+            } else {
+              // partner past the sequence end: no window term (zeros)
+              float* z = sc0 + (u & 1) * (NQS * SQ) + G * i * CH + lane;
+              z[3 * SQ] = 0.0f;
+              z[4 * SQ] = 0.0f;
+            }
           }
         } else {
           // past the chunk end: zeros (the walk then passes the token by)
@@ -599,12 +606,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
       }
     };
     // rows of the token being walked (dDelta in dY, dx_dir), stepped down by
-    // one row per token; tokens tau < npart have their window partner inside
-    // the sequence
+    // one row per token
     char* yrow = reinterpret_cast<char*>(static_cast<IO*>(a.dY) + (ta + S - 1) * a.ldy);
     char* xrow = reinterpret_cast<char*>(dxb + (ta + S - 1) * P);
-    const int64_t np64 = T - a.W - ta;
-    const int npart = np64 < 0 ? 0 : np64 > S ? S : static_cast<int>(np64);
 #pragma unroll
     for (int tau = S - 1; tau >= 0; tau--) {
       token_fence();
@@ -622,7 +626,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
 #pragma unroll
       for (int j = 0; j < NL; j++) hp[j] = (tau > 0) ? hr[tau > 0 ? tau - 1 : 0][j] : hs[j];
       const float sg = (G == 2) ? sig[tau] : one_minus_exp_neg(cur.s);
-      rev_token<IO, NL, G, WIN>(st, a, cur, bt, ct, cm, hp, hr[tau], sg, yrow, xrow, tau < len, tau < npart, valid, grp,
+      rev_token<IO, NL, G, WIN>(st, a, cur, bt, ct, cm, hp, hr[tau], sg, yrow, xrow, tau < len, valid, grp,
                                 pl, lane, red, rd_off, voff_dy, voff_dx, xw + (w * S + tau) * OUT,
                                 (!ST && tau >= S - kKeepA) ? alast[tau >= S - kKeepA ? tau - (S - kKeepA) : 0]
                                                            : nullptr);

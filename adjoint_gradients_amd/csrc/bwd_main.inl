@@ -149,7 +149,7 @@ template <typename IO, int NL, int G, bool WIN>
 __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, const Tok& tk, const float (&bt)[NL],
                                           const float (&ct)[NL], const float (&cm)[NL], const float (&hp)[NL],
                                           const float (&hc)[NL], float sg, char* yrow, char* xrow, bool live,
-                                          bool valid, int grp, int pl, int lane, float* red, int rd_off,
+                                          int grp, int pl, int lane, float* red, int rd_off,
                                           int voff_dy, int voff_dx, float* xw_tau, const float* a_in) {
   constexpr int CH = 64 / G;
   constexpr int NN = NL * G;
@@ -217,11 +217,11 @@ __device__ __forceinline__ void rev_token(RevState<NL>& st, const BwdArgs& a, co
   }
   st.dbias += dD;
   // channel sums of db = mu x and dc = g h through an LDS transpose (placement
-  // in red_layout.hpp).  Lanes past the last channel contribute zeros; their x
-  // and g are zeroed once per token rather than per product.
+  // in red_layout.hpp).  Lanes past the last channel contribute zeros: their
+  // x and g arrive as zeros.
   using RL = redl::Layout<NL, G>;
-  const float xz = valid ? tk.x : 0.0f;
-  const float gz = valid ? tk.g : 0.0f;
+  const float xz = tk.x;
+  const float gz = tk.g;
   float* wr = red + RL::lane_base(grp, pl);
 #pragma unroll
   for (int j = 0; j < NL; j++) {
@@ -350,7 +350,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
   // instruction (32 lanes per pass) hit disjoint banks.  Lane (grp, pl) brings
   // tokens grp, grp + G, ... of channel pc, so each instruction covers G token
   // rows.  x arrives raw (bf16 zero-extended to 4 bytes, or the float).  Only
-  // this wavefront reads the area.  Partner values of tokens whose partner
+  // this wavefront reads the area.  Lanes past the last channel keep zeros
+  // there (see below).  Partner values of tokens whose partner
   // lies past the sequence end are zeros (written here), so the walk drops no
   // window term for them.
   constexpr int NQS = WIN ? 5 : 3;
@@ -366,16 +367,18 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
     const uint32_t dst = lds_addr(sc0 + (u & 1) * (NQS * SQ));
     if (ta + S <= t1 && (!WIN || ta + S - 1 + a.W < T)) {
       // every token inside the chunk and every partner inside the sequence
+      if (valid) {
 #pragma unroll
-      for (int i = 0; i < SPL; i++) {
-        const int64_t tb = ta + G * i;  // the lane's token is tb + grp
-        const uint32_t d = dst + 4u * (G * i * CH);
-        dma_s(a.s + tb * P, voff4, d);
-        dma_s(xp + tb * P, voffx, d + 4u * SQ);
-        dma_s(a.g + tb * P, voff4, d + 8u * SQ);
-        if constexpr (WIN) {
-          dma_s(a.s + (tb + a.W) * P, voff4, d + 12u * SQ);
-          dma_s(a.g + (tb + a.W) * P, voff4, d + 16u * SQ);
+        for (int i = 0; i < SPL; i++) {
+          const int64_t tb = ta + G * i;  // the lane's token is tb + grp
+          const uint32_t d = dst + 4u * (G * i * CH);
+          dma_s(a.s + tb * P, voff4, d);
+          dma_s(xp + tb * P, voffx, d + 4u * SQ);
+          dma_s(a.g + tb * P, voff4, d + 8u * SQ);
+          if constexpr (WIN) {
+            dma_s(a.s + (tb + a.W) * P, voff4, d + 12u * SQ);
+            dma_s(a.g + (tb + a.W) * P, voff4, d + 16u * SQ);
+          }
         }
       }
     } else {
@@ -384,6 +387,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
         const int64_t t = ta + G * i + grp;
         const uint32_t d = dst + 4u * (G * i * CH);
         if (t < t1) {
+          if (!valid) continue;  // the lane's slots hold zeros
           dma_v(a.s + t * P + pc, d);
           dma_v(xp + t * P + pc, d + 4u * SQ);
           dma_v(a.g + t * P + pc, d + 8u * SQ);
@@ -408,6 +412,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
       }
     }
   };
+  // Lanes past the last channel take no part in the channel sums: their
+  // slots of the area hold zeros, written here and never refilled (their DMA
+  // is masked off).
+  if (!valid) {
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int q = 0; q < NQS; q++)
+#pragma unroll
+        for (int i = 0; i < SPL; i++) sc0[b * (NQS * SQ) + q * SQ + G * i * CH + lane] = 0.0f;
+  }
   const float* sc = sc0;  // area of the current sub-chunk
   auto scal = [&](int q, int tau) { return sc[q * SQ + tau * CH + pl]; };
   auto scal_x = [&](int tau) {
@@ -626,7 +641,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(BwdArgs a, int64_t NB, int6
 #pragma unroll
       for (int j = 0; j < NL; j++) hp[j] = (tau > 0) ? hr[tau > 0 ? tau - 1 : 0][j] : hs[j];
       const float sg = (G == 2) ? sig[tau] : one_minus_exp_neg(cur.s);
-      rev_token<IO, NL, G, WIN>(st, a, cur, bt, ct, cm, hp, hr[tau], sg, yrow, xrow, tau < len, valid, grp,
+      rev_token<IO, NL, G, WIN>(st, a, cur, bt, ct, cm, hp, hr[tau], sg, yrow, xrow, tau < len, grp,
                                 pl, lane, red, rd_off, voff_dy, voff_dx, xw + (w * S + tau) * OUT,
                                 (!ST && tau >= S - kKeepA) ? alast[tau >= S - kKeepA ? tau - (S - kKeepA) : 0]
                                                            : nullptr);

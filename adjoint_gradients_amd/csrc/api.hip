@@ -292,16 +292,17 @@ hipError_t run_forward(const ssm_dims* d, const ssm_layer* L, const void* x, flo
   return ssm::launch_forward_scan(fa, bf, st);
 }
 
-// Gradient of one layer.  If delta_io is set (stack), dx is folded into it:
-// delta_io <- delta_io + dx; otherwise dx goes to grads->dx when requested.
+// Gradient of one layer.  If delta_out is set (stack), dx is folded into the
+// cotangent stream: delta_out <- delta_in + dx (delta_out may be delta_in);
+// otherwise dx goes to grads->dx when requested.
 hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, const ssm_saved* sv,
-                        const float* g, int64_t W, const ssm_grads* gr, float* delta_io, const BwdWs& w,
-                        hipStream_t st, ssm::Marks mk = {}) {
+                        const float* g, int64_t W, const ssm_grads* gr, const float* delta_in, float* delta_out,
+                        const BwdWs& w, hipStream_t st, ssm::Marks mk = {}) {
   mk.rec(0, st);
   const bool bf = d->io == SSM_BF16;
   const int64_t T = d->T, P = d->P, N = d->N;
   const int64_t M = P + 2 * N;
-  const bool need_dx = (delta_io != nullptr) || (gr->dx != nullptr);
+  const bool need_dx = (delta_out != nullptr) || (gr->dx != nullptr);
   BwdArgs a{};
   a.T = T; a.P = P; a.N = N; a.W = W; a.C = d->chunk;
   a.s = sv->s; a.x = x; a.b = sv->b; a.c = sv->c; a.alpha = L->alpha; a.h_ckpt = sv->h_ckpt;
@@ -316,7 +317,7 @@ hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, co
   // the direct input cotangent: the stack's own buffer (its cotangent stream
   // is g here, read while dx_dir is written), else the dx output itself,
   // which the input-cotangent GEMM then completes in place
-  float* dxdir = delta_io ? w.dxdir : gr->dx;
+  float* dxdir = delta_out ? w.dxdir : gr->dx;
   a.dxdir = need_dx ? dxdir : nullptr;
   a.dalpha = gr->dalpha; a.dbias = gr->dbias;
   a.marks = mk;
@@ -334,7 +335,7 @@ hipError_t run_backward(const ssm_dims* d, const ssm_layer* L, const void* x, co
     if (e != hipSuccess) return e;
     // dx = dY W_cat + dxdir  (+ delta for the stack, in place)
     ssm::GemmOperands opx{T, P, M, w.dY, M, true, w.wcat, P, false};
-    ssm::EpiAddArgs ea{dxdir, delta_io, delta_io ? delta_io : gr->dx};
+    ssm::EpiAddArgs ea{dxdir, delta_out ? delta_in : nullptr, delta_out ? delta_out : gr->dx};
     e = ssm::gemm_add(opx, bf, ea, st);
   }
   mk.rec(6, st);
@@ -480,7 +481,7 @@ static ssm_status adjoint_impl(const ssm_dims* d, const ssm_layer* L, const void
   if ((s = check_ws(ws, ws_bytes, bwd_ws_bytes(d, W, need_dx, own_hsub, false, slab_chunks))) != SSM_OK) return s;
   Carver cv(ws);
   BwdWs w = carve_bwd(cv, d, W, need_dx, own_hsub, false, slab_chunks);
-  hipError_t e = run_backward(d, L, x, sv, g, W, gr, nullptr, w, static_cast<hipStream_t>(stream), mk);
+  hipError_t e = run_backward(d, L, x, sv, g, W, gr, nullptr, nullptr, w, static_cast<hipStream_t>(stream), mk);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -602,14 +603,17 @@ ssm_status ssm_stack_grad(int32_t K, const ssm_dims* d, const ssm_layer* layers,
     // r^{k+1} = r^k + y^k, then x^{k+1} (fused into the update when it is a plain cast)
     const bool plain_next = k + 1 < K && !layers[k + 1].norm_scale;
     void* xnext = plain_next ? xs + static_cast<size_t>(k + 1) * xbytes : nullptr;
-    if ((e = ssm::residual_update(TP, r, y, xnext, bf, st)) != hipSuccess) return SSM_ERR_HIP;
+    // the last layer's sum is the output x_K itself (r is not read afterwards)
+    float* rout = (k + 1 == K && xK) ? xK : nullptr;
+    if ((e = ssm::residual_update(TP, r, y, xnext, bf, st, rout)) != hipSuccess) return SSM_ERR_HIP;
     if (k + 1 < K && !plain_next && (e = make_input(k + 1)) != hipSuccess) return SSM_ERR_HIP;
   }
-  if (xK) {
-    if ((e = hipMemcpyAsync(xK, r, static_cast<size_t>(TP) * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess)
-      return SSM_ERR_HIP;
-  }
-  if ((e = hipMemcpyAsync(delta, g, static_cast<size_t>(TP) * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess)
+  // The cotangent stream delta starts as g.  A plain top layer reads g itself
+  // and writes g + dx^{K-1} into delta; a normalised one updates delta in
+  // place, so delta is first a copy of g.
+  const bool top_plain = !layers[K - 1].norm_scale;
+  if (!top_plain &&
+      (e = hipMemcpyAsync(delta, g, static_cast<size_t>(TP) * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess)
     return SSM_ERR_HIP;
   for (int32_t k = K - 1; k >= 0; k--) {
     void* xk = xs + static_cast<size_t>(k) * xbytes;
@@ -620,18 +624,22 @@ ssm_status ssm_stack_grad(int32_t K, const ssm_dims* d, const ssm_layer* layers,
     if (layers[k].norm_scale) {
       ssm_grads gl = grads[k];
       gl.dx = nw.dx;
-      if ((e = run_backward(d, &layers[k], xk, &sv[k], delta, W, &gl, nullptr, bw, st)) != hipSuccess)
+      if ((e = run_backward(d, &layers[k], xk, &sv[k], delta, W, &gl, nullptr, nullptr, bw, st)) != hipSuccess)
         return SSM_ERR_HIP;
       if ((e = ssm::rmsnorm_vjp(T, P, nw.rk + static_cast<size_t>(nslot[k]) * TP, nw.rinv + nslot[k] * T,
                                 layers[k].norm_scale,
                                 nw.dx, nw.m, delta, nw.part, grads[k].dnorm_scale, st)) != hipSuccess)
         return SSM_ERR_HIP;
     } else {
-      if ((e = run_backward(d, &layers[k], xk, &sv[k], delta, W, &grads[k], delta, bw, st)) != hipSuccess)
+      // cotangent of this layer: g for a plain top layer, else delta; the
+      // bottom layer's sum goes straight to dx0
+      const float* cot = (k == K - 1) ? g : delta;
+      float* out = (k == 0 && dx0) ? dx0 : delta;
+      if ((e = run_backward(d, &layers[k], xk, &sv[k], cot, W, &grads[k], cot, out, bw, st)) != hipSuccess)
         return SSM_ERR_HIP;
     }
   }
-  if (dx0) {
+  if (dx0 && layers[0].norm_scale) {
     if ((e = hipMemcpyAsync(dx0, delta, static_cast<size_t>(TP) * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess)
       return SSM_ERR_HIP;
   }

@@ -298,14 +298,14 @@ __global__ __launch_bounds__(256) void k_reduce_wgrad(const float* __restrict__ 
   else dWc[(row - P - N) * P + col] = v;
 }
 
-__global__ __launch_bounds__(256) void k_residual_update(int64_t n, float* __restrict__ r, const float* __restrict__ y,
-                                                         void* __restrict__ xio, int bf16) {
+__global__ __launch_bounds__(256) void k_residual_update(int64_t n, float* r, const float* __restrict__ y,
+                                                         void* __restrict__ xio, int bf16, float* rout) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= n) return;
   float v = r[e];
   if (y) {
     v += y[e];
-    r[e] = v;
+    rout[e] = v;
   }
   if (!xio) return;
   if (bf16) static_cast<bf16_t*>(xio)[e] = f32_to_bf16(v);
@@ -358,8 +358,9 @@ hipError_t reduce_weight_grads(const float* part, int splits, int64_t P, int64_t
   return hipGetLastError();
 }
 
-hipError_t residual_update(int64_t n, float* r, const float* y, void* xio, bool bf16, hipStream_t st) {
-  k_residual_update<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(n, r, y, xio, bf16 ? 1 : 0);
+hipError_t residual_update(int64_t n, float* r, const float* y, void* xio, bool bf16, hipStream_t st, float* rout) {
+  k_residual_update<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(n, r, y, xio, bf16 ? 1 : 0,
+                                                                             rout ? rout : r);
   return hipGetLastError();
 }
 

@@ -158,8 +158,9 @@ hipError_t reduce_weight_grads(const float* part, int splits, int64_t P, int64_t
                                float* dWc, hipStream_t st);
 
 // ---------------------------------------------------------------- stack helpers
-// r += y (if y) ; xio = io(r)
-hipError_t residual_update(int64_t n, float* r, const float* y, void* xio, bool bf16, hipStream_t st);
+// r += y (if y; the sum goes to rout instead of r when rout is set) ; xio = io(r + y)
+hipError_t residual_update(int64_t n, float* r, const float* y, void* xio, bool bf16, hipStream_t st,
+                           float* rout = nullptr);
 // r = io value of x0 (float32 residual stream initialised from the io input)
 hipError_t residual_init(int64_t n, const void* x0, bool bf16, float* r, hipStream_t st);
 

@@ -221,7 +221,8 @@ def test_poisoned_buffers(orc, T, P, N, io, window, chunk, mode):
 
 
 @pytest.mark.parametrize("io,window,mask", [("f32", 256, (1, 1, 1)), ("f32", 50, (1, 0, 1)),
-                                            ("bf16", 256, (1, 1, 1)), ("bf16", 50, (0, 1, 1))])
+                                            ("bf16", 256, (1, 1, 1)), ("bf16", 50, (0, 1, 1)),
+                                            ("f32", 50, (1, 1, 0))])
 def test_stack_normalised(orc, io, window, mask):
     # layers reading the RMS-normalised residual stream (mask: which layers
     # normalise); every gradient, dgamma, dx0 and r^K against the oracle

@@ -12,8 +12,8 @@
 //            local VJPs (equations in scan_bwd.hip).  A sub-chunk compiles to
 //            one basic block: a partial one runs the same code on tokens
 //            staged as zeros, stores go through buffer resources whose
-//            out-of-range lanes are dropped, and the window partner's terms
-//            are taken by select.
+//            out-of-range lanes are dropped, and window partners past the
+//            sequence end (and lanes past the last channel) read zeros.
 // Latency hiding: everything a sub-chunk reads from memory is brought by LDS
 // DMA during the previous sub-chunk (issued at its start, waited for at its
 // end, where the wait lets the walk's own stores stay in flight) -- the

@@ -191,7 +191,7 @@ __device__ __forceinline__ void stage_rows(float* rows, const float* __restrict_
 // The staged forward walk.  PARTS: the chunk's rows are staged in parts (the
 // launcher picks this instantiation when a chunk's rows exceed the staging
 // area); otherwise the whole chunk is staged at once.
-template <typename IO, int NL, int G, bool FINAL, bool PARTS>
+template <typename IO, int NL, int G, bool FINAL, bool PARTS, bool KEEP = false>
 __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_t N, int C, int64_t NB,
                                                     const float* __restrict__ sp, const IO* __restrict__ x,
                                                     const float* __restrict__ b, const float* __restrict__ c,
@@ -254,9 +254,13 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
   __syncthreads();  // staged rows visible
   // sub-chunk start states for the gradient, when kept (final pass only)
   const int64_t nsub_max = (C + kSub - 1) / kSub;
-  float* hsg = (FINAL && hsub && cb < NB) ? hsub + hsub_offset(k, cb, 0, NB, nsub_max, NL) + lane : nullptr;
+  // (KEEP: the final pass may store states; without it the pass stores y only)
+  float* hsg = (FINAL && KEEP && hsub && cb < NB) ? hsub + hsub_offset(k, cb, 0, NB, nsub_max, NL) + lane : nullptr;
   // every state, when kept (the store-everything baseline): h_t after token t
-  float* hag = (FINAL && hall && cb < NB) ? hall + hsub_offset(k, cb, 0, NB, C, NL) + lane : nullptr;
+  float* hag = (FINAL && KEEP && hall && cb < NB) ? hall + hsub_offset(k, cb, 0, NB, C, NL) + lane : nullptr;
+  // y rows are stored through buffer resources: lanes that store nothing
+  // carry an offset past the row, so the store needs no branch
+  const int voff_y = (valid && grp == 0) ? static_cast<int>(ob4) : kBufOutside;
   static_assert(D % kSub == 0, "ring length a multiple of the sub-chunk");
   double ss = 0.0;
   int plo = 0;  // first token of the staged part
@@ -265,7 +269,10 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
     // One token of the walk; `ahead` is the token whose s and x the ring
     // fetches now (D - 1 tokens on).
     auto token = [&](int r, int tau, bool fetch, int64_t ahead) {
-      if (FINAL && r % kSub == 0 && hsg) {
+      // one token's work stays together (left alone, the scheduler hoists
+      // later tokens' loads and exps and multiplies the live registers)
+      if constexpr (FINAL && !KEEP) __builtin_amdgcn_sched_barrier(0);
+      if (FINAL && KEEP && r % kSub == 0 && hsg) {
 #pragma unroll
         for (int j = 0; j < NL; j++) hsg[(tau / kSub * NL + j) * 64] = h[j];
       }
@@ -293,13 +300,14 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
             acc = fmaf(cq[jj], h[j + jj], acc);
           }
         }
-        if (hag) {
+        if (KEEP && hag) {
 #pragma unroll
           for (int j = 0; j < NL; j++) hag[(tau * NL + j) * 64] = h[j];
         }
         acc = group_sum<G, CH>(acc);
-        if (valid && grp == 0)
-          *reinterpret_cast<float*>(reinterpret_cast<char*>(y + (t0 + tau) * P) + ob4) = acc;
+        const __amdgpu_buffer_rsrc_t ry =
+            __builtin_amdgcn_make_buffer_rsrc(y + (t0 + tau) * P, 0, static_cast<int>(P * 4), kBufWord3);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), ry, voff_y, 0, 0);
       } else {
 #pragma unroll
         for (int j = 0; j < NL; j++) {
@@ -319,12 +327,12 @@ __global__ __launch_bounds__(256) void k_fwd_staged(int64_t T, int64_t P, int64_
         __syncthreads();
       }
     };
-    if (!FINAL && len % D == 0) {
+    if ((!FINAL || !KEEP) && len % D == 0) {
       // whole ring turns: no per-token bounds branches (the fetches past the
       // chunk end re-read its last token), so the state stays in place rather
-      // than being copied back at every token.  (The final pass keeps the
-      // checked loop: its per-token branches remain for the y and sub-chunk
-      // state stores, and there the checked form addresses its loads better.)
+      // than being copied back at every token, and with no branch in the ring
+      // turn the waits for its loads count them one by one.  (A final pass
+      // that stores states keeps the checked loop.)
       for (int q8 = 0; q8 < len; q8 += D) {
         next_part(q8);
 #pragma unroll
@@ -392,7 +400,10 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.marks.rec(3, st);
   if (staged) {
-    auto kf = parts_final ? k_fwd_staged<IO, NL, G, true, true> : k_fwd_staged<IO, NL, G, true, false>;
+    // states kept by the forward: the variant that stores them
+    const bool keep = a.hsub || a.hall;
+    auto kf = parts_final ? (keep ? k_fwd_staged<IO, NL, G, true, true, true> : k_fwd_staged<IO, NL, G, true, true>)
+                          : (keep ? k_fwd_staged<IO, NL, G, true, false, true> : k_fwd_staged<IO, NL, G, true, false>);
     kf<<<grid_s, 64 * kFwdWpb, rows_final, st>>>(a.T, a.P, a.N, a.C, NB, a.s, static_cast<const IO*>(a.x), a.b, a.c,
                                                  a.alpha, a.h_ckpt, a.y, a.hloc, a.ssum, a.hsub, a.hall);
   } else {

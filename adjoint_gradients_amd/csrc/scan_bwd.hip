@@ -466,7 +466,19 @@ __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
   const int64_t t1 = (t0 + C < T) ? t0 + C : T;
   const int len = static_cast<int>(t1 - t0);
   const int nsub_max = (C + S - 1) / S;
-  float* hsg = a.hsub + hsub_offset(k - a.hsub_k0, wave_live ? cb : 0, 0, NB, nsub_max, NL);
+  // The sub-chunk start states go through a buffer resource over this
+  // wavefront's region (covering no bytes for a wavefront past the last
+  // channel block), at this lane's offset plus the sub-chunk's, both in the
+  // range-checked vector offset (the scalar offset is not range-checked): no
+  // branch and no 64-bit address per store.  The state entering sub-chunk
+  // u + 1 is stored right after the token that ends sub-chunk u (a chunk's
+  // last one lands past the region and is dropped), the chunk checkpoint
+  // before the walk, so the walk never stores a state still being loaded and
+  // its ring's loads are not drained at every sub-chunk.
+  const __amdgpu_buffer_rsrc_t rsub = __builtin_amdgcn_make_buffer_rsrc(
+      a.hsub + hsub_offset(k - a.hsub_k0, wave_live ? cb : 0, 0, NB, nsub_max, NL), 0,
+      wave_live ? static_cast<int>(static_cast<int64_t>(nsub_max) * NL * 64 * 4) : 0, kBufWord3);
+  const int voff_lane = lane * 4;
   const int tp = len < TP ? len : TP;  // tokens per staged part
   float* crow = rows + static_cast<size_t>(tp) * NN;
   // rows of tokens [lo, lo + n) -> the staging area (the caller synchronises)
@@ -503,16 +515,16 @@ __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
 #pragma unroll
   for (int q = 0; q < D - 1; q++)
     if (q < len) ld(q, t0 + q);
+  // the state entering sub-chunk 0: the checkpoint
+#pragma unroll
+  for (int j = 0; j < NL; j++)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h[j]), rsub, voff_lane + j * 256, 0, 0);
   __syncthreads();  // staged rows visible
   static_assert(D % S == 0 || S % D == 0, "ring and sub-chunk sizes");
   int plo = 0;  // first token of the staged part
   {
     constexpr bool MULTI = PARTS;
     auto tok = [&](int r, int tau, bool fetch, int ahead) {
-      if (tau % S == 0 && wave_live) {
-#pragma unroll
-        for (int j = 0; j < NL; j++) hsg[((tau / S) * NL + j) * 64 + lane] = h[j];
-      }
       if (fetch) ld((r + D - 1) % D, t0 + ahead);
       const float ns = -rs[r];
       const float xv = raw_to_f32(rx[r]);
@@ -532,6 +544,12 @@ __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
           Q[j + jj] *= av;
           U[j + jj] = fmaf(gv * cq[jj], Q[j + jj], U[j + jj]);
         }
+      }
+      if ((tau + 1) % S == 0) {
+#pragma unroll
+        for (int j = 0; j < NL; j++)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h[j]), rsub,
+                                                voff_lane + ((tau + 1) / S) * (NL * 256) + j * 256, 0, 0);
       }
     };
     // the next part's rows, once every wavefront is done with this part's

@@ -5,8 +5,10 @@
 //   phase 1  forward walk from the chunk checkpoint h_{t0-1}; the state at
 //            the start of every S-token sub-chunk goes to a per-wavefront
 //            scratch area in global memory (written and read back by the same
-//            lanes).  Where k_bwd_hsub can stage the chunk's rows, it does this
-//            walk beforehand at higher occupancy and this phase is skipped;
+//            lanes).  Where the states are already there -- kept by the
+//            forward, or written by the slab's rebuild walk beforehand
+//            (k_bwd_local_hsub, or k_bwd_hsub where it can stage the chunk's
+//            rows), at higher occupancy -- this phase is skipped;
 //   phase 2  sub-chunks right to left: recompute the S states into registers,
 //            then walk them in reverse with the adjoint recurrence and the
 //            local VJPs (equations in scan_bwd.hip).  A sub-chunk compiles to

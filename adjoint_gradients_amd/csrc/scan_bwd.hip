@@ -25,8 +25,9 @@
 //   dc_i[n]  = sum_p g_i h_i[p]   (no time sum, hence no window)
 // h_{i-1} is recomputed inside each chunk from the checkpoint h_{kC-1}
 // (review of "Training Deep Nets with Sublinear Memory Cost": recompute
-// inside segments): a forward walk stores h at every S-token sub-chunk in
-// LDS, then each sub-chunk is recomputed into registers and walked in reverse.
+// inside segments): a forward walk stores h at the start of every S-token
+// sub-chunk in a workspace region that holds one slab of chunks, then each
+// sub-chunk is recomputed into registers and walked in reverse.
 // Sums over channels (db, dc) go through an LDS transpose per wavefront, an
 // LDS sum over the wavefronts of the workgroup, and a deterministic final sum
 // over workgroups in a separate kernel.

@@ -137,13 +137,33 @@ PHASE_SOURCES = {
 }
 
 
+# C/C++ tokens that matter for the hash: string and character literals are
+# kept whole, comments dropped, runs of whitespace folded to one space.
+_SRC_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/|\s+', re.S)
+
+
+def code_only(text):
+    """Source text without comments and with whitespace folded, so that an
+    edit of comments or layout alone does not change the hash below."""
+    def sub(m):
+        t = m.group(0)
+        if t.startswith("//") or t.startswith("/*"):
+            return " "
+        if t[0].isspace():
+            return " "
+        return t
+    return re.sub(r" +", " ", _SRC_TOKENS.sub(sub, text)).strip()
+
+
 def source_hash(phase):
+    """Hash of the code (comments and whitespace aside) of the sources a
+    phase's kernels are built from."""
     import hashlib
 
     h = hashlib.sha256()
     for f in PHASE_SOURCES.get(phase, []):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -617,6 +617,7 @@ __global__ __launch_bounds__(256) void k_bwd_local_hsub(BwdArgs a, int64_t NB) {
 // same carries, bit for bit, as one launch over all chunks.
 constexpr int kSegs = 16;
 
+template <int L>
 __global__ __launch_bounds__(64 * kSegs) void k_bwd_carry_seg(int64_t K, int64_t P, int64_t N, int64_t q,
                                                               int64_t k_lo, int64_t k_hi,
                                                               const float* __restrict__ alpha,
@@ -647,7 +648,7 @@ __global__ __launch_bounds__(64 * kSegs) void k_bwd_carry_seg(int64_t K, int64_t
   auto store = [&](int64_t k, float x) {
     if (live) carry[k * PN + e] = x;
   };
-  const float out = seg_affine_scan<kSegLen, kSegs, true>(k_lo, k_hi, cin, sA, sB, sg, lane, load, store);
+  const float out = seg_affine_scan<L, kSegs, true>(k_lo, k_hi, cin, sA, sB, sg, lane, load, store);
   if (k_lo > 0 && live && sg == 0) edge[e] = out;
   if (q > 0 && live && ee - p * N == 0) {
     for (int64_t k = k_lo + sg; k < k_hi; k += kSegs) {
@@ -834,9 +835,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   // (b and c rows in LDS, in parts of at most kHsubRowLds bytes)
   const size_t rows_f = std::min(static_cast<size_t>(2) * a.C * NNc * 4, kHsubRowLds / (2 * NNc * 4) / kBwdLocRing *
                                                                            kBwdLocRing * 2 * NNc * 4);
-  // (every state kept by the forward, a.hall: nothing is rebuilt)
-  const bool given = a.hsub_given || a.hall != nullptr;
-  const bool fused = !given && !wl && NNc % 4 == 0;
+  const bool fused = !(a.hsub_given || a.hall != nullptr) && !wl && NNc % 4 == 0;
   if (!fused) {
     const size_t rows_b = static_cast<size_t>(wl ? 2 : 1) * a.C * NNc * 4;
     const dim3 gs(static_cast<unsigned>(K), static_cast<unsigned>((NB + kBwdLocWpb - 1) / kBwdLocWpb));
@@ -856,9 +855,21 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   }
   a.marks.rec(1, st);
   const int64_t PN = a.P * a.N;
+  // States kept by the forward: nothing is rebuilt, and the carries run over
+  // all chunks at once.
+  const bool given = a.hsub_given || a.hall != nullptr;
+  // Segment length of the carry's scan: short segments when the default slab
+  // is short, so that the kSegs wavefronts of a workgroup all hold chunks of
+  // it (a carry over all chunks at once keeps the long ones).  It depends on
+  // the shapes only (not on the slab size a caller picks), and both lengths
+  // divide kSegLen: slabs at multiples of kSegLen give the same carries, bit
+  // for bit.
+  const int64_t nseg = fused ? bwd_hsub_slab_chunks(a.T, a.P, a.N, a.C) : K;
+  const bool short_seg = nseg <= static_cast<int64_t>(kSegs) * kSegLenShort;
   // carries of chunks [lo, hi) (windowed aggregates composed on the way)
   auto carry_range = [&](int64_t lo, int64_t hi) -> hipError_t {
-    k_bwd_carry_seg<<<static_cast<unsigned>((PN + 63) / 64), 64 * kSegs, 0, st>>>(
+    auto ck = short_seg ? k_bwd_carry_seg<kSegLenShort> : k_bwd_carry_seg<kSegLen>;
+    ck<<<static_cast<unsigned>((PN + 63) / 64), 64 * kSegs, 0, st>>>(
         K, a.P, a.N, compose ? a.W / a.C : 0, lo, hi, a.alpha, a.ssum, a.ps64, a.umu, a.carry, a.edge, a.hwin);
     return hipGetLastError();
   };

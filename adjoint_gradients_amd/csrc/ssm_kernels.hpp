@@ -108,9 +108,13 @@ size_t bwd_hsub_floats(int64_t T, int64_t P, int64_t N, int C);
 // Floats of every state of T tokens in the one-token-sub-chunk layout (the
 // store-everything baseline's buffer).
 size_t bwd_hall_floats(int64_t T, int64_t P, int64_t N, int C);
-// Chunks per segment of the carry's segmented scan.  Slabs that start at
-// multiples of it give the same carries, bit for bit, whatever their size.
+// Chunks per segment of the gradient's carry scan: kSegLen, or kSegLenShort
+// when the default slab holds few chunks (the length follows from the shapes
+// alone).  Slabs that start at multiples of kSegLen give the same carries,
+// bit for bit, whatever their size.
 constexpr int kSegLen = 16;
+constexpr int kSegLenShort = 4;
+static_assert(kSegLen % kSegLenShort == 0, "both segment lengths divide kSegLen");
 // Chunks per slab of the gradient's own sub-chunk-state region: at most
 // kHsubSlabBytes of states, a multiple of 32 chunks when that many fit (else
 // of kSegLen when that many fit), never more than the chunk count.

@@ -46,7 +46,13 @@ EXPORTED = (
     "ssm_stack_grad",
     "ssm_forward_timed",
     "ssm_adjoint_grad_timed",
+    # ssm_probe.h: issue-rate probes of single gfx950 units (no part of the gradient path)
+    "ssm_probe_units",
+    "ssm_probe_wall_clock_khz",
 )
+
+SSM_PROBE_FMA, SSM_PROBE_EXP, SSM_PROBE_EXP_FMA, SSM_PROBE_MFMA = 0, 1, 2, 3
+SSM_PROBE_WAVES_PER_WG = 4
 
 
 class SsmError(RuntimeError):
@@ -120,6 +126,11 @@ def _load():
     lib.ssm_forward_timed.restype = ctypes.c_int
     lib.ssm_adjoint_grad_timed.argtypes = lib.ssm_adjoint_grad.argtypes + [VP, ctypes.c_int32]
     lib.ssm_adjoint_grad_timed.restype = ctypes.c_int
+    lib.ssm_probe_units.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    lib.ssm_probe_units.restype = ctypes.c_int
+    lib.ssm_probe_wall_clock_khz.argtypes = [P(ctypes.c_int)]
+    lib.ssm_probe_wall_clock_khz.restype = ctypes.c_int
     return lib
 
 
@@ -490,3 +501,22 @@ def stack_grad(dims: Dims, layers: list, x0, g, window: int, ws=None, want_dx0=T
     ssm_stack_grad(K, dims, structs, x0, g, window, [grads_struct(gr, dims) for gr in grads],
                    dx0, xK, ws, ws.numel(), stream)
     return grads, dx0, xK
+
+
+# ---------------------------------------------------------------- unit probes (ssm_probe.h)
+
+def ssm_probe_units(kind: int, wgs: int, iters: int, sink, clk, stream=None):
+    """One probe launch (asynchronous): sink float32 [wgs * 256], clk int64
+    [wgs * SSM_PROBE_WAVES_PER_WG * 4] (raw uint64 clock readings)."""
+    import torch
+
+    _need(sink, "sink", int(wgs) * 256, torch.float32)
+    _need(clk, "clk", int(wgs) * SSM_PROBE_WAVES_PER_WG * 4, torch.int64)
+    _check(lib.ssm_probe_units(int(kind), int(wgs), int(iters), _ptr(sink), _ptr(clk), _stream(stream)),
+           "ssm_probe_units")
+
+
+def ssm_probe_wall_clock_khz() -> int:
+    khz = ctypes.c_int(0)
+    _check(lib.ssm_probe_wall_clock_khz(ctypes.byref(khz)), "ssm_probe_wall_clock_khz")
+    return int(khz.value)

@@ -353,6 +353,66 @@ def study_memory():
             del y, saved, grads, inp, x, g, lay
 
 
+# Unit probes: (name, kind, workgroups per CU, iterations, wave64 instructions
+# of each kind per wavefront and iteration).  Eight waves per SIMD for the
+# VALU probes, two for MFMA (as in the GEMMs); about 20-60 ms each.
+UNIT_PROBES = (
+    ("fp32_fma", 0, 8, 250000, {"fma": 8}),
+    ("exp2", 1, 8, 125000, {"exp": 8}),
+    ("exp2_and_fma", 2, 8, 100000, {"exp": 8, "fma": 8}),
+    ("mfma_bf16_32x32x16", 3, 2, 150000, {"mfma": 4}),
+)
+
+
+def calibrate_units():
+    """Issue rates of single gfx950 units (ssm_probe.h), each with the clock
+    the chip ran that load at (shader-clock cycles over wall-clock time, read
+    by every wavefront of the probe): the fp32 FMA rate, the cost of a
+    v_exp_f32 in VALU issue cycles (the scans' roofline counts two slots), and
+    the dense bf16 MFMA rate (the GEMMs' peak).  One JSON line per probe."""
+    import torch
+
+    import adjoint_gradients_amd as agm
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    khz = agm.ssm_probe_wall_clock_khz()
+    for name, kind, per_cu, iters, counts in UNIT_PROBES:
+        wgs = cus * per_cu
+        waves = wgs * agm.SSM_PROBE_WAVES_PER_WG
+        sink = torch.empty(wgs * 256, device="cuda:0", dtype=torch.float32)
+        clk = torch.empty(waves * 4, device="cuda:0", dtype=torch.int64)
+        agm.ssm_probe_units(kind, wgs, max(1, iters // 50), sink, clk)  # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        agm.ssm_probe_units(kind, wgs, iters, sink, clk)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        c = clk.view(waves, 4).cpu().double()
+        ghz_w = (c[:, 1] - c[:, 0]) / ((c[:, 3] - c[:, 2]) / (khz * 1e3)) / 1e9
+        ghz = float(ghz_w.median())
+        # SIMD issue cycles per wave64 instruction of the probe: 4 SIMDs a CU
+        simd_cycles = 4.0 * cus * ghz * 1e9 * ms * 1e-3
+        n_inst = waves * iters * sum(counts.values())
+        rec = {"probe": name, "workgroups": wgs, "waves_per_simd": per_cu * agm.SSM_PROBE_WAVES_PER_WG // 4,
+               "iters": iters, "ms": round(ms, 3), "clock_ghz": round(ghz, 3),
+               "clock_ghz_min_max": [round(float(ghz_w.min()), 3), round(float(ghz_w.max()), 3)],
+               "simd_cycles_per_wave_instruction": round(simd_cycles / n_inst, 3)}
+        if "mfma" in counts:
+            flops = waves * iters * counts["mfma"] * 2 * 32 * 32 * 16
+            rec["tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+            rec["flops_per_cu_per_clock"] = round(flops / (ms * 1e-3) / cus / (ghz * 1e9), 1)
+            rec["published_peak_at_this_clock_tflops"] = round(MFMA_BF16_PEAK_TFS * ghz / 2.4, 1)
+        else:
+            lane_ops = waves * 64 * iters * sum(counts.values())
+            rec["lane_ops_per_s"] = float(f"{lane_ops / (ms * 1e-3):.4g}")
+            rec["lane_ops_per_cu_per_clock"] = round(lane_ops / (ms * 1e-3) / cus / (ghz * 1e9), 2)
+            if kind == 2:
+                # one exp and one FMA a pair: the exp's issue cycles beyond the FMA's 4
+                rec["exp_issue_slots_when_mixed"] = round((2 * simd_cycles / n_inst - 4.0) / 4.0, 2)
+        print(json.dumps(rec), flush=True)
+
+
 def bench_stack(args, case_idx, window, chunk, norm=False):
     """One step of the K-layer residual stack: ssm_stack_grad (K forwards, then
     the K gradients in reverse with the cotangent passed down), timed whole
@@ -435,6 +495,9 @@ def main():
     ap.add_argument("--phases", action="store_true", help="print the per-phase breakdown to stderr")
     ap.add_argument("--study", choices=("truncation", "memory"), default=None,
                     help="run a measurement study instead of the benchmark (JSON lines on stdout)")
+    ap.add_argument("--calibrate-units", action="store_true",
+                    help="only run the unit probes (fp32 FMA, exp2, both, bf16 MFMA issue rates with the "
+                         "clock the chip ran each at; JSON lines on stdout)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB three times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -456,6 +519,9 @@ def main():
         return
     if args.study == "memory":
         study_memory()
+        return
+    if args.calibrate_units:
+        calibrate_units()
         return
     if args.calibrate_copy:
         # a plain device-to-device copy of known size: its FETCH_SIZE and

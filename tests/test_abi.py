@@ -2,19 +2,22 @@
 the header declares, sizes its buffers, and rejects bad arguments before any
 HIP call is made."""
 import ctypes
+import glob
 import os
 import re
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ssm_adjoint.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(ssm_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -252,3 +255,15 @@ def test_noalloc_refuses_oversize_before_launch(agm):
     rc = agm.lib.ssm_adjoint_grad_noalloc(ctypes.byref(d), ctypes.byref(L), 0x1000000, ctypes.byref(S),
                                           0x2000000, 0, ctypes.byref(G), None)
     assert rc == 1
+
+
+def test_probe_validation(agm):
+    # the unit probes reject bad arguments before any HIP call (fake
+    # non-null addresses are never dereferenced)
+    L = agm.lib
+    sink, clk = ctypes.c_void_p(0x600000), ctypes.c_void_p(0x700000)
+    for kind, wgs, iters, s, c in [(-1, 8, 10, sink, clk), (4, 8, 10, sink, clk), (0, 0, 10, sink, clk),
+                                   (0, (1 << 20) + 1, 10, sink, clk), (0, 8, 0, sink, clk),
+                                   (0, 8, 1 << 31, sink, clk), (3, 8, 10, None, clk), (3, 8, 10, sink, None)]:
+        assert L.ssm_probe_units(kind, wgs, iters, s, c, None) == 1, (kind, wgs, iters)
+    assert L.ssm_probe_wall_clock_khz(None) == 1
